@@ -1,0 +1,157 @@
+"""Seeded synthetic inputs for draft-tree construction.
+
+This module is shared by the tests, the benchmark and the smoke check. It
+holds input generation only: Gaussian draft-logit rows, bf16 rounding, and
+the target-token draws that stand in for the target model's argmax. It
+computes nothing that the tree builder computes (no normaliser, no ranking,
+no prefix selection), and it imports neither the oracle nor the HIP binding.
+
+Shapes follow the pages' workloads: L = 15 draft positions and a ~152k
+vocabulary (SparklingTree post, "Step 1: Sorting the DFlash marginals"),
+node budgets 64/128/256 (DDTree explainer, section 7 "Experiments": budget
+trade-off). The value distributions (per-row sigma ~ U[lo, hi] Gaussian,
+optional planted peak) are synthetic stand-ins for drafter rows; the pages
+give none.
+
+Every request b of configuration c with seed s draws from its own stream
+``numpy.random.default_rng(SeedSequence([c, s, b]))``; target draws use the
+stream ``SeedSequence([c, s, b, 1])``. Requests are therefore independent
+of the batch size they are generated in.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+DTYPE_BF16 = 0
+DTYPE_F32 = 1
+
+# name -> parameters. V=151936 is the Qwen3 vocabulary of the pages' targets.
+CONFIGS = {
+    1: dict(batch=1, L=15, V=1024, B=32, dtype=DTYPE_F32, sigma=(1.0, 6.0),
+            peak=False, targets="fresh_argmax"),
+    2: dict(batch=1, L=15, V=151936, B=64, dtype=DTYPE_BF16, sigma=(1.0, 6.0),
+            peak=True, targets="drafter"),
+    3: dict(batch=64, L=15, V=151936, B=128, dtype=DTYPE_BF16, sigma=(1.0, 6.0),
+            peak=True, targets="drafter"),
+    5: dict(batch=256, L=15, V=151936, B=256, dtype=DTYPE_BF16, sigma=(0.5, 8.0),
+            peak=False, targets="drafter"),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 with round-to-nearest-even; returns uint16 bits.
+
+    Finite inputs only (the generators never produce inf/NaN).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _rng(cfg_id: int, seed: int, b: int, stream: int | None = None) -> np.random.Generator:
+    key = [int(cfg_id), int(seed), int(b)] + ([] if stream is None else [int(stream)])
+    return np.random.default_rng(np.random.SeedSequence(key))
+
+
+def request_rows(cfg_id: int, seed: int, b: int, *, L: int, V: int, sigma, peak: bool,
+                 dtype: int) -> np.ndarray:
+    """Draft logits of one request, shape [L, V]: uint16 bf16 bits or float32."""
+    rng = _rng(cfg_id, seed, b)
+    lo, hi = sigma
+    s = rng.uniform(lo, hi, L).astype(np.float32)
+    g = rng.standard_normal((L, V), dtype=np.float32)
+    x = (s[:, None] * g).astype(np.float32)
+    if peak:
+        # Planted peak: one token per row sits U[2,10] above the row's Gaussian max.
+        pid = rng.integers(0, V, L)
+        off = rng.uniform(2.0, 10.0, L).astype(np.float32)
+        rowmax = x.max(axis=1)
+        x[np.arange(L), pid] = (rowmax + off).astype(np.float32)
+    if dtype == DTYPE_BF16:
+        return f32_to_bf16_bits(x)
+    return x
+
+
+def make_logits(cfg_id: int, seed: int = 0, *, batch: int | None = None, first: int = 0,
+                L: int | None = None, V: int | None = None) -> np.ndarray:
+    """Logits [batch, L, V] for requests first .. first+batch-1 of a configuration."""
+    c = CONFIGS[cfg_id]
+    batch = c["batch"] if batch is None else batch
+    L = c["L"] if L is None else L
+    V = c["V"] if V is None else V
+    dt = np.uint16 if c["dtype"] == DTYPE_BF16 else np.float32
+    out = np.empty((batch, L, V), dtype=dt)
+    for i in range(batch):
+        out[i] = request_rows(cfg_id, seed, first + i, L=L, V=V, sigma=c["sigma"],
+                              peak=c["peak"], dtype=c["dtype"])
+    return out
+
+
+def logits_as_f64(logits: np.ndarray, dtype: int) -> np.ndarray:
+    """Exact float64 values of generated logits (bf16 bits or float32)."""
+    if dtype == DTYPE_BF16:
+        return bf16_bits_to_f32(logits).astype(np.float64)
+    return np.asarray(logits, dtype=np.float32).astype(np.float64)
+
+
+def drafter_draws(cfg_id: int, seed: int, logits: np.ndarray, dtype: int, *,
+                  first: int = 0) -> np.ndarray:
+    """One sequence Y ~ Q per request, shape [batch, L+1] int32.
+
+    Y_d for d = 1..L is drawn from softmax(x_d) by the Gumbel-max rule
+    (argmax of x_d[v] + G_v with G_v standard Gumbel, in float64); Y_{L+1}
+    is uniform over the vocabulary. A tree node at depth d then receives the
+    target token Y_{d+1} (root: Y_1), so a node is reached by the greedy walk
+    exactly when the draft agrees with Y along its path, which happens with
+    probability equal to the node's prefix probability under the drafter's
+    factorised distribution (DDTree explainer, section 2 and Proposition 1).
+    """
+    batch, L, V = logits.shape
+    out = np.empty((batch, L + 1), dtype=np.int32)
+    for i in range(batch):
+        rng = _rng(cfg_id, seed, first + i, stream=1)
+        x = logits_as_f64(logits[i], dtype)
+        u = rng.random((L, V))
+        # Gumbel(0,1) = -log(-log U); U in (0,1) with probability one.
+        g = -np.log(-np.log(np.clip(u, 1e-300, None)))
+        out[i, :L] = np.argmax(x + g, axis=1).astype(np.int32)
+        out[i, L] = int(rng.integers(0, V))
+    return out
+
+
+def node_targets_from_depths(Y: np.ndarray, depths: np.ndarray, num_nodes: np.ndarray,
+                             B: int) -> np.ndarray:
+    """Per-node target tokens [batch, B+1]: root gets Y_1, a depth-d node Y_{d+1}.
+
+    Stand-in for the target model's argmax at each tree position. Entries past
+    num_nodes are unused by the walk and set to 0.
+    """
+    batch = Y.shape[0]
+    out = np.zeros((batch, B + 1), dtype=np.int32)
+    for i in range(batch):
+        n = int(num_nodes[i])
+        out[i, 0] = Y[i, 0]
+        if n:
+            out[i, 1:n + 1] = Y[i, np.asarray(depths[i, :n], dtype=np.int64)]
+    return out
+
+
+def fresh_argmax_targets(cfg_id: int, seed: int, batch: int, B: int, V: int, *,
+                         first: int = 0) -> np.ndarray:
+    """Targets independent of the tree: argmax of fresh 4*N(0,1) logits per node.
+
+    Shape [batch, B+1]; ties go to the lowest index (numpy.argmax).
+    """
+    out = np.empty((batch, B + 1), dtype=np.int32)
+    for i in range(batch):
+        rng = _rng(cfg_id, seed, first + i, stream=1)
+        g = 4.0 * rng.standard_normal((B + 1, V))
+        out[i] = np.argmax(g, axis=1).astype(np.int32)
+    return out
