@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Draft-tree construction benchmark on one MI355X.
+
+One step = the whole hot path over one batch of the batch-64 workload
+(64 requests x 15 draft positions x V = 151936 bf16 logits, node budget 128):
+  stage 1  ddtree_row_topk  per-row log-sum-exp + sorted top-128 (HBM-bound)
+  stage 2+3 ddtree_select   top-128 prefix tree + bit-packed ancestor mask
+  stage 4  ddtree_accept    greedy walk against per-node target tokens
+Inputs are synthetic (draft_tree_construction_depth_amd.gen), already resident
+in HBM; four copies of the batch rotate so that the 256 MB Infinity Cache
+cannot serve repeated reads. Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "draft trees/sec at batch 64, V=151936, L=15, B=128; achieved HBM GB/s vs peak"
+PEAK_HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_stage1_batch64.json")
+STAGE1_SOURCES = ["draft_tree_construction_depth_amd/csrc/stage1.hpp",
+                  "draft_tree_construction_depth_amd/csrc/common.hpp"]
+
+
+def stage1_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in STAGE1_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per stage-1 launch from committed rocprofv3 counters, or None
+    when the counters were taken on a different version of the kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != stage1_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(x, Y, B, L):
+    """The oracle as it stands, timed on this host over the same batch."""
+    import numpy as np
+
+    from draft_tree_construction_depth_amd import gen
+    from oracle import oracle as O
+    if not os.path.exists(O.LIB):
+        O.build_oracle()
+    threads = max(1, min(len(os.sched_getaffinity(0)), 16))
+    t0 = time.perf_counter()
+    o = O.build(x, gen.DTYPE_BF16, B, threads=threads, tables=False)
+    O.mask(o["parents"], o["num_nodes"], B)
+    t1 = time.perf_counter()
+    tgt = gen.node_targets_from_depths(Y, o["depths"], o["num_nodes"], B)
+    t2 = time.perf_counter()
+    O.accept(o["tree_tokens"], o["parents"], o["num_nodes"], tgt, L)
+    t3 = time.perf_counter()
+    secs = (t1 - t0) + (t3 - t2)
+    n = x.shape[0]
+    return {"value": n / secs, "unit": "trees/s", "cores": threads, "kind": "oracle",
+            "sample": f"all {n} requests of one batch (build + mask + accept), {secs:.2f} s"}, o
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--buffers", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): every draft tree is "
+              "independent, so more GPUs would each run this same per-GPU workload on their "
+              "own requests; multi-GPU runs are not part of this build.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import draft_tree_construction_depth_amd as pkg
+    from draft_tree_construction_depth_amd import gen
+
+    c = gen.CONFIGS[3]
+    batch, L, V, B = c["batch"], c["L"], c["V"], c["B"]
+    K = min(B, V)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    x = gen.make_logits(3, 0)
+    Y = gen.drafter_draws(3, 0, x, c["dtype"])
+    x_dev = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    bufs = [x_dev] + [x_dev.clone() for _ in range(args.buffers - 1)]
+
+    rows = batch * L
+    tables = dict(ids=torch.empty((rows, K), dtype=torch.int32, device=dev),
+                  vals=torch.empty((rows, K), dtype=torch.float32, device=dev),
+                  lse=torch.empty((rows,), dtype=torch.float64, device=dev))
+    tv = tables["vals"].view(batch, L, K)
+    ti = tables["ids"].view(batch, L, K)
+    tz = tables["lse"].view(batch, L)
+    ws_size = pkg.lib().ddtree_row_topk_workspace_size(rows, V, K, pkg.DDT_BF16)
+    ws = torch.zeros(ws_size, dtype=torch.uint8, device=dev)
+
+    # One untimed round gives the tree shape; the per-node target tokens (the
+    # target model's argmax at each node, a stand-in) follow from it.
+    pkg.ddtree_row_topk(bufs[0], K, out=tables, ws=ws)
+    tree = pkg.ddtree_select(tv, ti, tz, B)
+    torch.cuda.synchronize()
+    tgt = gen.node_targets_from_depths(Y, tree["depths"].cpu().numpy(),
+                                       tree["num_nodes"].cpu().numpy(), B)
+    tgt_dev = torch.from_numpy(tgt).to(dev)
+    acc = pkg.ddtree_accept(tree["tree_tokens"], tree["parents"], tree["num_nodes"], tgt_dev, L)
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        pkg.ddtree_row_topk(bufs[i % len(bufs)], K, out=tables, ws=ws)
+        if ev is not None:
+            ev[1].record()
+        pkg.ddtree_select(tv, ti, tz, B, out=tree)
+        pkg.ddtree_accept(tree["tree_tokens"], tree["parents"], tree["num_nodes"], tgt_dev, L,
+                          out=acc)
+
+    for i in range(args.warmup):
+        step(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    s1_ms = [a.elapsed_time(b) for a, b in evs]
+    s1_avg_ms = float(np.mean(s1_ms))
+    trees_per_s = batch * args.steps / (total_ms / 1e3)
+
+    logits_bytes = batch * L * V * 2
+    # Algorithmic bytes of the whole step (logits once, tree outputs, mask,
+    # targets read, walk outputs).
+    W = (B + 1 + 63) // 64
+    step_bytes = logits_bytes + batch * (B * 12 + B * 4 + 4 + (B + 1) * W * 8
+                                         + (B + 1) * 4 + (L + 2) * 4)
+    achieved = logits_bytes / (s1_avg_ms / 1e3) / 1e9
+    traffic = measured_traffic()
+
+    result = {
+        "metric": METRIC,
+        "value": round(trees_per_s, 1),
+        "unit": "trees/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32/f64",
+        "data": "synthetic",
+        "config": {"workload": "batch64_L15_V151936_B128_bf16_logits", "batch": batch, "L": L,
+                   "V": V, "B": B, "input_buffers": len(bufs)},
+        "whole_step_gbps": round(step_bytes * args.steps / (total_ms / 1e3) / 1e9, 1),
+        "wall_s": round(wall, 4),
+        "roofline": {"bound": "hbm", "kernel": "stage1 (ddtree_row_topk)",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "avg_launch_us": round(s1_avg_ms * 1e3, 2),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        cb, _ = cpu_baseline(x, Y, B, L)
+        result["cpu_baseline"] = {k: (round(v, 2) if isinstance(v, float) else v)
+                                  for k, v in cb.items()}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,17 @@
+"""MI355X-native draft-tree construction (DDTree-style) for speculative decoding.
+
+The compute lives in libddtree.so (hand-written HIP for gfx950, C ABI in
+include/ddtree.h); this package only binds it:
+
+    ddtree_build     logits [batch, L, V] -> top-B prefix tree (+ ancestor mask)
+    ddtree_select    stage 2 alone, from stage-1 tables (+ mask)
+    ddtree_mask      parents -> bit-packed ancestor-only attention mask
+    ddtree_accept    tree + target tokens -> accepted path, new bonus token
+    ddtree_row_topk  stage 1 alone: per-row sorted top-K and log-sum-exp
+"""
+
+from ._lib import (DDT_BF16, DDT_F32, DDTreeError, ddtree_accept, ddtree_build, ddtree_mask,
+                   ddtree_row_topk, ddtree_select, lib, status_string)
+
+__all__ = ["DDT_BF16", "DDT_F32", "DDTreeError", "ddtree_accept", "ddtree_build", "ddtree_mask",
+           "ddtree_row_topk", "ddtree_select", "lib", "status_string"]

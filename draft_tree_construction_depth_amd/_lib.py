@@ -1,0 +1,195 @@
+"""ctypes binding of libddtree.so (C ABI in include/ddtree.h).
+
+Argument marshalling only: every function below passes torch tensors' device
+pointers and the current HIP stream to the function of the same name in the
+library; all computation happens in the library's HIP kernels. There is no
+fallback: if the library is missing, loading it raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libddtree.so")
+
+DDT_OK, DDT_EINVAL, DDT_ENOTSUP, DDT_EWORKSPACE, DDT_EHIP = 0, -1, -2, -3, -4
+DDT_BF16, DDT_F32 = 0, 1
+
+_lib = None
+
+
+class DDTreeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+def lib() -> C.CDLL:
+    """Load libddtree.so from the package directory (raises if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"HIP library not built: {LIB_PATH} is missing; run __graft_entry__.build()")
+        L = C.CDLL(LIB_PATH)
+        p, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+        L.ddt_abi_version.restype = C.c_int
+        L.ddt_status_string.restype = C.c_char_p
+        L.ddt_status_string.argtypes = [C.c_int]
+        L.ddtree_build_workspace_size.restype = sz
+        L.ddtree_build_workspace_size.argtypes = [i64, i32, i64, i32, C.c_int]
+        L.ddtree_row_topk_workspace_size.restype = sz
+        L.ddtree_row_topk_workspace_size.argtypes = [i64, i64, i32, C.c_int]
+        L.ddtree_build.restype = C.c_int
+        L.ddtree_build.argtypes = [p, C.c_int, i64, i32, i64, i32, p, p, p, p, p, p, p, sz, p]
+        L.ddtree_select.restype = C.c_int
+        L.ddtree_select.argtypes = [p, p, p, i64, i32, i32, i32, p, p, p, p, p, p, p]
+        L.ddtree_mask.restype = C.c_int
+        L.ddtree_mask.argtypes = [p, p, i64, i32, p, p]
+        L.ddtree_accept.restype = C.c_int
+        L.ddtree_accept.argtypes = [p, p, p, p, i64, i32, i32, p, p, p, p]
+        L.ddtree_row_topk.restype = C.c_int
+        L.ddtree_row_topk.argtypes = [p, C.c_int, i64, i64, i32, p, p, p, p, sz, p]
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().ddt_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DDT_BF16
+    if t.dtype == torch.float32:
+        return DDT_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(fn, rc):
+    if rc != DDT_OK:
+        raise DDTreeError(fn, rc)
+
+
+_workspaces: dict = {}
+
+
+def workspace(kind: str, size: int, device, key) -> torch.Tensor:
+    """Zero-filled workspace cached per (kind, device, shape key).
+
+    The library leaves a workspace zero-filled for the next call of the same
+    shape, so one buffer per shape is reused across calls on one stream.
+    """
+    k = (kind, str(device), key)
+    ws = _workspaces.get(k)
+    if ws is None or ws.numel() < size:
+        ws = torch.zeros(max(size, 1), dtype=torch.uint8, device=device)
+        _workspaces[k] = ws
+    return ws
+
+
+def ddtree_build(logits: torch.Tensor, B: int, *, with_mask: bool = True, out: dict | None = None,
+                 ws: torch.Tensor | None = None) -> dict:
+    """Stages 1-2 (+3): logits [batch, L, V] (bf16/f32, cuda) -> tree tensors."""
+    assert logits.is_cuda and logits.dim() == 3 and logits.is_contiguous()
+    batch, L, V = logits.shape
+    dev = logits.device
+    dt = _dtype_code(logits)
+    if out is None:
+        out = _tree_out(batch, B, dev, with_mask)
+    size = lib().ddtree_build_workspace_size(batch, L, V, B, dt)
+    if ws is None:
+        ws = workspace("build", size, dev, (batch, L, V, B, dt))
+    rc = lib().ddtree_build(_ptr(logits), dt, batch, L, V, B, _ptr(out["tree_tokens"]),
+                            _ptr(out["parents"]), _ptr(out["logq"]), _ptr(out.get("depths")),
+                            _ptr(out["num_nodes"]), _ptr(out.get("mask")), _ptr(ws),
+                            ws.numel(), _stream(dev))
+    _check("ddtree_build", rc)
+    return out
+
+
+def _tree_out(batch, B, dev, with_mask):
+    out = dict(
+        tree_tokens=torch.empty((batch, B), dtype=torch.int32, device=dev),
+        parents=torch.empty((batch, B), dtype=torch.int32, device=dev),
+        logq=torch.empty((batch, B), dtype=torch.float32, device=dev),
+        depths=torch.empty((batch, B), dtype=torch.int32, device=dev),
+        num_nodes=torch.empty((batch,), dtype=torch.int32, device=dev),
+    )
+    if with_mask:
+        out["mask"] = torch.empty((batch, B + 1, (B + 1 + 63) // 64), dtype=torch.int64, device=dev)
+    return out
+
+
+def ddtree_select(vals: torch.Tensor, ids: torch.Tensor, lse: torch.Tensor, B: int, *,
+                  with_mask: bool = True, out: dict | None = None) -> dict:
+    """Stage 2 (+3) from tables vals/ids [batch, L, K] and lse [batch, L]."""
+    batch, L, K = vals.shape
+    if out is None:
+        out = _tree_out(batch, B, vals.device, with_mask)
+    rc = lib().ddtree_select(_ptr(vals), _ptr(ids), _ptr(lse), batch, L, K, B,
+                             _ptr(out["tree_tokens"]), _ptr(out["parents"]), _ptr(out["logq"]),
+                             _ptr(out.get("depths")), _ptr(out["num_nodes"]), _ptr(out.get("mask")),
+                             _stream(vals.device))
+    _check("ddtree_select", rc)
+    return out
+
+
+def ddtree_mask(parents: torch.Tensor, num_nodes: torch.Tensor, B: int,
+                mask: torch.Tensor | None = None) -> torch.Tensor:
+    batch = num_nodes.shape[0]
+    W = (B + 1 + 63) // 64
+    if mask is None:
+        mask = torch.empty((batch, B + 1, W), dtype=torch.int64, device=parents.device)
+    rc = lib().ddtree_mask(_ptr(parents), _ptr(num_nodes), batch, B, _ptr(mask),
+                           _stream(parents.device))
+    _check("ddtree_mask", rc)
+    return mask
+
+
+def ddtree_accept(tree_tokens: torch.Tensor, parents: torch.Tensor, num_nodes: torch.Tensor,
+                  target_tokens: torch.Tensor, L: int, out: dict | None = None) -> dict:
+    batch, B = tree_tokens.shape
+    dev = tree_tokens.device
+    if out is None:
+        out = dict(accepted_nodes=torch.empty((batch, L), dtype=torch.int32, device=dev),
+                   accept_len=torch.empty((batch,), dtype=torch.int32, device=dev),
+                   next_token=torch.empty((batch,), dtype=torch.int32, device=dev))
+    rc = lib().ddtree_accept(_ptr(tree_tokens), _ptr(parents), _ptr(num_nodes),
+                             _ptr(target_tokens), batch, B, L, _ptr(out["accepted_nodes"]),
+                             _ptr(out["accept_len"]), _ptr(out["next_token"]), _stream(dev))
+    _check("ddtree_accept", rc)
+    return out
+
+
+def ddtree_row_topk(logits: torch.Tensor, K: int, *, out: dict | None = None,
+                    ws: torch.Tensor | None = None) -> dict:
+    """Stage 1 alone: logits [..., V] -> ids/vals [rows, K], lse [rows] (float64)."""
+    assert logits.is_cuda and logits.is_contiguous()
+    V = logits.shape[-1]
+    rows = logits.numel() // V
+    dev = logits.device
+    dt = _dtype_code(logits)
+    if out is None:
+        out = dict(ids=torch.empty((rows, K), dtype=torch.int32, device=dev),
+                   vals=torch.empty((rows, K), dtype=torch.float32, device=dev),
+                   lse=torch.empty((rows,), dtype=torch.float64, device=dev))
+    size = lib().ddtree_row_topk_workspace_size(rows, V, K, dt)
+    if ws is None:
+        ws = workspace("row_topk", size, dev, (rows, V, K, dt))
+    rc = lib().ddtree_row_topk(_ptr(logits), dt, rows, V, K, _ptr(out["ids"]), _ptr(out["vals"]),
+                               _ptr(out["lse"]), _ptr(ws), ws.numel(), _stream(dev))
+    _check("ddtree_row_topk", rc)
+    return out

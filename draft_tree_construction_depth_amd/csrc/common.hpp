@@ -1,0 +1,121 @@
+// Shared device helpers for the draft-tree kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ddt {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Total order on float32 bit patterns as unsigned integers: larger key <=>
+// larger value, with -0 mapped onto +0. NaN is outside the supported inputs.
+__device__ __forceinline__ uint32_t order_key(uint32_t u) {
+  u = (u == 0x80000000u) ? 0u : u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// 64-bit candidate key: value key in the high word, inverted id in the low
+// word, so that a larger key means a larger value or, on equal values, a
+// lower id. Key 0 never occurs for a real element and marks padding.
+__device__ __forceinline__ uint64_t cand_key(uint32_t vkey, uint32_t id) {
+  return ((uint64_t)vkey << 32) | (uint32_t)(0xFFFFFFFFu - id);
+}
+__device__ __forceinline__ uint32_t cand_id(uint64_t k) { return 0xFFFFFFFFu - (uint32_t)k; }
+__device__ __forceinline__ uint32_t cand_vkey(uint64_t k) { return (uint32_t)(k >> 32); }
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    T w = __shfl_xor(v, o);
+    v = v > w ? v : w;
+  }
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_min(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    T w = __shfl_xor(v, o);
+    v = v < w ? v : w;
+  }
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// In-place exclusive scan of a[0..n) (LDS) by NT threads; returns the total.
+// wsum needs NT/64 ints of LDS. Ends with a barrier.
+template <int NT>
+__device__ int block_excl_scan(int* a, int n, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int NW = NT / kWave;
+  const int seg = (n + NT - 1) / NT;
+  const int b0 = min(tid * seg, n), b1 = min(b0 + seg, n);
+  int s = 0;
+  for (int i = b0; i < b1; ++i) s += a[i];
+  int x = s;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) wsum[w] = x;
+  __syncthreads();
+  int pre = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    int t = wsum[i];
+    pre += (i < w) ? t : 0;
+    total += t;
+  }
+  int run = pre + x - s;
+  for (int i = b0; i < b1; ++i) {
+    int t = a[i];
+    a[i] = run;
+    run += t;
+  }
+  __syncthreads();
+  return total;
+}
+
+// Bitonic sort of n (a power of two) 64-bit keys in LDS, largest first.
+template <int NT>
+__device__ void bitonic_desc_u64(uint64_t* a, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < (n >> 1); i += NT) {
+        const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+        const int hi = lo + j;
+        const uint64_t x = a[lo], y = a[hi];
+        const bool big_first = (lo & k) == 0;
+        if (big_first ? (x < y) : (x > y)) {
+          a[lo] = y;
+          a[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ int next_pow2(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+}  // namespace ddt

@@ -1,0 +1,114 @@
+// Stage 3 (standalone) and stage 4: ancestor mask and greedy acceptance walk.
+//
+// Mask: SparklingTree post, "Step 4: Creating the tree mask" -- each node
+// sees itself, its ancestors and the root. Bits are packed LSB first into
+// 64-bit words; one thread builds one row by walking the parent chain.
+//
+// Walk: DDTree explainer, section 5 (verifier walk), TreeSpark README item 4
+// (argmax-following acceptance walk). One wavefront per request holds the
+// request's parent/token arrays in registers (B <= 512, so <= 8 nodes per
+// lane); each step is one compare per held node and a wave-wide min, and the
+// walk takes at most L steps.
+#pragma once
+
+#include "common.hpp"
+
+namespace ddt {
+
+constexpr int kMaskThreads = 256;
+constexpr int kWalkMaxPerLane = 8;  // B <= 512
+
+struct MaskParams {
+  const int32_t* parents;
+  const int32_t* num_nodes;
+  int64_t batch;
+  int32_t B;
+  int32_t W;
+  uint64_t* mask;
+};
+
+__global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskParams p) {
+  constexpr int MW = (512 + 1 + 63) / 64;
+  const int64_t b = blockIdx.x;
+  const int B = p.B, W = p.W;
+  int n = p.num_nodes[b];
+  n = n < 0 ? 0 : (n > B ? B : n);
+  const int32_t* par = p.parents + (size_t)b * B;
+  for (int i = threadIdx.x; i <= B; i += kMaskThreads) {
+    uint64_t m[MW];
+#pragma unroll
+    for (int q = 0; q < MW; ++q) m[q] = 0;
+    if (i <= n) {
+      int u = i;
+      for (int step = 0; step <= B; ++step) {
+        const int wq = u >> 6;
+        const uint64_t bit = 1ull << (u & 63);
+#pragma unroll
+        for (int q = 0; q < MW; ++q) m[q] |= (q == wq) ? bit : 0ull;
+        if (u == 0) break;
+        const int pu = par[u - 1];
+        if (pu < 0 || pu >= u) break;  // malformed parent: stop the walk
+        u = pu;
+      }
+    }
+    uint64_t* dst = p.mask + ((size_t)b * (B + 1) + i) * W;
+#pragma unroll
+    for (int q = 0; q < MW; ++q)
+      if (q < W) dst[q] = m[q];
+  }
+}
+
+struct WalkParams {
+  const int32_t* tree_tokens;
+  const int32_t* parents;
+  const int32_t* num_nodes;
+  const int32_t* target_tokens;  // [batch][B+1]
+  int64_t batch;
+  int32_t B;
+  int32_t L;
+  int32_t* accepted_nodes;  // [batch][L]
+  int32_t* accept_len;
+  int32_t* next_token;
+};
+
+__global__ __launch_bounds__(kWave) void walk_kernel(WalkParams p) {
+  const int64_t b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int B = p.B, L = p.L;
+  int n = p.num_nodes[b];
+  n = n < 0 ? 0 : (n > B ? B : n);
+  int par[kWalkMaxPerLane], tok[kWalkMaxPerLane];
+#pragma unroll
+  for (int t = 0; t < kWalkMaxPerLane; ++t) {
+    const int j = lane + t * kWave;
+    par[t] = -2;
+    tok[t] = 0;
+    if (j < n) {
+      par[t] = p.parents[(size_t)b * B + j];
+      tok[t] = p.tree_tokens[(size_t)b * B + j];
+    }
+  }
+  const int32_t* tgt = p.target_tokens + (size_t)b * (B + 1);
+  int cur = 0, len = 0;
+  while (len < L) {
+    const int want = tgt[cur];
+    int found = 0x7FFFFFFF;
+#pragma unroll
+    for (int t = 0; t < kWalkMaxPerLane; ++t) {
+      const int j = lane + t * kWave;
+      if (par[t] == cur && tok[t] == want) found = j + 1;
+    }
+    found = wave_min(found);
+    if (found == 0x7FFFFFFF) break;
+    if (lane == 0) p.accepted_nodes[(size_t)b * L + len] = found;
+    ++len;
+    cur = found;
+  }
+  for (int i = len + lane; i < L; i += kWave) p.accepted_nodes[(size_t)b * L + i] = -1;
+  if (lane == 0) {
+    p.accept_len[b] = len;
+    p.next_token[b] = tgt[cur];
+  }
+}
+
+}  // namespace ddt

@@ -1,0 +1,181 @@
+/*
+ * ddtree.h -- C ABI of libddtree.so: draft-tree construction on MI355X (gfx950).
+ *
+ * The library turns a block drafter's per-position logits into the draft
+ * tree that DDTree verifies in one target pass, and walks the verified tree.
+ * Operations and where the pages define them:
+ *
+ *  - ddtree_build: the tree of the B most probable draft prefixes under the
+ *    drafter's factorised distribution. DDTree explainer ("DDTree Explained:
+ *    From Block Diffusion to Optimal Diffusion Draft Trees"), section 2
+ *    (objective), section 3 (Proposition 2: the top-B prefixes form the
+ *    optimal tree; Lemma 1: the top K = min(B, V) tokens per position
+ *    suffice) and section 5 (build_tree returns the tree's tokens and
+ *    parent indices); SparklingTree post, sections "Step 1" (per-row top-K
+ *    and log-sum-exp) and "Step 3" (best-first order of the nodes).
+ *  - ddtree_mask: the ancestor-only attention mask. SparklingTree post,
+ *    section "Step 4: Creating the tree mask"; DDTree explainer, section 5.
+ *  - ddtree_accept: the greedy verifier walk. DDTree explainer, section 5;
+ *    TreeSpark README, item 4 (argmax-following acceptance walk).
+ *  - ddtree_row_topk: stage 1 alone (row log-sum-exp and sorted top-K).
+ *    SparklingTree post, section "Step 1".
+ *  - ddtree_select: stage 2 alone, from stage 1's tables. DDTree explainer,
+ *    sections 3-4; SparklingTree post, section "Step 3".
+ *    ddtree_build = ddtree_row_topk + ddtree_select in one call.
+ *
+ * Conventions shared by every call:
+ *  - Device pointers. Every array argument is device memory owned by the
+ *    caller; the library never allocates, frees or retains memory.
+ *  - Streams. Work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *    stream) and runs asynchronously. Outputs are valid once the stream has
+ *    reached that point. No call synchronises with the host.
+ *  - Errors. Arguments are checked on the host before anything is enqueued:
+ *    DDT_EINVAL for null pointers or bad sizes, DDT_ENOTSUP for sizes outside
+ *    the supported region, DDT_EWORKSPACE for a workspace that is too small;
+ *    nothing is enqueued then. DDT_EHIP reports a failed launch. Device-side
+ *    contents (token ids, parent indices) are not validated.
+ *  - Layouts are row-major and contiguous. Node numbering: node 0 is the
+ *    root (the bonus token, which is not an output); node j+1 is the j-th
+ *    emitted node, and nodes are emitted in best-first order, so a parent
+ *    always precedes its children.
+ *  - Threading: the library keeps no state; concurrent calls need separate
+ *    workspaces.
+ */
+#ifndef DDTREE_H
+#define DDTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DDT_OK = 0,
+  DDT_EINVAL = -1,     /* null pointer or invalid size */
+  DDT_ENOTSUP = -2,    /* valid but outside the supported region */
+  DDT_EWORKSPACE = -3, /* workspace smaller than the matching *_workspace_size() */
+  DDT_EHIP = -4        /* a HIP launch failed */
+};
+
+enum { DDT_BF16 = 0, DDT_F32 = 1 };
+
+/* Supported region. */
+#define DDT_MAX_B 512   /* node budget */
+#define DDT_MAX_L 32    /* draft positions (tree depth) */
+#define DDT_MAX_LK 8192 /* L * min(B, V) */
+
+int ddt_abi_version(void);
+const char* ddt_status_string(int status);
+
+/*
+ * Workspace. ddtree_build and ddtree_row_topk need a device scratch buffer of
+ * at least the size the matching *_workspace_size() returns. The buffer must
+ * be zero-filled before its first use and again whenever it is reused with a
+ * different shape (batch, L, V, B, dtype) or passed to the other call; every
+ * call that completes leaves it ready for the next call of the same shape.
+ * A workspace must not be used by two calls that can run concurrently.
+ */
+size_t ddtree_build_workspace_size(int64_t batch, int32_t L, int64_t V, int32_t B, int dtype);
+size_t ddtree_row_topk_workspace_size(int64_t rows, int64_t V, int32_t K, int dtype);
+
+/*
+ * ddtree_build -- stages 1 and 2 (and optionally 3) for a batch of requests.
+ *
+ * logits       [batch][L][V] drafter logits, bf16 (DDT_BF16) or float32
+ *              (DDT_F32), 16-byte aligned (DDT_EINVAL otherwise). Row d of a
+ *              request is draft position d+1. Finite values only.
+ * B            node budget, 1 <= B <= DDT_MAX_B. K = min(B, V) tokens per
+ *              row are ranked; 1 <= L <= DDT_MAX_L; L*K <= DDT_MAX_LK; and
+ *              L * ceil(log2 K) <= 122.
+ * Outputs, per request b:
+ *  tree_tokens [batch][B] int32  token of node j+1;
+ *  parents     [batch][B] int32  node number of node j+1's parent (0 = root);
+ *  logq        [batch][B] float  node's prefix log-probability;
+ *  depths      [batch][B] int32  node depth 1..L (may be NULL);
+ *  num_nodes   [batch]    int32  number of nodes emitted, min(B, number of
+ *              prefixes of length <= L over the top-K tokens);
+ *  mask        [batch][B+1][ceil((B+1)/64)] uint64 or NULL: the ancestor
+ *              mask of ddtree_mask, written by the same launch.
+ *  Entries j >= num_nodes hold token -1, parent -1, depth 0, logq -inf.
+ *
+ * Node selection. With z_d the log-sum-exp of row d and x_d[t] the logit of
+ * token t, a prefix (t_1..t_d) scores S - Z with S = x_1[t_1] + ... +
+ * x_d[t_d] and Z = z_1 + ... + z_d (float64, left to right), capped at its
+ * parent's score. The emitted nodes are the B highest-scoring prefixes; ties
+ * go to the lexicographically smaller tuple of per-row ranks (a prefix before
+ * its extensions), and tokens of equal logit within a row rank by lower id.
+ * The row normalisers are computed in float32/float64 on the device, so
+ * prefixes of different depths whose scores differ by less than about 1e-6
+ * may order differently than in exact arithmetic.
+ */
+int ddtree_build(const void* logits, int dtype, int64_t batch, int32_t L, int64_t V, int32_t B,
+                 int32_t* tree_tokens, int32_t* parents, float* logq, int32_t* depths,
+                 int32_t* num_nodes, uint64_t* mask, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/*
+ * ddtree_select -- stage 2 alone (plus the optional fused mask): the tree of
+ * ddtree_build from per-row tables, e.g. those of ddtree_row_topk.
+ * vals [batch][L][K] float and ids [batch][L][K] int32: each row's K largest
+ *      logits in descending order (equal values by ascending id) and their
+ *      token ids; lse [batch][L] double: the rows' log-sum-exp.
+ * 1 <= K <= DDT_MAX_B, L*K <= DDT_MAX_LK, L * ceil(log2 K) <= 122; with
+ * K = min(B, V) the result equals ddtree_build's (Lemma 1). Outputs and
+ * selection rule as in ddtree_build.
+ */
+int ddtree_select(const float* vals, const int32_t* ids, const double* lse, int64_t batch,
+                  int32_t L, int32_t K, int32_t B, int32_t* tree_tokens, int32_t* parents,
+                  float* logq, int32_t* depths, int32_t* num_nodes, uint64_t* mask,
+                  hipStream_t stream);
+
+/*
+ * ddtree_mask -- stage 3. Row i of request b has bit j (word j/64, bit j%64,
+ * LSB first) set iff node j is node i or one of its ancestors; node 0 (the
+ * root) is visible to every node. Rows i > num_nodes[b] are zero.
+ * parents   [batch][B] int32, as written by ddtree_build (parents[j] <= j);
+ * num_nodes [batch] int32 in [0, B];
+ * mask      [batch][B+1][ceil((B+1)/64)] uint64 output.
+ */
+int ddtree_mask(const int32_t* parents, const int32_t* num_nodes, int64_t batch, int32_t B,
+                uint64_t* mask, hipStream_t stream);
+
+/*
+ * ddtree_accept -- stage 4, the greedy walk. From the root, repeatedly move to
+ * the child whose token equals the target's choice at the current node, until
+ * no child matches. Siblings carry distinct tokens, so the walk is unique.
+ * target_tokens  [batch][B+1] int32: the target's argmax at each node
+ *                (index 0 = root);
+ * accepted_nodes [batch][L] int32: node numbers along the accepted path,
+ *                padded with -1;
+ * accept_len     [batch] int32: number of accepted draft tokens;
+ * next_token     [batch] int32: the target's token at the last accepted node
+ *                (the new bonus token). Committed tokens = accept_len + 1.
+ */
+int ddtree_accept(const int32_t* tree_tokens, const int32_t* parents, const int32_t* num_nodes,
+                  const int32_t* target_tokens, int64_t batch, int32_t B, int32_t L,
+                  int32_t* accepted_nodes, int32_t* accept_len, int32_t* next_token,
+                  hipStream_t stream);
+
+/*
+ * ddtree_row_topk -- stage 1 alone over `rows` independent rows of length V
+ * (logits as in ddtree_build: 16-byte aligned, finite).
+ * ids  [rows][K] int32 and vals [rows][K] float: the K largest logits of each
+ *      row in descending order, equal values by ascending id (-0 equals +0);
+ *      vals are the exact input values.
+ * lse  [rows] double: log sum_v exp(x[v]); per-element exponentials in
+ *      float32, sums combined in float64 (absolute error ~1e-6).
+ * 1 <= K <= min(V, DDT_MAX_B).
+ */
+int ddtree_row_topk(const void* logits, int dtype, int64_t rows, int64_t V, int32_t K,
+                    int32_t* ids, float* vals, double* lse, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DDTREE_H */

@@ -1,0 +1,123 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any launch."""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from draft_tree_construction_depth_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ddtree.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from draft_tree_construction_depth_amd import _build
+        _build.build_library()
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:ddt|ddtree)_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_operations():
+    names = declared_functions()
+    for n in ("ddtree_build", "ddtree_select", "ddtree_mask", "ddtree_accept", "ddtree_row_topk",
+              "ddtree_build_workspace_size", "ddtree_row_topk_workspace_size",
+              "ddt_status_string", "ddt_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.ddt_abi_version() == 1
+    assert _lib.status_string(0) == "ok"
+    assert _lib.status_string(-1) == "invalid argument"
+    assert _lib.status_string(-2) == "unsupported size"
+    assert _lib.status_string(-3) == "workspace too small"
+    assert _lib.status_string(-4) == "HIP launch failed"
+    assert _lib.status_string(-99) == "unknown status"
+
+
+def test_workspace_sizes(L):
+    s3 = L.ddtree_build_workspace_size(64, 15, 151936, 128, 0)
+    assert s3 > 64 * 15 * 128 * 8
+    assert L.ddtree_build_workspace_size(0, 15, 151936, 128, 0) == 0
+    assert L.ddtree_build_workspace_size(1, 15, 151936, 128, 7) == 0
+    assert L.ddtree_row_topk_workspace_size(960, 151936, 128, 0) > 0
+    # more rows never need less workspace
+    assert L.ddtree_build_workspace_size(256, 15, 151936, 256, 0) >= s3
+
+
+FAKE = C.c_void_p(0x100000)      # never dereferenced: every call below fails validation
+MISALIGNED = C.c_void_p(0x100004)
+
+
+def _build(L, logits=FAKE, dtype=0, batch=1, Lr=15, V=1024, B=32, out=FAKE, ws=FAKE,
+           ws_bytes=1 << 30):
+    return L.ddtree_build(logits, dtype, batch, Lr, V, B, out, out, out, out, out, out, ws,
+                          ws_bytes, None)
+
+
+def test_build_validation(L):
+    assert _build(L, logits=None) == -1
+    assert _build(L, out=None) == -1
+    assert _build(L, ws=None) == -1
+    assert _build(L, dtype=5) == -1
+    assert _build(L, B=0) == -1
+    assert _build(L, Lr=0) == -1
+    assert _build(L, V=0) == -1
+    assert _build(L, logits=MISALIGNED) == -1
+    assert _build(L, B=513) == -2
+    assert _build(L, Lr=33) == -2
+    assert _build(L, Lr=16, B=512, V=5000) == -2      # L*K over the supported size
+    assert _build(L, ws_bytes=16) == -3
+    assert _build(L, batch=0) == 0                     # empty batch: nothing to do
+
+
+def test_select_validation(L):
+    sel = lambda vals=FAKE, batch=1, Lr=15, K=128, B=128, out=FAKE: L.ddtree_select(
+        vals, FAKE, FAKE, batch, Lr, K, B, out, out, out, out, out, out, None)
+    assert sel(vals=None) == -1
+    assert sel(out=None) == -1
+    assert sel(K=0) == -1
+    assert sel(K=600) == -2
+    assert sel(Lr=16, K=512, B=512) == -2
+    assert sel(batch=0) == 0
+
+
+def test_mask_accept_topk_validation(L):
+    assert L.ddtree_mask(None, FAKE, 1, 32, FAKE, None) == -1
+    assert L.ddtree_mask(FAKE, FAKE, 1, 0, FAKE, None) == -1
+    assert L.ddtree_mask(FAKE, FAKE, 1, 600, FAKE, None) == -2
+    assert L.ddtree_mask(FAKE, FAKE, 0, 32, FAKE, None) == 0
+    assert L.ddtree_accept(FAKE, FAKE, FAKE, None, 1, 32, 15, FAKE, FAKE, FAKE, None) == -1
+    assert L.ddtree_accept(FAKE, FAKE, FAKE, FAKE, 1, 32, 0, FAKE, FAKE, FAKE, None) == -1
+    assert L.ddtree_accept(FAKE, FAKE, FAKE, FAKE, 1, 32, 40, FAKE, FAKE, FAKE, None) == -2
+    assert L.ddtree_accept(FAKE, FAKE, FAKE, FAKE, 0, 32, 15, FAKE, FAKE, FAKE, None) == 0
+    assert L.ddtree_row_topk(FAKE, 0, 4, 100, 200, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+    assert L.ddtree_row_topk(FAKE, 0, 4, 1000, 600, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -2
+    assert L.ddtree_row_topk(FAKE, 0, 4, 1000, 64, FAKE, FAKE, FAKE, FAKE, 8, None) == -3
+    assert L.ddtree_row_topk(MISALIGNED, 0, 4, 1000, 64, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                             None) == -1
+    assert L.ddtree_row_topk(FAKE, 0, 0, 1000, 64, FAKE, FAKE, FAKE, FAKE, 0, None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()

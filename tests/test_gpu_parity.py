@@ -1,0 +1,316 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every input is seeded and synthetic (draft_tree_construction_depth_amd.gen).
+Trees must match exactly up to the counted excuse classes of parity_util;
+stage-1 ids and values are bit-exact, row normalisers within 2e-6; masks and
+walks are bit-exact. The largest cases run at the full sizes of the workloads
+(batch 64 / 256, V = 151936) in the same launch configuration as bench.py.
+"""
+
+from __future__ import annotations
+
+import functools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import draft_tree_construction_depth_amd as pkg
+from draft_tree_construction_depth_amd import gen
+from oracle import oracle as O
+from parity_util import classify, compare_batch, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+F32, BF16 = gen.DTYPE_F32, gen.DTYPE_BF16
+THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@functools.lru_cache(maxsize=8)
+def _inputs(cfg, seed, batch=None, first=0):
+    return gen.make_logits(cfg, seed, batch=batch, first=first)
+
+
+@functools.lru_cache(maxsize=8)
+def _oracle(cfg, seed, batch=None, first=0):
+    c = gen.CONFIGS[cfg]
+    return O.build(_inputs(cfg, seed, batch, first), c["dtype"], c["B"], threads=THREADS)
+
+
+def _gpu_build(x, dt, B, **kw):
+    out = pkg.ddtree_build(to_device(x, dt), B, **kw)
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+# ----------------------------------------------------------------------------
+# stage 1
+# ----------------------------------------------------------------------------
+
+ROW_CASES = [
+    # rows, V, K, dtype, kind
+    (3, 1024, 32, F32, "gauss"),
+    (5, 1000, 64, BF16, "gauss"),
+    (4, 5003, 128, BF16, "gauss"),      # row length not a multiple of 16 bytes
+    (7, 40001, 256, F32, "gauss"),
+    (2, 151936, 512, BF16, "gauss"),
+    (3, 20000, 100, BF16, "ints"),      # heavy ties
+    (2, 9000, 300, F32, "const"),       # every value tied
+    (6, 3000, 1, BF16, "gauss"),
+    (1, 7, 7, F32, "ints"),             # K == V
+    (40, 151936, 128, BF16, "gauss"),
+]
+
+
+def _rows(rows, V, dt, kind, seed=0):
+    rng = np.random.default_rng(seed)
+    if kind == "gauss":
+        x = (rng.uniform(0.5, 8, (rows, 1)) * rng.standard_normal((rows, V))).astype(np.float32)
+    elif kind == "ints":
+        x = rng.integers(-3, 4, (rows, V)).astype(np.float32)
+        x[:, :5] = -0.0
+    else:
+        x = np.full((rows, V), 1.25, np.float32)
+    return gen.f32_to_bf16_bits(x) if dt == BF16 else x
+
+
+@pytest.mark.parametrize("case", ROW_CASES, ids=[f"{c[0]}x{c[1]}k{c[2]}d{c[3]}{c[4]}" for c in ROW_CASES])
+def test_row_topk_matches_oracle(case):
+    rows, V, K, dt, kind = case
+    _say("row_topk", case)
+    x = _rows(rows, V, dt, kind)
+    r = pkg.ddtree_row_topk(to_device(x, dt), K)
+    torch.cuda.synchronize()
+    ids, vals, lse = (r[k].cpu().numpy() for k in ("ids", "vals", "lse"))
+    for i in range(rows):
+        oi, ov = O.row_rank(x[i], dt, K)
+        np.testing.assert_array_equal(ids[i], oi, err_msg=f"row {i}")
+        np.testing.assert_array_equal(vals[i].astype(np.float64), ov, err_msg=f"row {i}")
+        assert abs(lse[i] - O.row_lse(x[i], dt)) < 2e-6
+
+
+def test_row_topk_full_batch64_tables():
+    # The 960 rows of the batch-64 workload, in its own launch configuration.
+    x = _inputs(3, 0)
+    o = _oracle(3, 0)
+    _say("row_topk c3 full")
+    r = pkg.ddtree_row_topk(to_device(x, BF16), 128)
+    torch.cuda.synchronize()
+    ids = r["ids"].cpu().numpy().reshape(64, 15, 128)
+    vals = r["vals"].cpu().numpy().reshape(64, 15, 128)
+    lse = r["lse"].cpu().numpy().reshape(64, 15)
+    np.testing.assert_array_equal(ids, o["top_ids"])
+    np.testing.assert_array_equal(vals.astype(np.float64), o["top_vals"])
+    assert np.abs(lse - o["z"]).max() < 2e-6
+
+
+# ----------------------------------------------------------------------------
+# stage 2 (+3): whole build against the oracle
+# ----------------------------------------------------------------------------
+
+def _check_counts(res, label):
+    _say(label, res["counts"])
+    assert not res["fails"], f"{label}: {res['fails'][:5]}"
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_build_c1(seed):
+    x = _inputs(1, seed)
+    g = _gpu_build(x, F32, 32)
+    o = _oracle(1, seed)
+    res = compare_batch(g, o, 32)
+    _check_counts(res, f"c1 seed {seed}")
+    assert res["counts"].get("exact", 0) == 1
+    np.testing.assert_array_equal(g["mask"], O.mask(o["parents"], o["num_nodes"], 32))
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_build_c2(seed):
+    x = _inputs(2, seed)
+    g = _gpu_build(x, BF16, 64)
+    o = _oracle(2, seed)
+    _check_counts(compare_batch(g, o, 64), f"c2 seed {seed}")
+
+
+def test_build_c3_full_batch():
+    x = _inputs(3, 0)
+    g = _gpu_build(x, BF16, 128)
+    o = _oracle(3, 0)
+    res = compare_batch(g, o, 128)
+    _check_counts(res, "c3 seed 0 (64 requests)")
+    exact = [b for b in range(64) if classify({k: v[b:b + 1] for k, v in g.items()},
+                                              {k: v[b:b + 1] for k, v in o.items()}, 0, 128) == "exact"]
+    om = O.mask(o["parents"][exact], o["num_nodes"][exact], 128)
+    np.testing.assert_array_equal(g["mask"][exact], om)
+
+
+def test_build_c5_full_batch_sampled():
+    # The GPU builds all 256 trees; the oracle checks a 32-request sample.
+    x = _inputs(5, 0)
+    g = _gpu_build(x, BF16, 256)
+    idx = np.arange(0, 256, 8)
+    o = O.build(np.ascontiguousarray(x[idx]), BF16, 256, threads=THREADS)
+    _check_counts(compare_batch(g, o, 256, idx=idx), "c5 seed 0 (32 of 256 requests)")
+
+
+@pytest.mark.parametrize("seed", range(1, 4))
+def test_build_c3_small_batches(seed):
+    # A few requests of the batch-64 workload (smaller launch shape).
+    x = _inputs(3, seed, batch=3)
+    g = _gpu_build(x, BF16, 128)
+    o = _oracle(3, seed, batch=3)
+    _check_counts(compare_batch(g, o, 128), f"c3 seed {seed} batch 3")
+
+
+EDGE = [
+    # name, L, V, B, dtype, kind
+    ("V_below_B", 4, 20, 64, F32, "gauss"),
+    ("budget_beyond_prefixes", 3, 3, 100, F32, "gauss"),
+    ("L1", 1, 5000, 32, BF16, "gauss"),
+    ("B1", 15, 5000, 1, BF16, "gauss"),
+    ("const_rows", 6, 4000, 48, BF16, "const"),
+    ("const_rows_V_below_B", 5, 30, 128, F32, "const"),
+    ("int_ties", 8, 3001, 96, F32, "ints"),
+    ("one_hot", 5, 1000, 40, F32, "onehot"),
+    ("unaligned_V", 15, 10001, 128, BF16, "gauss"),
+    ("L32_K8", 32, 8, 8, F32, "gauss"),
+    ("B512_L13", 13, 5000, 512, BF16, "gauss"),
+]
+
+
+def _edge_logits(L, V, dt, kind, batch, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "gauss":
+        x = (rng.uniform(0.3, 4, (batch, L, 1)) * rng.standard_normal((batch, L, V))).astype(np.float32)
+    elif kind == "const":
+        x = np.full((batch, L, V), -2.0, np.float32)
+    elif kind == "ints":
+        x = rng.integers(-2, 3, (batch, L, V)).astype(np.float32)
+    else:
+        x = np.full((batch, L, V), -900.0, np.float32)
+        x[:, :, 3] = rng.uniform(-5, 5, (batch, L)).astype(np.float32)
+        x[:, ::2, 7] = x[:, ::2, 3] - 0.5
+    return gen.f32_to_bf16_bits(x) if dt == BF16 else x
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[e[0] for e in EDGE])
+def test_build_edge_cases(case):
+    name, L, V, B, dt, kind = case
+    _say("edge", name)
+    x = _edge_logits(L, V, dt, kind, 3, seed=len(name))
+    g = _gpu_build(x, dt, B)
+    o = O.build(x, dt, B)
+    _check_counts(compare_batch(g, o, B), name)
+    om = O.mask(o["parents"], o["num_nodes"], B)
+    for b in range(3):
+        if classify({k: v[b:b + 1] for k, v in g.items()}, {k: v[b:b + 1] for k, v in o.items()},
+                    0, B) == "exact":
+            np.testing.assert_array_equal(g["mask"][b], om[b])
+
+
+def test_build_is_deterministic_and_reuses_workspace():
+    x = _inputs(3, 1, batch=64)
+    d = to_device(x, BF16)
+    a = to_host(pkg.ddtree_build(d, 128))
+    for _ in range(3):
+        b = to_host(pkg.ddtree_build(d, 128))
+        for k in a:
+            np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_build_rejects_bad_arguments():
+    d = to_device(_inputs(1, 0), F32)
+    with pytest.raises(pkg.DDTreeError) as e:
+        pkg.ddtree_build(d, 1000)
+    assert e.value.status == -2
+
+
+# ----------------------------------------------------------------------------
+# stages 3 and 4 on oracle trees
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg,seed", [(1, 0), (2, 0), (3, 2)])
+def test_mask_kernel_on_oracle_trees(cfg, seed):
+    B = gen.CONFIGS[cfg]["B"]
+    o = _oracle(cfg, seed, batch=min(4, gen.CONFIGS[cfg]["batch"]))
+    m = pkg.ddtree_mask(torch.from_numpy(o["parents"]).to(DEV),
+                        torch.from_numpy(o["num_nodes"]).to(DEV), B)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(m.cpu().numpy().view(np.uint64),
+                                  O.mask(o["parents"], o["num_nodes"], B))
+
+
+def _walk_both(o, tgt, L):
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    r = pkg.ddtree_accept(dv(o["tree_tokens"]), dv(o["parents"]), dv(o["num_nodes"]), dv(tgt), L)
+    torch.cuda.synchronize()
+    ga = [r[k].cpu().numpy() for k in ("accepted_nodes", "accept_len", "next_token")]
+    oa = O.accept(o["tree_tokens"], o["parents"], o["num_nodes"], tgt, L)
+    for a, b in zip(ga, oa):
+        np.testing.assert_array_equal(a, b)
+    return ga
+
+
+def test_walk_c1_fresh_argmax_targets():
+    for seed in range(5):
+        o = _oracle(1, seed)
+        tgt = gen.fresh_argmax_targets(1, seed, 1, 32, 1024)
+        _walk_both(o, tgt, 15)
+
+
+def test_walk_c3_drafter_targets_full_batch():
+    x = _inputs(3, 0)
+    o = _oracle(3, 0)
+    Y = gen.drafter_draws(3, 0, x, BF16)
+    tgt = gen.node_targets_from_depths(Y, o["depths"], o["num_nodes"], 128)
+    _, alen, _ = _walk_both(o, tgt, 15)
+    _say("c3 accept_len mean", float(alen.mean()))
+
+
+def test_prop1_monte_carlo_through_gpu_walk():
+    # Proposition 1 (DDTree explainer, section 3): E[accepted] = sum_u q(u),
+    # with the walk run on the GPU over 2e5 draws Y ~ Q.
+    rng = np.random.default_rng(11)
+    L, V, B, N = 6, 12, 24, 200000
+    x = (rng.uniform(0.5, 2.5) * rng.standard_normal((1, L, V))).astype(np.float32)
+    g = _gpu_build(x, F32, B)
+    o = O.build(x, F32, B)
+    assert classify(g, o, 0, B) == "exact"
+    from scipy.special import log_softmax
+    p = np.exp(log_softmax(x[0].astype(np.float64), axis=1))
+    Y = np.empty((N, L + 1), np.int64)
+    for d in range(L):
+        Y[:, d] = np.minimum(np.searchsorted(np.cumsum(p[d]), rng.random(N), side="right"), V - 1)
+    Y[:, L] = 0
+    n = int(g["num_nodes"][0])
+    dep = np.concatenate([[0], g["depths"][0]])
+    tgt = Y[:, dep].astype(np.int32)
+    tgt[:, n + 1:] = 0
+    rep = lambda a: torch.from_numpy(np.repeat(a, N, axis=0)).to(DEV)
+    r = pkg.ddtree_accept(rep(g["tree_tokens"]), rep(g["parents"]), rep(g["num_nodes"]),
+                          torch.from_numpy(tgt).to(DEV), L)
+    alen = r["accept_len"].cpu().numpy()
+    expected = float(np.exp(o["score64"][0, :n]).sum())
+    se = alen.std() / math.sqrt(N)
+    assert abs(alen.mean() - expected) < 5 * se
+
+
+@pytest.mark.parametrize("a,g,printed", [(0.5, 4, 1.94), (0.5, 8, 2.00), (0.8, 4, 3.4)])
+def test_chain_closed_form_through_gpu(a, g, printed):
+    # DSpark guide page: tokens per pass (1 - a^(g+1)) / (1 - a).
+    V = 10 if (a, g) != (0.5, 8) else 256
+    row = np.full(V, math.log((1 - a) / (V - 1)))
+    row[0] = math.log(a)
+    x = np.tile(row.astype(np.float32), (1, g, 1))
+    t = _gpu_build(x, F32, g)
+    assert list(t["depths"][0]) == list(range(1, g + 1))
+    assert list(t["parents"][0]) == list(range(g))
+    tokens = 1.0 + float(np.exp(t["logq"][0].astype(np.float64)).sum())
+    assert tokens == pytest.approx((1 - a ** (g + 1)) / (1 - a), abs=1e-5)
+    assert round(tokens, 2 if printed != 3.4 else 1) == pytest.approx(printed)
