@@ -66,6 +66,26 @@ def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
 
 
+def _arg(t, name, dtypes, shape=None):
+    """Check that a tensor argument is a contiguous device tensor of the
+    expected dtype (and shape); the library reads raw row-major memory."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype {' or '.join(map(str, dtypes))}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+_I32 = (torch.int32,)
+_LOGITS = (torch.bfloat16, torch.float32)
+
+
 def _stream(device):
     return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
@@ -103,7 +123,9 @@ def workspace(kind: str, size: int, device, key) -> torch.Tensor:
 def ddtree_build(logits: torch.Tensor, B: int, *, with_mask: bool = True, out: dict | None = None,
                  ws: torch.Tensor | None = None) -> dict:
     """Stages 1-2 (+3): logits [batch, L, V] (bf16/f32, cuda) -> tree tensors."""
-    assert logits.is_cuda and logits.dim() == 3 and logits.is_contiguous()
+    _arg(logits, "logits", _LOGITS)
+    if logits.dim() != 3:
+        raise ValueError("logits must be [batch, L, V]")
     batch, L, V = logits.shape
     dev = logits.device
     dt = _dtype_code(logits)
@@ -136,7 +158,10 @@ def _tree_out(batch, B, dev, with_mask):
 def ddtree_select(vals: torch.Tensor, ids: torch.Tensor, lse: torch.Tensor, B: int, *,
                   with_mask: bool = True, out: dict | None = None) -> dict:
     """Stage 2 (+3) from tables vals/ids [batch, L, K] and lse [batch, L]."""
+    _arg(vals, "vals", (torch.float32,))
     batch, L, K = vals.shape
+    _arg(ids, "ids", _I32, (batch, L, K))
+    _arg(lse, "lse", (torch.float64,), (batch, L))
     if out is None:
         out = _tree_out(batch, B, vals.device, with_mask)
     rc = lib().ddtree_select(_ptr(vals), _ptr(ids), _ptr(lse), batch, L, K, B,
@@ -149,7 +174,9 @@ def ddtree_select(vals: torch.Tensor, ids: torch.Tensor, lse: torch.Tensor, B: i
 
 def ddtree_mask(parents: torch.Tensor, num_nodes: torch.Tensor, B: int,
                 mask: torch.Tensor | None = None) -> torch.Tensor:
+    _arg(num_nodes, "num_nodes", _I32)
     batch = num_nodes.shape[0]
+    _arg(parents, "parents", _I32, (batch, B))
     W = (B + 1 + 63) // 64
     if mask is None:
         mask = torch.empty((batch, B + 1, W), dtype=torch.int64, device=parents.device)
@@ -161,7 +188,11 @@ def ddtree_mask(parents: torch.Tensor, num_nodes: torch.Tensor, B: int,
 
 def ddtree_accept(tree_tokens: torch.Tensor, parents: torch.Tensor, num_nodes: torch.Tensor,
                   target_tokens: torch.Tensor, L: int, out: dict | None = None) -> dict:
+    _arg(tree_tokens, "tree_tokens", _I32)
     batch, B = tree_tokens.shape
+    _arg(parents, "parents", _I32, (batch, B))
+    _arg(num_nodes, "num_nodes", _I32, (batch,))
+    _arg(target_tokens, "target_tokens", _I32, (batch, B + 1))
     dev = tree_tokens.device
     if out is None:
         out = dict(accepted_nodes=torch.empty((batch, L), dtype=torch.int32, device=dev),
@@ -177,7 +208,7 @@ def ddtree_accept(tree_tokens: torch.Tensor, parents: torch.Tensor, num_nodes: t
 def ddtree_row_topk(logits: torch.Tensor, K: int, *, out: dict | None = None,
                     ws: torch.Tensor | None = None) -> dict:
     """Stage 1 alone: logits [..., V] -> ids/vals [rows, K], lse [rows] (float64)."""
-    assert logits.is_cuda and logits.is_contiguous()
+    _arg(logits, "logits", _LOGITS)
     V = logits.shape[-1]
     rows = logits.numel() // V
     dev = logits.device

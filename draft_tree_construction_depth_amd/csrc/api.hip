@@ -17,51 +17,78 @@ int elems_per_vec(int dtype) { return dtype == DDT_BF16 ? 8 : 4; }
 size_t elem_size(int dtype) { return dtype == DDT_BF16 ? 2 : 4; }
 
 struct S1Plan {
+  bool row;       // one workgroup per row (double-buffered chunks), no merge
   int nv;         // 16-byte vectors per thread
-  int64_t chunk;  // elements per chunk
+  int64_t chunk;  // elements per chunk (256 * nv * elements per vector)
   int S;          // chunks per row
+  int capp;       // candidate slots per chunk record
+  bool ok;        // a supported geometry exists
 };
 
+int groups_per_thread(int nv) { return nv == 2 ? 1 : nv / 4; }
 
-// Chunk geometry: big register-resident chunks (16 vectors per thread) when
-// the grid already has >= 1024 blocks; smaller chunks for few rows, so that
-// a single request still spreads over the 256 CUs.
-S1Plan plan_stage1(int64_t rows, int64_t V, int dtype) {
+// Chunk geometry. Big register-resident chunks (16 vectors per thread) once
+// the grid has >= 1024 blocks; smaller chunks for few rows, so that a single
+// request still spreads over the 256 CUs. Then grow the chunk until the row
+// merge can hold every record
+// (S * capp <= 64 * kMergeSlots register slots with capp >= K, S <= 64) and
+// each wave has >= K/2 group maxima for its threshold.
+S1Plan plan_stage1(int64_t rows, int64_t V, int dtype, int K) {
   const int epv = elems_per_vec(dtype);
-  // Rows whose byte length is not a multiple of 16 use element loads, which
-  // only the smaller chunk shapes can hold in registers.
   const bool vec_rows = ((size_t)V * elem_size(dtype)) % 16 == 0;
   auto nchunks = [&](int nv) {
     const int64_t cap = (int64_t)ddt::kS1Threads * nv * epv;
     return (V + cap - 1) / cap;
   };
-  int nv = 16;
-  if (!vec_rows || rows * nchunks(16) < 1024) nv = 4;
-  if (nv == 4 && rows * nchunks(4) < 256) nv = 2;
   S1Plan p;
-  p.nv = nv;
-  p.S = (int)nchunks(nv);
-  int64_t c = (V + p.S - 1) / p.S;
-  p.chunk = (c + epv - 1) / epv * epv;
-  return p;
+  p.ok = false;
+  p.row = false;
+  // Many rows: one workgroup per row, 8 vectors per thread per chunk, double
+  // buffered (every CU holds >= 2 rows in flight).
+  if (vec_rows && rows >= 512) {
+    p.row = true;
+    p.nv = 8;
+    p.chunk = (int64_t)ddt::kS1Threads * 8 * epv;
+    p.S = (int)nchunks(8);
+    p.capp = 0;
+    p.ok = true;
+    return p;
+  }
+  const int max_nv = vec_rows ? 16 : 8;
+  int nv = 2;
+  if (rows * nchunks(4) >= 256) nv = 4;
+  if (rows * nchunks(8) >= 512) nv = 8;
+  if (rows * nchunks(16) >= 1024) nv = 16;
+  if (nv > max_nv) nv = max_nv;
+  for (;; nv *= 2) {
+    if (nv > max_nv) return p;
+    const int64_t S = nchunks(nv);
+    if (S > 64) continue;
+    const int64_t slots = (int64_t)ddt::kWave * ddt::kMergeSlots;
+    const int64_t capp = 2 * (int64_t)K < slots / S ? 2 * (int64_t)K : slots / S;
+    if (capp < K) continue;
+    if (64 * groups_per_thread(nv) * 2 < K && nv < max_nv) continue;
+    p.nv = nv;
+    p.S = (int)S;
+    p.chunk = (int64_t)ddt::kS1Threads * nv * epv;
+    p.capp = (int)capp;
+    p.ok = true;
+    return p;
+  }
 }
 
 struct S1Layout {
-  size_t ctr, keys, ms, end;
+  size_t cnt, thr, meta, cands, end;
 };
 
-S1Layout s1_layout(int64_t rows, const S1Plan& pl, int K, size_t base) {
+S1Layout s1_layout(int64_t rows, const S1Plan& pl, size_t base) {
   S1Layout l;
-  l.ctr = base;
-  size_t off = align_up(base + (size_t)rows * sizeof(uint32_t));
-  l.keys = off;
-  l.ms = off;
-  if (pl.S > 1) {
-    off = align_up(off + (size_t)rows * pl.S * K * sizeof(uint64_t));
-    l.ms = off;
-    off = align_up(off + (size_t)rows * pl.S * 2 * sizeof(double));
-  }
-  l.end = off;
+  const size_t recs = pl.row ? 0 : (size_t)rows * pl.S;
+  l.cnt = base + kAlign;  // a small header keeps every valid size positive
+  l.thr = align_up(l.cnt + recs * sizeof(int32_t));
+  l.meta = align_up(l.thr + recs * sizeof(uint32_t));
+  l.cands = align_up(l.meta + recs * 2 * sizeof(double));
+  l.end = align_up(l.cands + recs * pl.capp * sizeof(uint64_t));
   return l;
 }
 
@@ -74,7 +101,7 @@ BuildLayout build_layout(int64_t batch, int32_t L, int64_t V, int32_t B, int dty
   const int64_t rows = batch * L;
   const int K = (int)(B < V ? B : V);
   BuildLayout l;
-  l.s1 = s1_layout(rows, plan_stage1(rows, V, dtype), K, 0);
+  l.s1 = s1_layout(rows, plan_stage1(rows, V, dtype, K), 0);
   size_t off = l.s1.end;
   l.vals = off;
   off = align_up(off + (size_t)rows * K * sizeof(float));
@@ -86,22 +113,49 @@ BuildLayout build_layout(int64_t batch, int32_t L, int64_t V, int32_t B, int dty
   return l;
 }
 
+template <int DT, int NV, int GS>
+void launch_chunks(bool aligned, dim3 grid, const ddt::Stage1Params& prm, hipStream_t st) {
+  if (aligned) {
+    hipLaunchKernelGGL((ddt::stage1_chunk_kernel<DT, NV, GS, true>), grid,
+                       dim3(ddt::kS1Threads), 0, st, prm);
+  } else {
+    hipLaunchKernelGGL((ddt::stage1_chunk_kernel<DT, NV, GS, false>), grid,
+                       dim3(ddt::kS1Threads), 0, st, prm);
+  }
+}
+
 template <int DT>
 hipError_t launch_stage1_dt(const S1Plan& pl, bool aligned, int64_t rows,
                             const ddt::Stage1Params& prm, hipStream_t st) {
-  const dim3 grid((unsigned)(rows * pl.S)), block(ddt::kS1Threads);
-  if (pl.nv == 16) {
-    // plan_stage1 picks 16 vectors per thread only for 16-byte multiple rows.
-    if (!aligned) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((ddt::stage1_kernel<DT, 16, 4, true>), grid, block, 0, st, prm);
-  } else if (pl.nv == 4) {
-    if (aligned) hipLaunchKernelGGL((ddt::stage1_kernel<DT, 4, 4, true>), grid, block, 0, st, prm);
-    else hipLaunchKernelGGL((ddt::stage1_kernel<DT, 4, 4, false>), grid, block, 0, st, prm);
-  } else {
-    if (aligned) hipLaunchKernelGGL((ddt::stage1_kernel<DT, 2, 2, true>), grid, block, 0, st, prm);
-    else hipLaunchKernelGGL((ddt::stage1_kernel<DT, 2, 2, false>), grid, block, 0, st, prm);
+  if (pl.row) {
+    hipLaunchKernelGGL((ddt::stage1_row_kernel<DT, 8, 4>), dim3((unsigned)rows),
+                       dim3(ddt::kS1Threads), 0, st, prm);
+    return hipGetLastError();
   }
+  const dim3 grid((unsigned)(rows * pl.S));
+  switch (pl.nv) {
+    case 16:
+      // plan_stage1 picks 16 vectors per thread only for 16-byte multiple rows
+      if (!aligned) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((ddt::stage1_chunk_kernel<DT, 16, 4, true>), grid,
+                         dim3(ddt::kS1Threads), 0, st, prm);
+      break;
+    case 8: launch_chunks<DT, 8, 4>(aligned, grid, prm, st); break;
+    case 4: launch_chunks<DT, 4, 4>(aligned, grid, prm, st); break;
+    default: launch_chunks<DT, 2, 2>(aligned, grid, prm, st); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 mgrid((unsigned)((rows + ddt::kMergeWaves - 1) / ddt::kMergeWaves));
+  hipLaunchKernelGGL((ddt::stage1_merge_kernel<DT>), mgrid, dim3(ddt::kWave * ddt::kMergeWaves),
+                     0, st, prm);
   return hipGetLastError();
+}
+
+int ceil_log2_64(int64_t x) {
+  int b = 0;
+  while (((int64_t)1 << b) < x) ++b;
+  return b;
 }
 
 hipError_t launch_stage1(int dtype, const S1Plan& pl, const void* logits, int64_t rows,
@@ -114,9 +168,12 @@ hipError_t launch_stage1(int dtype, const S1Plan& pl, const void* logits, int64_
   prm.chunk = pl.chunk;
   prm.S = pl.S;
   prm.K = K;
-  prm.part_keys = (uint64_t*)(ws + lay.keys);
-  prm.part_ms = (double*)(ws + lay.ms);
-  prm.row_ctr = (uint32_t*)(ws + lay.ctr);
+  prm.capp = pl.capp;
+  prm.idbits = ceil_log2_64(V) < 1 ? 1 : ceil_log2_64(V);
+  prm.cnt = (int32_t*)(ws + lay.cnt);
+  prm.thr = (uint32_t*)(ws + lay.thr);
+  prm.meta = (double*)(ws + lay.meta);
+  prm.cands = (uint64_t*)(ws + lay.cands);
   prm.out_ids = ids;
   prm.out_vals = vals;
   prm.out_lse = lse;
@@ -178,8 +235,9 @@ const char* ddt_status_string(int status) {
 }
 
 size_t ddtree_row_topk_workspace_size(int64_t rows, int64_t V, int32_t K, int dtype) {
-  if (rows <= 0 || V <= 0 || K <= 0 || !valid_dtype(dtype)) return 0;
-  return s1_layout(rows, plan_stage1(rows, V, dtype), K, 0).end;
+  if (rows <= 0 || V <= 0 || K <= 0 || K > V || !valid_dtype(dtype)) return 0;
+  const S1Plan pl = plan_stage1(rows, V, dtype, K);
+  return pl.ok ? s1_layout(rows, pl, 0).end : 0;
 }
 
 int ddtree_row_topk(const void* logits, int dtype, int64_t rows, int64_t V, int32_t K,
@@ -191,9 +249,9 @@ int ddtree_row_topk(const void* logits, int dtype, int64_t rows, int64_t V, int3
   if (!logits || !ids || !vals || !lse || !workspace) return DDT_EINVAL;
   if ((uintptr_t)logits % 16 != 0) return DDT_EINVAL;
   if (K > DDT_MAX_B || V > 0x7FFFFFFFLL) return DDT_ENOTSUP;
-  const S1Plan pl = plan_stage1(rows, V, dtype);
-  if (rows * pl.S > 0x7FFFFFFFLL) return DDT_ENOTSUP;
-  const S1Layout lay = s1_layout(rows, pl, K, 0);
+  const S1Plan pl = plan_stage1(rows, V, dtype, K);
+  if (!pl.ok || rows * pl.S > 0x7FFFFFFFLL) return DDT_ENOTSUP;
+  const S1Layout lay = s1_layout(rows, pl, 0);
   if (workspace_bytes < lay.end) return DDT_EWORKSPACE;
   const hipError_t e = launch_stage1(dtype, pl, logits, rows, V, K, lay, (char*)workspace, ids,
                                      vals, lse, stream);
@@ -202,6 +260,8 @@ int ddtree_row_topk(const void* logits, int dtype, int64_t rows, int64_t V, int3
 
 size_t ddtree_build_workspace_size(int64_t batch, int32_t L, int64_t V, int32_t B, int dtype) {
   if (batch <= 0 || L <= 0 || V <= 0 || B <= 0 || !valid_dtype(dtype)) return 0;
+  const int K = (int)(B < V ? B : V);
+  if (!plan_stage1(batch * L, V, dtype, K).ok) return 0;
   return build_layout(batch, L, V, B, dtype).end;
 }
 
@@ -219,8 +279,8 @@ int ddtree_build(const void* logits, int dtype, int64_t batch, int32_t L, int64_
   const int bpd = ceil_log2(K) < 1 ? 1 : ceil_log2(K);
   if ((int64_t)L * K > DDT_MAX_LK || L * bpd > 122) return DDT_ENOTSUP;
   const int64_t rows = batch * L;
-  const S1Plan pl = plan_stage1(rows, V, dtype);
-  if (rows * pl.S > 0x7FFFFFFFLL || batch > 0x7FFFFFFFLL) return DDT_ENOTSUP;
+  const S1Plan pl = plan_stage1(rows, V, dtype, K);
+  if (!pl.ok || rows * pl.S > 0x7FFFFFFFLL || batch > 0x7FFFFFFFLL) return DDT_ENOTSUP;
   const BuildLayout lay = build_layout(batch, L, V, B, dtype);
   if (workspace_bytes < lay.end) return DDT_EWORKSPACE;
   char* ws = (char*)workspace;

@@ -229,6 +229,15 @@ def test_build_rejects_bad_arguments():
     with pytest.raises(pkg.DDTreeError) as e:
         pkg.ddtree_build(d, 1000)
     assert e.value.status == -2
+    with pytest.raises(ValueError, match="contiguous"):
+        pkg.ddtree_build(d.transpose(1, 2).contiguous().transpose(1, 2), 32)
+    t = pkg.ddtree_build(d, 32)
+    bad_tgt = torch.zeros((33, 2), dtype=torch.int32, device=DEV).t()[:1]
+    with pytest.raises(ValueError, match="contiguous"):
+        pkg.ddtree_accept(t["tree_tokens"], t["parents"], t["num_nodes"], bad_tgt, 15)
+    with pytest.raises(TypeError):
+        pkg.ddtree_accept(t["tree_tokens"], t["parents"], t["num_nodes"],
+                          torch.zeros((1, 33), dtype=torch.int64, device=DEV), 15)
 
 
 # ----------------------------------------------------------------------------
@@ -290,7 +299,7 @@ def test_prop1_monte_carlo_through_gpu_walk():
     Y[:, L] = 0
     n = int(g["num_nodes"][0])
     dep = np.concatenate([[0], g["depths"][0]])
-    tgt = Y[:, dep].astype(np.int32)
+    tgt = np.ascontiguousarray(Y[:, dep], dtype=np.int32)
     tgt[:, n + 1:] = 0
     rep = lambda a: torch.from_numpy(np.repeat(a, N, axis=0)).to(DEV)
     r = pkg.ddtree_accept(rep(g["tree_tokens"]), rep(g["parents"]), rep(g["num_nodes"]),
