@@ -499,77 +499,252 @@ __global__ __launch_bounds__(kWave* kMergeWaves) void stage1_merge_kernel(Stage1
 }
 
 // ---------------------------------------------------------------------------
-// Row-persistent kernel (one workgroup per row).
+// Row-persistent kernel (one workgroup per row, no barrier inside the loop).
+//
+// Claims. Each wave keeps in registers the largest 32-element group maxima it
+// has seen in its part of the row (at most 64 * kListRegs of them) and
+// publishes in LDS the largest value key T with >= ceil(K/4) of them at or
+// above T. A claim certifies ceil(K/4) distinct row elements >= T in that
+// wave's part, so the smallest of the four claims certifies >= K elements:
+// the row's K-th largest value is at or above it. Claims only grow, so a
+// wave may read the others' claims without a barrier (a stale claim is a
+// smaller, still valid, one); only the first chunk waits for all four.
+// Keeping. A 16-byte vector whose maximum reaches the running threshold is
+// copied, with its position, into the wave's LDS region (one ballot per
+// vector, no per-element work). After the last chunk the kept vectors are
+// filtered against the final threshold and the exact top K is selected.
+// Normaliser. Per thread, terms 2^(x*c - mc) with an integer offset mc =
+// ceil(m*c) of the running maximum m: every exponent argument is <= ~0 and
+// raising the offset rescales the float64 sum exactly (ldexp). Each chunk
+// takes a max pass (vector maxima, which also feed the claims and the keep
+// test) and an exponent pass.
+// Loads. Every 16-byte load is a buffer load whose resource covers one 4 KiB
+// slab of the row (its bytes left, clamped): vectors past the row's end read
+// as zero without touching memory and are then set to -inf.
+
+constexpr int kVecCap = 256;  // kept vectors per wave
+constexpr int kKeyCap = 512;  // candidate keys per wave after the final filter
+constexpr int kListRegs = 2;  // list of 64 * kListRegs group maxima per wave (>= ceil(K/4))
 
 struct RowSmem {
-  uint64_t cand[kCandCap];
+  v4u32 vec[kS1Waves][kVecCap];       // kept vectors (later: the finish's staging area)
+  uint32_t vpos[kS1Waves][kVecCap];   // index of each kept vector's first element
+  uint64_t keys[kS1Waves][kKeyCap];   // final candidates (main loop: list compaction)
+  uint32_t claim[kS1Waves];
+  uint32_t red_u[kS1Waves];
   double red_d[kS1Waves];
-  uint32_t red_u[2][kS1Waves];
   int wn[kS1Waves];
 };
 
-// Loads are issued unconditionally so that the wait counts stay static: a
-// chunk past the row's end (nvec == 0) loads one vector of the row's start in
-// every lane, which costs one cache line per wave.
-template <int NV>
-__device__ __forceinline__ void load_chunk_vec(v4u32 (&buf)[NV], const char* rowp, int64_t c0,
-                                               int64_t nvec, size_t esz) {
-  const gvec_ptr base = (gvec_ptr)(rowp + (nvec > 0 ? c0 * esz : 0));
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int vi = j * kS1Threads + threadIdx.x;
-    buf[j] = base[vi < nvec ? vi : 0];
+__device__ __forceinline__ float fmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+template <int DT>
+__device__ __forceinline__ float vec_max(const float (&x)[DT == 0 ? 8 : 4]) {
+  if constexpr (DT == 0) {
+    const float a = fmax3(x[0], x[1], x[2]);
+    const float b = fmax3(x[3], x[4], x[5]);
+    return fmax3(fmax3(a, x[6], x[7]), b, b);
+  } else {
+    return fmax3(fmax3(x[0], x[1], x[2]), x[3], x[3]);
   }
 }
 
-// One register-resident chunk of the row: fold it into the thread's running
-// (max, offset, sum), raise the row threshold `rthr` with this chunk's
-// threshold and append the chunk's elements at or above it.
-template <int DT, int NV, int GS>
-__device__ __forceinline__ void row_process(v4u32 (&raw)[NV], RowSmem& sm, int par, int64_t c0,
-                                            int64_t nvec, int K, float& m_run, float& mc_run,
-                                            double& s_run, uint32_t& rthr, int& wn) {
+// Chunk loads: slab j of the chunk (256 threads x 16 B) through its own
+// buffer resource; the thread's offset is the same for every slab.
+template <int NV>
+__device__ __forceinline__ void load_chunk_buf(v4u32 (&buf)[NV], const char* rowp,
+                                               int64_t cbyte, int64_t rowbytes) {
+  const int voff = (int)threadIdx.x * 16;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int64_t off = cbyte + (int64_t)j * kS1Threads * 16;
+    const int64_t left = rowbytes - off;
+    const int nrec = left <= 0 ? 0 : (left >= kS1Threads * 16 ? kS1Threads * 16 : (int)left);
+    __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(rowp + (left > 0 ? off : 0)), (short)0, nrec,
+                                          0x00020000);
+    buf[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
+  }
+}
+
+// Vector maxima of a register-resident chunk.
+template <int DT, int NV>
+__device__ __forceinline__ void max_pass(v4u32 (&raw)[NV], float (&vmax)[NV]) {
+  constexpr int EPV = DT == 0 ? 8 : 4;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    asm volatile("" : "+v"(raw[j]));  // convert, use and drop vector j before j+1
+    float x[EPV];
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) x[e] = __uint_as_float(elem_bits<DT>(raw[j], e));
+    vmax[j] = vec_max<DT>(x);
+  }
+}
+
+// The thread's sum of 2^(x*c - mc) over the chunk: 8-term sums per vector,
+// then pairwise over vectors.
+template <int DT, int NV>
+__device__ __forceinline__ float exp_pass(v4u32 (&raw)[NV], float mc) {
+  constexpr int EPV = DT == 0 ? 8 : 4;
+  static_assert(NV <= 16 && (NV & (NV - 1)) == 0, "pairwise levels");
+  float lvl[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float total = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    asm volatile("" : "+v"(raw[j]));
+    float a = __builtin_amdgcn_exp2f(__builtin_fmaf(__uint_as_float(elem_bits<DT>(raw[j], 0)),
+                                                    kLog2eF, -mc));
+#pragma unroll
+    for (int e = 1; e < EPV; ++e)
+      a += __builtin_amdgcn_exp2f(__builtin_fmaf(__uint_as_float(elem_bits<DT>(raw[j], e)),
+                                                 kLog2eF, -mc));
+    asm volatile("" : "+v"(a));
+    int L = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (L == b && ((j >> b) & 1)) {
+        a += lvl[b];
+        L = b + 1;
+      }
+    }
+    if (L < 4) lvl[L] = a;
+    if (j == NV - 1) total = a;
+  }
+  return total;
+}
+
+// Raise this wave's claim with G new group-maximum keys per lane (0 = a group
+// of padding only). lst holds the list (0 = empty slot); stage is wave-private
+// LDS for 64 * kListRegs keys. Returns the claim (0 = none yet).
+template <int DT, int G>
+__device__ __forceinline__ uint32_t claim_update(uint32_t (&lst)[kListRegs],
+                                                 const uint32_t (&gk)[G], int need,
+                                                 int lregs, uint32_t* stage) {
+  uint32_t T = 0;
+  for (int bit = 31; bit >= (DT == 0 ? 16 : 0); --bit) {
+    const uint32_t c = T | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < kListRegs; ++r)
+      if (r < lregs) cnt += __popcll(__ballot(lst[r] >= c));
+#pragma unroll
+    for (int g = 0; g < G; ++g) cnt += __popcll(__ballot(gk[g] >= c));
+    if (cnt >= need) T = c;
+  }
+  // keep the entries at or above T (all nonzero entries while T = 0)
+  const uint32_t lo = T ? T : 1u;
+  const int cap = kWave * lregs;
+  const int lane = threadIdx.x & 63;
+  int n = 0;
+  auto put = [&](uint32_t v) {
+    const bool keep = v >= lo;
+    const uint64_t M = __ballot(keep);
+    const int pos = n + lanes_below(M);
+    if (keep && pos < cap) stage[pos] = v;
+    n += __popcll(M);
+  };
+#pragma unroll
+  for (int r = 0; r < kListRegs; ++r)
+    if (r < lregs) put(lst[r]);
+#pragma unroll
+  for (int g = 0; g < G; ++g) put(gk[g]);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int r = 0; r < kListRegs; ++r) {
+    const int i = r * kWave + lane;
+    lst[r] = (r < lregs && i < n && i < cap) ? stage[i] : 0u;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  return T;
+}
+
+struct RowRun {
+  float m;       // running maximum of the thread's elements
+  float mc;      // integer offset ceil(m * c) of s (-inf while m = -inf)
+  double s;      // sum of 2^(x*c - mc) over the thread's elements so far
+  uint32_t thr;  // running threshold (value key; 0 = none yet)
+  int wn;        // vectors kept by this wave (uniform)
+  uint32_t lst[kListRegs];
+};
+
+template <int DT, int NV, int GS, bool FIRST>
+__device__ __forceinline__ void row_chunk(v4u32 (&raw)[NV], RowSmem& sm, int64_t c0, int64_t nvec,
+                                          int need, int lregs, RowRun& st) {
+  constexpr int EPV = DT == 0 ? 8 : 4;
   constexpr int G = NV / GS;
   constexpr uint32_t NEG_INF_DW = DT == 0 ? 0xFF80FF80u : 0xFF800000u;
+  static_assert(GS == 4, "group = 4 vectors");
   const int tid = threadIdx.x, w = tid >> 6;
-  launder<NV>(raw);
   if (nvec < (int64_t)NV * kS1Threads) {
 #pragma unroll
     for (int j = 0; j < NV; ++j)
       if (j * kS1Threads + tid >= nvec) raw[j] = v4u32{NEG_INF_DW, NEG_INF_DW, NEG_INF_DW, NEG_INF_DW};
   }
-  float gmax[G];
+  float vmax[NV];
+  max_pass<DT, NV>(raw, vmax);
   uint32_t gk[G];
-  group_maxima<DT, NV, GS>(raw, gmax, gk);
-  float cmax = gmax[0];
+  float cm = -INFINITY;
 #pragma unroll
-  for (int g = 1; g < G; ++g) cmax = fmaxf(cmax, gmax[g]);
-  const uint32_t Tw = wave_threshold<DT, G>(gk, (K + 3) >> 2);
-  if ((tid & 63) == 0) sm.red_u[par][w] = Tw;
-  __syncthreads();
-  uint32_t t0 = sm.red_u[par][0];
-#pragma unroll
-  for (int i = 1; i < kS1Waves; ++i) t0 = min(t0, sm.red_u[par][i]);
-  rthr = rthr > t0 ? rthr : t0;
+  for (int g = 0; g < G; ++g) {
+    const float m = fmax3(fmax3(vmax[4 * g], vmax[4 * g + 1], vmax[4 * g + 2]), vmax[4 * g + 3],
+                          vmax[4 * g + 3]);
+    gk[g] = m == -INFINITY ? 0u : order_key(__float_as_uint(m));
+    cm = fmax3(cm, m, m);
+  }
+  if (cm > st.m) {
+    const float mcn = ceilf(cm * kLog2eF);
+    if (mcn != st.mc) {
+      const double d = (double)st.mc - (double)mcn;  // exact: both are integers; -inf at first
+      st.s = d < -1100.0 ? 0.0 : ldexp(st.s, (int)d);
+      st.mc = mcn;
+    }
+    st.m = cm;
+  }
 
-  // The previous terms were taken relative to the rounded offset mc_run, so
-  // they are rescaled by exactly 2^(mc_run - mc).
-  const float m_new = fmaxf(m_run, cmax);
-  const float mc = m_new == m_run ? mc_run : m_new * kLog2eF;
-  launder<NV>(raw);
-  const float acc = exp_collect<DT, NV>(raw, m_new == -INFINITY ? 0.0f : mc, key_threshold(rthr),
-                                        c0, sm.cand + w * kWaveCap, wn);
-  if (m_new != -INFINITY) {
-    const double scale = s_run == 0.0 ? 0.0 : exp2((double)mc_run - (double)mc);
-    s_run = s_run * scale + (double)acc;
-    m_run = m_new;
-    mc_run = mc;
+  // claims
+  const uint32_t Tw = claim_update<DT, G>(st.lst, gk, need, lregs, (uint32_t*)&sm.keys[w][0]);
+  if ((tid & 63) == 0)
+    __hip_atomic_store(&sm.claim[w], Tw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (FIRST) __syncthreads();
+  uint32_t t0 = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < kS1Waves; ++i)
+    t0 = min(t0, __hip_atomic_load(&sm.claim[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+  st.thr = st.thr > t0 ? st.thr : t0;
+  const float tf = key_threshold(st.thr);
+
+  // normaliser terms
+  st.s += (double)exp_pass<DT, NV>(raw, st.m == -INFINITY ? 0.0f : st.mc);
+
+  // keep the vectors that reach the threshold
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const bool keep = vmax[j] >= tf;
+    const uint64_t M = __ballot(keep);
+    if (M) {
+      const int pos = st.wn + lanes_below(M);
+      if (keep && pos < kVecCap) {
+        sm.vec[w][pos] = raw[j];
+        sm.vpos[w][pos] = (uint32_t)c0 + (uint32_t)((j * kS1Threads + tid) * EPV);
+      }
+      st.wn += __popcll(M);
+    }
   }
 }
 
-// Exact top-K of a whole row from memory (survivors overflow: massive ties).
+// Exact top-K of a whole row from memory (kept vectors overflowed: massive
+// ties). Leaves the K keys in keys (flat) and returns K.
 template <int DT>
 __device__ __noinline__ int exact_row_select(const char* rowp, int64_t V, int K, RowSmem& sm) {
+  uint64_t* out = &sm.keys[0][0];
   auto key_at = [&](int64_t idx) -> uint64_t {
     const uint32_t bits = DT == 0 ? ((uint32_t)((const uint16_t*)rowp)[idx] << 16)
                                   : ((const uint32_t*)rowp)[idx];
@@ -582,11 +757,11 @@ __device__ __noinline__ int exact_row_select(const char* rowp, int64_t V, int K,
     for (int64_t i = threadIdx.x; i < V; i += kS1Threads) cnt += key_at(i) >= c ? 1u : 0u;
     cnt = wave_sum(cnt);
     __syncthreads();
-    if ((threadIdx.x & 63) == 0) sm.red_u[0][threadIdx.x >> 6] = cnt;
+    if ((threadIdx.x & 63) == 0) sm.red_u[threadIdx.x >> 6] = cnt;
     __syncthreads();
     uint32_t tot = 0;
 #pragma unroll
-    for (int w = 0; w < kS1Waves; ++w) tot += sm.red_u[0][w];
+    for (int w = 0; w < kS1Waves; ++w) tot += sm.red_u[w];
     if (tot >= (uint32_t)K) T = c;
   }
   __syncthreads();
@@ -594,7 +769,7 @@ __device__ __noinline__ int exact_row_select(const char* rowp, int64_t V, int K,
   __syncthreads();
   for (int64_t i = threadIdx.x; i < V; i += kS1Threads) {
     const uint64_t k = key_at(i);
-    if (k >= T) sm.cand[atomicAdd(&sm.wn[0], 1)] = k;
+    if (k >= T) out[atomicAdd(&sm.wn[0], 1)] = k;
   }
   __syncthreads();
   return sm.wn[0];
@@ -607,51 +782,84 @@ __global__ __launch_bounds__(kS1Threads) void stage1_row_kernel(Stage1Params p) 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int64_t row = blockIdx.x;
   const int K = p.K, S = p.S;
+  const int need = (K + 3) >> 2, lregs = (need + kWave - 1) / kWave;
   const size_t esz = DT == 0 ? 2 : 4;
   const char* rowp = (const char*)p.logits + (size_t)row * (size_t)p.V * esz;
   const int64_t CH = p.chunk;
+  const int64_t rowbytes = p.V * (int64_t)esz, CB = CH * (int64_t)esz;
   auto nvec_of = [&](int c) -> int64_t {  // 0 past the row's end
     const int64_t c0 = (int64_t)c * CH;
     const int64_t c1 = c0 + CH < p.V ? c0 + CH : p.V;
     return c1 > c0 ? (c1 - c0) / EPV : 0;
   };
-  float m_run = -INFINITY, mc_run = -INFINITY;
-  double s_run = 0.0;
-  uint32_t rthr = 0;
-  int wn = 0;
+  RowRun st;
+  st.m = -INFINITY;
+  st.mc = -INFINITY;
+  st.s = 0.0;
+  st.thr = 0;
+  st.wn = 0;
+#pragma unroll
+  for (int r = 0; r < kListRegs; ++r) st.lst[r] = 0;
+
   v4u32 A[NV], Bf[NV];
-  load_chunk_vec<NV>(A, rowp, 0, nvec_of(0), esz);
-  for (int c = 0; c < S; c += 2) {
-    load_chunk_vec<NV>(Bf, rowp, (int64_t)(c + 1) * CH, nvec_of(c + 1), esz);
-    row_process<DT, NV, GS>(A, sm, 0, (int64_t)c * CH, nvec_of(c), K, m_run, mc_run, s_run, rthr,
-                            wn);
-    load_chunk_vec<NV>(A, rowp, (int64_t)(c + 2) * CH, nvec_of(c + 2), esz);
+  load_chunk_buf<NV>(A, rowp, 0, rowbytes);
+  load_chunk_buf<NV>(Bf, rowp, CB, rowbytes);
+  row_chunk<DT, NV, GS, true>(A, sm, 0, nvec_of(0), need, lregs, st);
+  load_chunk_buf<NV>(A, rowp, 2 * CB, rowbytes);
+  for (int c = 1; c < S; c += 2) {
+    row_chunk<DT, NV, GS, false>(Bf, sm, (int64_t)c * CH, nvec_of(c), need, lregs, st);
+    load_chunk_buf<NV>(Bf, rowp, (int64_t)(c + 2) * CB, rowbytes);
     if (c + 1 < S)
-      row_process<DT, NV, GS>(Bf, sm, 1, (int64_t)(c + 1) * CH, nvec_of(c + 1), K, m_run, mc_run,
-                              s_run, rthr, wn);
+      row_chunk<DT, NV, GS, false>(A, sm, (int64_t)(c + 1) * CH, nvec_of(c + 1), need, lregs, st);
+    load_chunk_buf<NV>(A, rowp, (int64_t)(c + 3) * CB, rowbytes);
   }
 
   // row normaliser: per thread s * 2^(mc + m*(log2 e - c)), float64
-  const double off = m_run == -INFINITY ? -INFINITY : (double)mc_run + (double)m_run * kLog2eErr;
+  const double off = st.m == -INFINITY ? -INFINITY : (double)st.mc + (double)st.m * kLog2eErr;
   const double off_w = wave_max(off);
-  __syncthreads();  // every survivor is in; the red_u reads are done
   if (lane == 0) {
     sm.red_d[w] = off_w;
-    sm.wn[w] = wn;
+    sm.wn[w] = st.wn;
   }
-  __syncthreads();
+  __syncthreads();  // claims, kept vectors and counts are final
   double OFF = sm.red_d[0];
 #pragma unroll
   for (int i = 1; i < kS1Waves; ++i) OFF = OFF > sm.red_d[i] ? OFF : sm.red_d[i];
-  const double part_w = wave_sum(m_run == -INFINITY ? 0.0 : s_run * exp2(off - OFF));
-  int wcnt[kS1Waves], ovf = 0;
+  const double part_w = wave_sum(st.m == -INFINITY ? 0.0 : st.s * exp2(off - OFF));
+  uint32_t T = 0xFFFFFFFFu;
+  int ovf = 0;
 #pragma unroll
   for (int i = 0; i < kS1Waves; ++i) {
-    wcnt[i] = sm.wn[i];
-    ovf |= wcnt[i] > kWaveCap;
+    T = min(T, sm.claim[i]);
+    ovf |= sm.wn[i] > kVecCap;
   }
   __syncthreads();
   if (lane == 0) sm.red_d[w] = part_w;
+
+  // filter this wave's kept vectors against the final threshold
+  int kn = 0;
+  if (!ovf) {
+    const float tf = key_threshold(T);
+    const int nvk = st.wn;
+    for (int i0 = 0; i0 < nvk; i0 += kWave) {
+      const int i = i0 + lane;
+      const bool valid = i < nvk;
+      const v4u32 v = sm.vec[w][valid ? i : 0];
+      const uint32_t p0 = sm.vpos[w][valid ? i : 0];
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        const uint32_t bits = elem_bits<DT>(v, e);
+        const bool keep = valid && __uint_as_float(bits) >= tf;
+        const uint64_t M = __ballot(keep);
+        if (M) {
+          const int pos = kn + lanes_below(M);
+          if (keep && pos < kKeyCap) sm.keys[w][pos] = cand_key(order_key(bits), p0 + e);
+          kn += __popcll(M);
+        }
+      }
+    }
+  }
+  if (lane == 0) sm.wn[w] = kn;
   __syncthreads();
   if (tid == 0) {
     double tot = 0.0;
@@ -659,39 +867,50 @@ __global__ __launch_bounds__(kS1Threads) void stage1_row_kernel(Stage1Params p) 
     for (int i = 0; i < kS1Waves; ++i) tot += sm.red_d[i];
     p.out_lse[row] = kLn2 * (OFF + log2(tot));
   }
+  int kcnt[kS1Waves], ntot = 0;
+#pragma unroll
+  for (int i = 0; i < kS1Waves; ++i) {
+    kcnt[i] = sm.wn[i];
+    ovf |= kcnt[i] > kKeyCap;
+    ntot += kcnt[i];
+  }
   if (ovf) {
-    // survivors overflowed a wave region: exact selection from memory
-    const int n = exact_row_select<DT>(rowp, p.V, K, sm);
-    const int np = next_pow2(n < 1 ? 1 : n);
-    for (int i = n + tid; i < np; i += kS1Threads) sm.cand[i] = 0;
+    // exact selection from memory
     __syncthreads();
-    bitonic_desc_u64<kS1Threads>(sm.cand, np);
+    const int n = exact_row_select<DT>(rowp, p.V, K, sm);
+    uint64_t* a = &sm.keys[0][0];
+    const int np = next_pow2(n < 1 ? 1 : n);
+    for (int i = n + tid; i < np; i += kS1Threads) a[i] = 0;
+    __syncthreads();
+    bitonic_desc_u64<kS1Threads>(a, np);
     for (int i = tid; i < K; i += kS1Threads) {
-      const uint64_t k = sm.cand[i];
+      const uint64_t k = a[i];
       p.out_ids[row * K + i] = (int32_t)cand_id(k);
       p.out_vals[row * K + i] = key_value(cand_vkey(k));
     }
     return;
   }
-  // wave 0 finishes the row from the four regions (<= kCandCap survivors)
+  // wave 0 finishes the row from the candidates (>= K of them, all distinct)
   if (w != 0) return;
-  const uint64_t lo = (uint64_t)rthr << 32;
-  constexpr int R = kCandCap / kWave;
+  constexpr int R = kS1Waves * kKeyCap / kWave;
+  const int Ract = __builtin_amdgcn_readfirstlane((ntot + kWave - 1) / kWave);
+  int b1 = kcnt[0], b2 = b1 + kcnt[1], b3 = b2 + kcnt[2];
   uint64_t v[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    {
-      const int i = r * kWave + lane;  // slot i of region i / kWaveCap
-      const int ww = i / kWaveCap, k = i - ww * kWaveCap;
-      const uint64_t key = k < wcnt[ww] ? sm.cand[i] : 0ull;
-      v[r] = key >= lo ? key : 0ull;
+    v[r] = 0;
+    if (r < Ract) {
+      const int i = r * kWave + lane;
+      const int ww = (i >= b1) + (i >= b2) + (i >= b3);
+      const int k = i - (ww == 0 ? 0 : ww == 1 ? b1 : ww == 2 ? b2 : b3);
+      v[r] = i < ntot ? sm.keys[ww][k] : 0ull;
     }
   }
-  // the survivors are in registers now: sm.cand serves as the staging area
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  wave_topk_finish(v, R, K, p.idbits, DT == 0, sm.cand, p.out_ids + row * K, p.out_vals + row * K);
+  wave_topk_finish(v, Ract, K, p.idbits, DT == 0, (uint64_t*)&sm.vec[0][0], p.out_ids + row * K,
+                   p.out_vals + row * K);
 }
 
 }  // namespace ddt
