@@ -30,6 +30,12 @@ __device__ __forceinline__ uint64_t cand_key(uint32_t vkey, uint32_t id) {
 __device__ __forceinline__ uint32_t cand_id(uint64_t k) { return 0xFFFFFFFFu - (uint32_t)k; }
 __device__ __forceinline__ uint32_t cand_vkey(uint64_t k) { return (uint32_t)(k >> 32); }
 
+// Number of set bits of m at lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
 #pragma unroll

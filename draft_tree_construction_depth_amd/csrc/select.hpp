@@ -13,11 +13,15 @@
 // (Proposition 2) and every node's parent is emitted before it.
 //
 // MI355X design: no serial heap on the common path. One 1024-thread
-// workgroup per request:
+// workgroup per request (four waves per SIMD: a lone wave issues only about
+// a quarter of the SIMD's vector rate, and every step here is short):
 //  1. Threshold. tau = the B-th best score among the L*K prefixes that
-//     deviate from the all-rank-0 spine only in their last position (found
-//     to ~1e-6 by a block-parallel bisection). These are B valid prefixes,
-//     so every one of the true top B scores at least tau.
+//     deviate from the all-rank-0 spine only in their last position: exact,
+//     by a merge tree over the rows (each row's scores are sorted); for
+//     shapes whose first merge level would not fit, to 8^-8 of their range
+//     by an 8-ary search whose counts are ballots.
+//     These are B valid prefixes, so every one of the true top B scores at
+//     least tau.
 //  2. Enumerate E = {prefixes with score >= tau} by "chains": a chain is an
 //     anchor prefix whose last rank is >= 1 followed by its rank-0
 //     extensions, which one thread walks in registers. Generation g holds
@@ -26,8 +30,11 @@
 //     scan and walked in parallel. Drafter trees have <= 3 deviations per
 //     path in practice, so this needs a few block-synchronous steps instead
 //     of one per tree level.
-//  3. Bitonic-sort E (LDS) by (score, 128-bit lexicographic rank key) and
-//     emit the first B, mapping parents to output node numbers.
+//  3. Histogram E's scores into bins over [tau, best]; the first bins that
+//     hold >= B entries form E2, which contains the output. Place each entry
+//     of E2 in the order (score, then 128-bit lexicographic rank key) by
+//     counting the entries before it. Emit the first B, mapping parents to
+//     output node numbers (a parent is in the output and precedes it).
 //  4. Write the bit-packed ancestor mask rows from the parents in LDS.
 // If E would exceed kECap entries (flat rows with V < B, massive ties), the
 // block instead runs the pages' best-first heap in one thread, in LDS:
@@ -45,8 +52,9 @@ constexpr int kMaxLK = 8192;
 constexpr int kMaxL = 32;
 constexpr int kMaxB = 512;
 constexpr int kMaxW = (kMaxB + 1 + 63) / 64;
-constexpr int kCPT = kMaxLK / kSelThreads;  // one-deviation prefixes per thread
 constexpr int kHeapCap = 2 * kMaxB + 2;
+// capacity of one merge-tree level: ceil(L / 2) * min(2K, B) entries
+constexpr int kMergeCap = 4096;
 
 struct SelectParams {
   const float* vals;   // [batch][L][K] sorted logits
@@ -72,8 +80,8 @@ struct SelEnum {
   int16_t ePar[kECap];
   uint16_t eRank[kECap];
   uint8_t eDep[kECap];
-  uint16_t idx[kECap];
-  int cnt[kECap + 1];
+  int cnt[kECap + 1];  // enumeration: child counts; then: output rank of each entry
+  uint16_t ord[kECap];  // entries at or above the second threshold
 };
 
 struct SelHeap {
@@ -91,16 +99,25 @@ struct SelHeap {
 
 struct SelectSmem {
   float v[kMaxLK];
+  double lse[kMaxL];
   double Z[kMaxL];
   double P0[kMaxL + 1];
   double sig[kMaxL + 1];
   union {
     SelEnum en;
     SelHeap hp;
+    struct {  // merge tree of the threshold (before the enumeration)
+      double a[kMergeCap];
+      double b[kMergeCap];
+    } mt;
   } u;
   int opar[kMaxB];  // parent node number of output node j+1
   int wsum[kSelWaves];
   int redI[2][kSelWaves];
+  int cnt8[2][8][kSelWaves];  // [parity][pivot][wave]
+  int n2;
+  int kcut;
+  int hist[kSelThreads];
   double redD[kSelWaves];
   double tau;
   int nE;
@@ -111,23 +128,26 @@ struct SelectSmem {
 __device__ __forceinline__ void lex_set_digit(uint64_t& hi, uint64_t& lo, int d, uint32_t r,
                                               int bpd) {
   const int s = 128 - d * bpd;  // bit position of the digit's LSB (>= 6)
-  if (s >= 64) {
-    hi |= (uint64_t)r << (s - 64);
-  } else if (s + bpd <= 64) {
-    lo |= (uint64_t)r << s;
-  } else {
-    hi |= (uint64_t)r >> (64 - s);
-    lo |= (uint64_t)r << s;
-  }
+  const uint64_t v = r;
+  // the digit lies in the high word, the low word, or straddles them
+  const uint64_t h = s >= 64 ? v << (s - 64) : (s + bpd > 64 ? v >> (64 - s) : 0ull);
+  const uint64_t l = s >= 64 ? 0ull : v << s;
+  hi |= h;
+  lo |= l;
 }
 
+// Block sum of per-wave (uniform) counts; alternating buffers need one barrier.
 __device__ __forceinline__ int sel_block_sum(int v, SelectSmem& sm, int& parity) {
-  v = wave_sum(v);
+  static_assert(kSelWaves % 4 == 0, "16-byte reads");
   if ((threadIdx.x & 63) == 0) sm.redI[parity][threadIdx.x >> 6] = v;
   __syncthreads();
+  const int4* r = (const int4*)sm.redI[parity];
   int t = 0;
 #pragma unroll
-  for (int i = 0; i < kSelWaves; ++i) t += sm.redI[parity][i];
+  for (int i = 0; i < kSelWaves / 4; ++i) {
+    const int4 q = r[i];
+    t += q.x + q.y + q.z + q.w;
+  }
   parity ^= 1;
   return t;
 }
@@ -136,22 +156,32 @@ __device__ __forceinline__ double sel_block_min(double v, SelectSmem& sm) {
   v = wave_min(v);
   if ((threadIdx.x & 63) == 0) sm.redD[threadIdx.x >> 6] = v;
   __syncthreads();
-  double r = sm.redD[0];
+  const double2* r = (const double2*)sm.redD;
+  double m = INFINITY;
 #pragma unroll
-  for (int i = 1; i < kSelWaves; ++i) r = r < sm.redD[i] ? r : sm.redD[i];
+  for (int i = 0; i < kSelWaves / 2; ++i) {
+    const double2 q = r[i];
+    m = q.x < m ? q.x : m;
+    m = q.y < m ? q.y : m;
+  }
   __syncthreads();
-  return r;
+  return m;
 }
 
 __device__ __forceinline__ double sel_block_max(double v, SelectSmem& sm) {
   v = wave_max(v);
   if ((threadIdx.x & 63) == 0) sm.redD[threadIdx.x >> 6] = v;
   __syncthreads();
-  double r = sm.redD[0];
+  const double2* r = (const double2*)sm.redD;
+  double m = -INFINITY;
 #pragma unroll
-  for (int i = 1; i < kSelWaves; ++i) r = r > sm.redD[i] ? r : sm.redD[i];
+  for (int i = 0; i < kSelWaves / 2; ++i) {
+    const double2 q = r[i];
+    m = q.x > m ? q.x : m;
+    m = q.y > m ? q.y : m;
+  }
   __syncthreads();
-  return r;
+  return m;
 }
 
 // e1 strictly before e2 in the output order (PAD = 0xFFFF is last).
@@ -254,6 +284,190 @@ __device__ void heap_fallback(const SelectParams& p, SelectSmem& sm, int64_t b) 
 }
 
 // ---------------------------------------------------------------------------
+// Largest lo (to 8^-8 of the value range, from below) with >= B of the
+// block's scores (NS per thread, -inf = none) at or above it: an 8-ary
+// search, seven pivots and one barrier per step; lane q sums pivot q's
+// per-wave counts.
+template <int NS>
+__device__ __forceinline__ double sel_kth(const double (&sc)[NS], double lo_l, double hi_l, int B,
+                          SelectSmem& sm, int& parity) {
+  auto count_ge = [&](double t) -> int {
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) c += __popcll(__ballot(sc[i] >= t));
+    return c;
+  };
+  double lo = sel_block_min(lo_l, sm), hi = sel_block_max(hi_l, sm);
+  if (sel_block_sum(count_ge(hi), sm, parity) >= B) return hi;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int it = 0; it < 8; ++it) {
+    const double step = (hi - lo) * 0.125;
+    if (!(step > 0.0)) break;
+    int cq = 0;
+#pragma unroll
+    for (int q = 1; q < 8; ++q) {
+      const int c = count_ge(lo + step * q);
+      if (lane == q) cq = c;
+    }
+    if (lane >= 1 && lane < 8) sm.cnt8[parity][lane][w] = cq;
+    __syncthreads();
+    int tot = 0;
+    if (lane >= 1 && lane < 8) {
+      const int4* r = (const int4*)sm.cnt8[parity][lane];
+#pragma unroll
+      for (int i = 0; i < kSelWaves / 4; ++i) {
+        const int4 q = r[i];
+        tot += q.x + q.y + q.z + q.w;
+      }
+    }
+    parity ^= 1;
+    // counts fall with the pivot: the last pivot with >= B becomes lo
+    const uint64_t ok = __ballot(lane >= 1 && lane < 8 && tot >= B);
+    const int best = ok ? 63 - __builtin_clzll(ok) : 0;
+    const double nlo = lo + step * best;
+    const double nhi = best == 7 ? hi : lo + step * (best + 1);
+    lo = nlo;
+    hi = nhi;
+  }
+  return lo;
+}
+
+// Exact B-th best one-deviation score by a merge tree. Row d's scores
+// s_d(r) = min(sig_d, P0_d + v_d[r] - Z_d) do not increase with r, so the
+// rows are sorted lists; each level merges pairs of lists (merge-path search
+// per output position) and keeps the best B of each merge. ceil(log2 L)
+// levels, one barrier each. Requires L * K >= B and a first level of at
+// most kMergeCap entries.
+__device__ double sel_tau_merge(SelectSmem& sm, int L, int K, int B) {
+  auto onedev = [&](int d, int r) -> double {
+    const double raw = (sm.P0[d] + (double)sm.v[d * K + r]) - sm.Z[d];
+    return raw > sm.sig[d] ? sm.sig[d] : raw;
+  };
+  if (L == 1) return onedev(0, B - 1);
+  double* src = sm.u.mt.a;
+  double* dst = sm.u.mt.b;
+  int m = L, len = K;  // m lists, each of length len except possibly the last
+  int last = K;        // length of the last list
+  bool rows = true;
+  while (m > 1) {
+    const int mo = (m + 1) >> 1;
+    const int lo_len = len + len < B ? len + len : B;                // merged pair
+    const int last_pair = (m & 1) ? last : (len + last < B ? len + last : B);
+    const int total = (mo - 1) * lo_len + last_pair;
+    for (int o = threadIdx.x; o < total; o += kSelThreads) {
+      const int i = o / lo_len, k = o - i * lo_len;
+      const int ia = 2 * i, ib = 2 * i + 1;
+      const int nA = ia == m - 1 ? last : len;
+      const int nB = ib < m ? (ib == m - 1 ? last : len) : 0;
+      auto A = [&](int x) -> double { return rows ? onedev(ia, x) : src[ia * len + x]; };
+      auto Bv = [&](int x) -> double { return rows ? onedev(ib, x) : src[ib * len + x]; };
+      // a = elements of A among the best k+1
+      int lo = k + 1 - nB > 0 ? k + 1 - nB : 0, hi = k + 1 < nA ? k + 1 : nA;
+      while (lo < hi) {
+        const int a = (lo + hi + 1) >> 1, b = k + 1 - a;
+        if (b < nB && A(a - 1) < Bv(b)) hi = a - 1;  // too many from A
+        else lo = a;
+      }
+      // lo is the largest a whose last A element still beats B's next one
+      const int a = lo, b = k + 1 - a;
+      double out;
+      if (a == 0) out = Bv(b - 1);
+      else if (b == 0) out = A(a - 1);
+      else {
+        const double x = A(a - 1), y = Bv(b - 1);
+        out = x < y ? x : y;
+      }
+      dst[i * lo_len + k] = out;
+    }
+    __syncthreads();
+    double* t = src;
+    src = dst;
+    dst = t;
+    m = mo;
+    len = lo_len;
+    last = last_pair;
+    rows = false;
+  }
+  return src[B - 1];
+}
+
+// B-th best score among the one-deviation prefixes (NS per thread).
+template <int NS>
+__device__ __forceinline__ double sel_threshold(SelectSmem& sm, int L, int K, int B, int& parity) {
+  const int tid = threadIdx.x, LK = L * K;
+  double sc1[NS];
+  double lo_l = INFINITY, hi_l = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int c = tid + i * kSelThreads;
+    sc1[i] = -INFINITY;
+    if (c < LK) {
+      const int d = c / K + 1;
+      const double raw = (sm.P0[d - 1] + (double)sm.v[c]) - sm.Z[d - 1];
+      const double sc = raw > sm.sig[d - 1] ? sm.sig[d - 1] : raw;
+      sc1[i] = sc;
+      lo_l = sc < lo_l ? sc : lo_l;
+      hi_l = sc > hi_l ? sc : hi_l;
+    }
+  }
+  return sel_kth<NS>(sc1, lo_l, hi_l, B, sm, parity);
+}
+
+// Position in the output order (score desc, then lexicographic rank key asc;
+// keys are unique) of every entry listed in ord[0..n2), left in cnt: the
+// number of listed entries before it. The listed scores sit compactly in
+// s2. Each entry's count is split over P lanes (P a power of two, P * n2 <=
+// the block size when it fits) and summed by shuffles; equal scores (rare:
+// log-probabilities only tie exactly) take the lexicographic keys.
+__device__ void sel_rank(SelEnum& en, const double* s2, int n2) {
+  int P = 1;
+  while (P < kWave && 2 * P * n2 <= kSelThreads) P *= 2;
+  const int groups = kSelThreads / P;
+  const int tid = threadIdx.x, g = tid / P, part = tid - g * P;
+  const int per = (n2 + P - 1) / P;
+  for (int k0 = 0; k0 < n2; k0 += groups) {  // uniform trip count
+    const int k = k0 + g;
+    int rank = 0;
+    int i = 0;
+    if (k < n2) {
+      const double si = s2[k];
+      i = en.ord[k];
+      const uint64_t hi_i = en.eLh[i], lo_i = en.eLl[i];
+      const int j0 = part * per, j1 = j0 + per < n2 ? j0 + per : n2;
+      auto before = [&](int j, double sj) -> int {
+        const int e = en.ord[j];
+        const uint64_t hj = en.eLh[e], lj = en.eLl[e];
+        return (sj == si && j != k && (hj < hi_i || (hj == hi_i && lj < lo_i))) ? 1 : 0;
+      };
+      constexpr int U = 8;
+      int j = j0;
+      for (; j + U <= j1; j += U) {
+        double sj[U];
+        bool tie = false;
+#pragma unroll
+        for (int u = 0; u < U; ++u) sj[u] = s2[j + u];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          rank += sj[u] > si ? 1 : 0;
+          tie |= sj[u] == si && j + u != k;
+        }
+        if (tie) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) rank += before(j + u, sj[u]);
+        }
+      }
+      for (; j < j1; ++j) {
+        const double sj = s2[j];
+        rank += (sj > si ? 1 : 0) + before(j, sj);
+      }
+    }
+    for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o);
+    if (k < n2 && part == 0) en.cnt[i] = rank;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   __shared__ SelectSmem sm;
   SelEnum& en = sm.u.en;
@@ -264,15 +478,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   int parity = 0;
 
   for (int i = tid; i < LK; i += kSelThreads) sm.v[i] = vals[i];
+  if (tid < L) sm.lse[tid] = p.lse[(size_t)b * L + tid];
+  __syncthreads();
   if (tid == 0) {
     // Z_d and the spine (all ranks 0): float64, left to right.
     double acc = 0.0, S = 0.0, sc = 0.0;
     sm.P0[0] = 0.0;
     sm.sig[0] = 0.0;
     for (int d = 1; d <= L; ++d) {
-      acc += p.lse[(size_t)b * L + d - 1];
+      acc += sm.lse[d - 1];
       sm.Z[d - 1] = acc;
-      S += (double)vals[(size_t)(d - 1) * K];
+      S += (double)sm.v[(d - 1) * K];
       const double raw = S - acc;
       sc = raw > sc ? sc : raw;
       sm.P0[d] = S;
@@ -284,41 +500,19 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   __syncthreads();
 
   // ---- 1. threshold from the one-deviation prefixes -------------------------
-  double sc1[kCPT];
-  double lo_l = INFINITY, hi_l = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kCPT; ++i) {
-    const int c = tid + i * kSelThreads;
-    sc1[i] = -INFINITY;
-    if (c < LK) {
-      const int d = c / K + 1;
-      const double raw = (sm.P0[d - 1] + (double)sm.v[c]) - sm.Z[d - 1];
-      const double s = raw > sm.sig[d - 1] ? sm.sig[d - 1] : raw;
-      sc1[i] = s;
-      lo_l = s < lo_l ? s : lo_l;
-      hi_l = s > hi_l ? s : hi_l;
-    }
-  }
   double tau = -INFINITY;
   if (LK >= B) {
-    double lo = sel_block_min(lo_l, sm), hi = sel_block_max(hi_l, sm);
-    int c_hi = 0;
-#pragma unroll
-    for (int i = 0; i < kCPT; ++i) c_hi += sc1[i] >= hi ? 1 : 0;
-    if (sel_block_sum(c_hi, sm, parity) >= B) {
-      lo = hi;
+    const int lvl1 = ((L + 1) >> 1) * (2 * K < B ? 2 * K : B);
+    if (lvl1 <= kMergeCap) {
+      tau = sel_tau_merge(sm, L, K, B);
     } else {
-      for (int it = 0; it < 24; ++it) {
-        const double mid = lo + 0.5 * (hi - lo);
-        if (!(mid > lo && mid < hi)) break;
-        int c = 0;
-#pragma unroll
-        for (int i = 0; i < kCPT; ++i) c += sc1[i] >= mid ? 1 : 0;
-        if (sel_block_sum(c, sm, parity) >= B) lo = mid;
-        else hi = mid;
-      }
+      const int nslot = (LK + kSelThreads - 1) / kSelThreads;
+      static_assert(kMaxLK <= 8 * kSelThreads, "eight one-deviation prefixes per thread at most");
+      if (nslot <= 1) tau = sel_threshold<1>(sm, L, K, B, parity);
+      else if (nslot <= 2) tau = sel_threshold<2>(sm, L, K, B, parity);
+      else if (nslot <= 4) tau = sel_threshold<4>(sm, L, K, B, parity);
+      else tau = sel_threshold<8>(sm, L, K, B, parity);
     }
-    tau = lo;
   }
 
   // ---- 2. enumerate E = {score >= tau} by chains ----------------------------
@@ -447,48 +641,84 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     if (tid == 0) heap_fallback(p, sm, b);
     __syncthreads();
   } else {
-    // ---- 3. sort E and emit the first B -----------------------------------
+    // ---- 3. order E, emit the first B ----------------------------------------
+    // Second cut: E's scores fall into kSelThreads bins over [tau, best]
+    // (bin index monotone in the score, so equal scores share a bin); E2 =
+    // the entries of the first bins that hold >= B of them. E2 is closed
+    // upwards in the order, so it holds the output, and it is ranked alone.
     const int nE = sm.nE;
-    const int N = next_pow2(nE < 1 ? 1 : nE);
-    for (int i = tid; i < N; i += kSelThreads) en.idx[i] = (uint16_t)(i < nE ? i : 0xFFFF);
+    static_assert(kECap <= 2 * kSelThreads, "two entries per thread at most");
+    const double top = sm.sig[1];  // the best prefix: depth 1, rank 0
+    const double span = top - tau;
+    const bool cut = nE > B && span > 0.0;
+    const double scale = cut ? (double)kSelThreads / span : 0.0;
+    auto bin_of = [&](double sc) -> int {
+      const double t = (top - sc) * scale;
+      return t >= (double)(kSelThreads - 1) ? kSelThreads - 1 : (t > 0.0 ? (int)t : 0);
+    };
+    int kcut = kSelThreads - 1;
+    if (cut) {
+      sm.hist[tid] = 0;
+      __syncthreads();
+      for (int i = tid; i < nE; i += kSelThreads) atomicAdd(&sm.hist[bin_of(en.eSc[i])], 1);
+      __syncthreads();
+      // inclusive scan of the bins; the first bin reaching B is the cut
+      int x = sm.hist[tid];
+      const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      if (lane == kWave - 1) sm.wsum[w] = x;
+      __syncthreads();
+      int pre = 0;
+      for (int q = 0; q < w; ++q) pre += sm.wsum[q];
+      const int inc = pre + x, exc = inc - sm.hist[tid];
+      if (inc >= B && exc < B) sm.kcut = tid;
+      __syncthreads();
+      kcut = sm.kcut;
+    }
+    if (tid == 0) sm.n2 = 0;
     __syncthreads();
-    for (int k = 2; k <= N; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < (N >> 1); i += kSelThreads) {
-          const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-          const int hi = lo + j;
-          const int x = en.idx[lo], y = en.idx[hi];
-          const bool best_first = (lo & k) == 0;
-          if (best_first ? sel_before(en, y, x) : sel_before(en, x, y)) {
-            en.idx[lo] = (uint16_t)y;
-            en.idx[hi] = (uint16_t)x;
-          }
-        }
-        __syncthreads();
+    double* s2 = en.eS;  // dead after the enumeration
+    for (int i0 = 0; i0 < nE; i0 += kSelThreads) {
+      const int i = i0 + tid;
+      const bool keep = i < nE && (!cut || bin_of(en.eSc[i]) <= kcut);
+      const uint64_t M = __ballot(keep);
+      int base = 0;
+      if ((tid & 63) == 0 && M) base = atomicAdd(&sm.n2, __popcll(M));
+      base = __shfl(base, 0);
+      if (keep) {
+        const int k = base + lanes_below(M);
+        en.ord[k] = (uint16_t)i;
+        s2[k] = en.eSc[i];
       }
     }
+    __syncthreads();
+    const int n2 = sm.n2;
+    sel_rank(en, s2, n2);
     const int nsel = nE < B ? nE : B;
-    for (int i = tid; i < nE; i += kSelThreads) en.cnt[i] = -1;
-    __syncthreads();
-    for (int j = tid; j < nsel; j += kSelThreads) en.cnt[en.idx[j]] = j;
-    __syncthreads();
-    for (int j = tid; j < B; j += kSelThreads) {
-      const size_t o = (size_t)b * B + j;
+    for (int k = tid; k < n2; k += kSelThreads) {
+      const int i = en.ord[k];
+      const int j = en.cnt[i];
       if (j < nsel) {
-        const int e = en.idx[j];
-        const int d = en.eDep[e], r = en.eRank[e], pe = en.ePar[e];
+        const size_t o = (size_t)b * B + j;
+        const int d = en.eDep[i], r = en.eRank[i], pe = en.ePar[i];
         const int par = pe < 0 ? 0 : en.cnt[pe] + 1;
         p.tree_tokens[o] = p.ids[(size_t)b * LK + (size_t)(d - 1) * K + r];
         p.parents[o] = par;
-        p.logq[o] = (float)en.eSc[e];
+        p.logq[o] = (float)en.eSc[i];
         if (p.depths) p.depths[o] = d;
         sm.opar[j] = par;
-      } else {
-        p.tree_tokens[o] = -1;
-        p.parents[o] = -1;
-        p.logq[o] = -INFINITY;
-        if (p.depths) p.depths[o] = 0;
       }
+    }
+    for (int j = nsel + tid; j < B; j += kSelThreads) {
+      const size_t o = (size_t)b * B + j;
+      p.tree_tokens[o] = -1;
+      p.parents[o] = -1;
+      p.logq[o] = -INFINITY;
+      if (p.depths) p.depths[o] = 0;
     }
     if (tid == 0) {
       p.num_nodes[b] = nsel;

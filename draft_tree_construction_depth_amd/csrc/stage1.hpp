@@ -38,6 +38,7 @@
 namespace ddt {
 
 typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
+typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
 typedef const __attribute__((address_space(1))) v4u32* gvec_ptr;
 typedef const __attribute__((address_space(1))) uint16_t* gu16_ptr;
 typedef const __attribute__((address_space(1))) uint32_t* gu32_ptr;
@@ -87,12 +88,6 @@ template <int NV>
 __device__ __forceinline__ void launder(v4u32 (&raw)[NV]) {
 #pragma unroll
   for (int j = 0; j < NV; ++j) asm volatile("" : "+v"(raw[j]));
-}
-
-// Number of set bits of m at lanes below this one.
-__device__ __forceinline__ int lanes_below(uint64_t m) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // Float threshold equivalent to "order key >= t": t = 0 admits every finite
@@ -522,14 +517,18 @@ __global__ __launch_bounds__(kWave* kMergeWaves) void stage1_merge_kernel(Stage1
 // slab of the row (its bytes left, clamped): vectors past the row's end read
 // as zero without touching memory and are then set to -inf.
 
-constexpr int kVecCap = 256;  // kept vectors per wave
-constexpr int kKeyCap = 512;  // candidate keys per wave after the final filter
-constexpr int kListRegs = 2;  // list of 64 * kListRegs group maxima per wave (>= ceil(K/4))
+constexpr int kVecCap = 448;          // kept vectors per wave
+constexpr int kKeyCap = 2 * kVecCap;  // candidate keys per wave (in the wave's vector region)
+constexpr int kListRegs = 2;          // list of 64 * kListRegs group maxima per wave (>= ceil(K/4))
 
+// 37.1 KiB: four workgroups fit in one CU's 160 KiB.
 struct RowSmem {
-  v4u32 vec[kS1Waves][kVecCap];       // kept vectors (later: the finish's staging area)
-  uint32_t vpos[kS1Waves][kVecCap];   // index of each kept vector's first element
-  uint64_t keys[kS1Waves][kKeyCap];   // final candidates (main loop: list compaction)
+  union {
+    v4u32 vec[kS1Waves][kVecCap];      // kept vectors
+    uint64_t keys[kS1Waves][kKeyCap];  // after the loop: final candidates
+  };
+  uint32_t vpos[kS1Waves][kVecCap];  // index of each kept vector's first element
+  uint32_t lst[kS1Waves][kWave * kListRegs];  // list compaction
   uint32_t claim[kS1Waves];
   uint32_t red_u[kS1Waves];
   double red_d[kS1Waves];
@@ -554,7 +553,9 @@ __device__ __forceinline__ float vec_max(const float (&x)[DT == 0 ? 8 : 4]) {
 }
 
 // Chunk loads: slab j of the chunk (256 threads x 16 B) through its own
-// buffer resource; the thread's offset is the same for every slab.
+// buffer resource; the thread's offset is the same for every slab. The
+// logits are read once, so the loads carry the nontemporal hint.
+constexpr int kLoadNT = 2;  // cache-policy bit "nt" of buffer loads
 template <int NV>
 __device__ __forceinline__ void load_chunk_buf(v4u32 (&buf)[NV], const char* rowp,
                                                int64_t cbyte, int64_t rowbytes) {
@@ -567,7 +568,7 @@ __device__ __forceinline__ void load_chunk_buf(v4u32 (&buf)[NV], const char* row
     __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(rowp + (left > 0 ? off : 0)), (short)0, nrec,
                                           0x00020000);
-    buf[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
+    buf[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, kLoadNT);
   }
 }
 
@@ -710,7 +711,7 @@ __device__ __forceinline__ void row_chunk(v4u32 (&raw)[NV], RowSmem& sm, int64_t
   }
 
   // claims
-  const uint32_t Tw = claim_update<DT, G>(st.lst, gk, need, lregs, (uint32_t*)&sm.keys[w][0]);
+  const uint32_t Tw = claim_update<DT, G>(st.lst, gk, need, lregs, &sm.lst[w][0]);
   if ((tid & 63) == 0)
     __hip_atomic_store(&sm.claim[w], Tw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   if (FIRST) __syncthreads();
@@ -776,7 +777,7 @@ __device__ __noinline__ int exact_row_select(const char* rowp, int64_t V, int K,
 }
 
 template <int DT, int NV, int GS>
-__global__ __launch_bounds__(kS1Threads) void stage1_row_kernel(Stage1Params p) {
+__global__ __launch_bounds__(kS1Threads, 4) void stage1_row_kernel(Stage1Params p) {
   constexpr int EPV = DT == 0 ? 8 : 4;
   __shared__ RowSmem sm;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -836,25 +837,38 @@ __global__ __launch_bounds__(kS1Threads) void stage1_row_kernel(Stage1Params p) 
   __syncthreads();
   if (lane == 0) sm.red_d[w] = part_w;
 
-  // filter this wave's kept vectors against the final threshold
+  // filter this wave's kept vectors against the final threshold; the keys
+  // go to the same region once the vectors are in registers
+  constexpr int VR = (kVecCap + kWave - 1) / kWave;
   int kn = 0;
   if (!ovf) {
     const float tf = key_threshold(T);
     const int nvk = st.wn;
-    for (int i0 = 0; i0 < nvk; i0 += kWave) {
-      const int i = i0 + lane;
-      const bool valid = i < nvk;
-      const v4u32 v = sm.vec[w][valid ? i : 0];
-      const uint32_t p0 = sm.vpos[w][valid ? i : 0];
+    v4u32 kv[VR];
+    uint32_t kp[VR];
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const uint32_t bits = elem_bits<DT>(v, e);
-        const bool keep = valid && __uint_as_float(bits) >= tf;
-        const uint64_t M = __ballot(keep);
-        if (M) {
-          const int pos = kn + lanes_below(M);
-          if (keep && pos < kKeyCap) sm.keys[w][pos] = cand_key(order_key(bits), p0 + e);
-          kn += __popcll(M);
+    for (int r = 0; r < VR; ++r) {
+      const int i = r * kWave + lane;
+      const bool valid = i < nvk;
+      kv[r] = valid ? sm.vec[w][i] : v4u32{0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};
+      kp[r] = valid ? sm.vpos[w][i] : 0u;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int r = 0; r < VR; ++r) {
+      if (r * kWave < nvk) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const uint32_t bits = elem_bits<DT>(kv[r], e);
+          const bool keep = (r * kWave + lane) < nvk && __uint_as_float(bits) >= tf;
+          const uint64_t M = __ballot(keep);
+          if (M) {
+            const int pos = kn + lanes_below(M);
+            if (keep && pos < kKeyCap) sm.keys[w][pos] = cand_key(order_key(bits), kp[r] + e);
+            kn += __popcll(M);
+          }
         }
       }
     }
@@ -874,6 +888,8 @@ __global__ __launch_bounds__(kS1Threads) void stage1_row_kernel(Stage1Params p) 
     ovf |= kcnt[i] > kKeyCap;
     ntot += kcnt[i];
   }
+  int32_t* oid = p.out_ids + row * K;
+  float* oval = p.out_vals + row * K;
   if (ovf) {
     // exact selection from memory
     __syncthreads();
@@ -885,32 +901,39 @@ __global__ __launch_bounds__(kS1Threads) void stage1_row_kernel(Stage1Params p) 
     bitonic_desc_u64<kS1Threads>(a, np);
     for (int i = tid; i < K; i += kS1Threads) {
       const uint64_t k = a[i];
-      p.out_ids[row * K + i] = (int32_t)cand_id(k);
-      p.out_vals[row * K + i] = key_value(cand_vkey(k));
+      oid[i] = (int32_t)cand_id(k);
+      oval[i] = key_value(cand_vkey(k));
     }
     return;
   }
-  // wave 0 finishes the row from the candidates (>= K of them, all distinct)
-  if (w != 0) return;
-  constexpr int R = kS1Waves * kKeyCap / kWave;
-  const int Ract = __builtin_amdgcn_readfirstlane((ntot + kWave - 1) / kWave);
-  int b1 = kcnt[0], b2 = b1 + kcnt[1], b3 = b2 + kcnt[2];
-  uint64_t v[R];
+  // >= K distinct candidates: each one's rank is the number of larger ones
+  const int b1 = kcnt[0], b2 = b1 + kcnt[1], b3 = b2 + kcnt[2];
+  for (int i = tid; i < ntot; i += kS1Threads) {
+    const int ww = (i >= b1) + (i >= b2) + (i >= b3);
+    const uint64_t mine = sm.keys[ww][i - (ww == 0 ? 0 : ww == 1 ? b1 : ww == 2 ? b2 : b3)];
+    int rank = 0;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    v[r] = 0;
-    if (r < Ract) {
-      const int i = r * kWave + lane;
-      const int ww = (i >= b1) + (i >= b2) + (i >= b3);
-      const int k = i - (ww == 0 ? 0 : ww == 1 ? b1 : ww == 2 ? b2 : b3);
-      v[r] = i < ntot ? sm.keys[ww][k] : 0ull;
+    for (int q = 0; q < kS1Waves; ++q) {
+      // 16-byte LDS reads, eight keys per batch (the region starts 16-byte aligned)
+      const u64x2* kq = (const u64x2*)&sm.keys[q][0];
+      const int n = kcnt[q], np = n >> 1;
+      int j = 0;
+      for (; j + 4 <= np; j += 4) {
+        const u64x2 a0 = kq[j], a1 = kq[j + 1], a2 = kq[j + 2], a3 = kq[j + 3];
+        rank += (a0.x > mine) + (a0.y > mine) + (a1.x > mine) + (a1.y > mine) +
+                (a2.x > mine) + (a2.y > mine) + (a3.x > mine) + (a3.y > mine);
+      }
+      for (; j < np; ++j) {
+        const u64x2 a0 = kq[j];
+        rank += (a0.x > mine) + (a0.y > mine);
+      }
+      if (n & 1) rank += sm.keys[q][n - 1] > mine ? 1 : 0;
+    }
+    if (rank < K) {
+      oid[rank] = (int32_t)cand_id(mine);
+      oval[rank] = key_value(cand_vkey(mine));
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  wave_topk_finish(v, Ract, K, p.idbits, DT == 0, (uint64_t*)&sm.vec[0][0], p.out_ids + row * K,
-                   p.out_vals + row * K);
 }
 
 }  // namespace ddt

@@ -6,9 +6,10 @@
 //
 // Walk: DDTree explainer, section 5 (verifier walk), TreeSpark README item 4
 // (argmax-following acceptance walk). One wavefront per request holds the
-// request's parent/token arrays in registers (B <= 512, so <= 8 nodes per
-// lane); each step is one compare per held node and a wave-wide min, and the
-// walk takes at most L steps.
+// request's parent, token and target-token arrays in registers (B <= 512, so
+// <= 8 nodes per lane); each step is one compare and one ballot per held
+// slot plus one cross-lane read of the next target, and the walk takes at
+// most L steps.
 #pragma once
 
 #include "common.hpp"
@@ -77,37 +78,48 @@ __global__ __launch_bounds__(kWave) void walk_kernel(WalkParams p) {
   const int B = p.B, L = p.L;
   int n = p.num_nodes[b];
   n = n < 0 ? 0 : (n > B ? B : n);
-  int par[kWalkMaxPerLane], tok[kWalkMaxPerLane];
+  const int32_t* tgt = p.target_tokens + (size_t)b * (B + 1);
+  // node j+1 lives in lane j % 64, slot j / 64, with its parent, token and
+  // target token; every load is issued before the walk starts
+  int par[kWalkMaxPerLane], tok[kWalkMaxPerLane], tg[kWalkMaxPerLane];
 #pragma unroll
   for (int t = 0; t < kWalkMaxPerLane; ++t) {
     const int j = lane + t * kWave;
-    par[t] = -2;
-    tok[t] = 0;
-    if (j < n) {
-      par[t] = p.parents[(size_t)b * B + j];
-      tok[t] = p.tree_tokens[(size_t)b * B + j];
-    }
+    const bool ok = j < n;
+    par[t] = ok ? p.parents[(size_t)b * B + j] : -2;
+    tok[t] = ok ? p.tree_tokens[(size_t)b * B + j] : 0;
+    tg[t] = ok ? tgt[j + 1] : 0;
   }
-  const int32_t* tgt = p.target_tokens + (size_t)b * (B + 1);
-  int cur = 0, len = 0;
+  const int root_tgt = tgt[0];
+  // target token of node u (uniform): the root's, or a read of the owner lane
+  auto target_of = [&](int u) -> int {
+    if (u == 0) return root_tgt;
+    const int j = u - 1, t = j >> 6, src = j & 63;
+    int v = 0;
+#pragma unroll
+    for (int q = 0; q < kWalkMaxPerLane; ++q)
+      if (q == t) v = __shfl(tg[q], src);
+    return v;
+  };
+  int cur = 0, len = 0, want = root_tgt;
   while (len < L) {
-    const int want = tgt[cur];
-    int found = 0x7FFFFFFF;
+    // the child of cur carrying the wanted token (lowest node number if several)
+    int found = 0;
 #pragma unroll
     for (int t = 0; t < kWalkMaxPerLane; ++t) {
-      const int j = lane + t * kWave;
-      if (par[t] == cur && tok[t] == want) found = j + 1;
+      const uint64_t M = __ballot(par[t] == cur && tok[t] == want);
+      if (found == 0 && M) found = t * kWave + __builtin_ctzll(M) + 1;
     }
-    found = wave_min(found);
-    if (found == 0x7FFFFFFF) break;
+    if (found == 0) break;
     if (lane == 0) p.accepted_nodes[(size_t)b * L + len] = found;
     ++len;
     cur = found;
+    want = target_of(cur);
   }
   for (int i = len + lane; i < L; i += kWave) p.accepted_nodes[(size_t)b * L + i] = -1;
   if (lane == 0) {
     p.accept_len[b] = len;
-    p.next_token[b] = tgt[cur];
+    p.next_token[b] = want;
   }
 }
 
