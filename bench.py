@@ -81,6 +81,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--buffers", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 3 device-to-device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): every draft tree is "
@@ -90,6 +92,18 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.copy_probe:
+        # A plain copy of known size: what FETCH_SIZE / WRITE_SIZE read for it
+        # calibrates the per-dispatch byte counts of the kernels.
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+        return 0
 
     import draft_tree_construction_depth_amd as pkg
     from draft_tree_construction_depth_amd import gen
