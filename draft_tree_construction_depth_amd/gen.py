@@ -155,3 +155,56 @@ def fresh_argmax_targets(cfg_id: int, seed: int, batch: int, B: int, V: int, *,
         g = 4.0 * rng.standard_normal((B + 1, V))
         out[i] = np.argmax(g, axis=1).astype(np.int32)
     return out
+
+
+# ---------------------------------------------------------------------------
+# TreeSpark parent-conditioned expansion (TreeSpark README, item 1: one
+# backbone pass gives per-depth vocabulary logits l_d; a first-order Markov
+# head adds W . e(t_u) for parent token t_u; k = 4, 7 depths, N = 32 packed
+# non-root nodes; the model width 2560 is Qwen3-4B's hidden size).
+TREESPARK = dict(batch=32, D=7, V=151936, H=2560, k=4, F=4, N=32, sigma=(1.0, 6.0), wscale=0.02)
+CFG_TREESPARK = 4
+
+
+def treespark_backbone(seed: int, b: int, *, D: int, V: int, sigma=(1.0, 6.0)) -> np.ndarray:
+    """Backbone logits of one request, [D, V] bf16 bits: per-depth sigma ~ U[lo, hi] Gaussian."""
+    rng = _rng(CFG_TREESPARK, seed, b)
+    lo, hi = sigma
+    s = rng.uniform(lo, hi, D).astype(np.float32)
+    g = rng.standard_normal((D, V), dtype=np.float32)
+    return f32_to_bf16_bits((s[:, None] * g).astype(np.float32))
+
+
+def treespark_matrix(seed: int, which: int, *, V: int, H: int, wscale: float = 0.02) -> np.ndarray:
+    """Head weight (which = 2) or embedding table (which = 3): [V, H] bf16 bits, N(0, wscale^2)."""
+    assert which in (2, 3)
+    rng = _rng(CFG_TREESPARK, seed, 0, stream=which)
+    out = np.empty((V, H), dtype=np.uint16)
+    step = 8192  # generate in row blocks to bound the float32 temporary
+    for r0 in range(0, V, step):
+        r1 = min(V, r0 + step)
+        out[r0:r1] = f32_to_bf16_bits(
+            (rng.standard_normal((r1 - r0, H), dtype=np.float32) * np.float32(wscale)).astype(np.float32))
+    return out
+
+
+def treespark_anchor(seed: int, b: int, *, V: int) -> int:
+    """The anchor (root) token of request b."""
+    return int(_rng(CFG_TREESPARK, seed, b, stream=4).integers(0, V))
+
+
+def treespark_inputs(seed: int = 0, *, batch: int | None = None, first: int = 0, D: int | None = None,
+                     V: int | None = None, H: int | None = None, sigma=None, wscale: float | None = None):
+    """(backbone [batch, D, V] bf16 bits, W [V, H] bf16 bits, E [V, H] bf16 bits, anchor [batch] int32)."""
+    c = TREESPARK
+    batch = c["batch"] if batch is None else batch
+    D = c["D"] if D is None else D
+    V = c["V"] if V is None else V
+    H = c["H"] if H is None else H
+    sigma = c["sigma"] if sigma is None else sigma
+    wscale = c["wscale"] if wscale is None else wscale
+    bb = np.stack([treespark_backbone(seed, first + b, D=D, V=V, sigma=sigma) for b in range(batch)])
+    W = treespark_matrix(seed, 2, V=V, H=H, wscale=wscale)
+    E = treespark_matrix(seed, 3, V=V, H=H, wscale=wscale)
+    anchor = np.array([treespark_anchor(seed, first + b, V=V) for b in range(batch)], dtype=np.int32)
+    return bb, W, E, anchor
