@@ -54,6 +54,11 @@ def lib() -> C.CDLL:
         L.ddtree_accept.argtypes = [p, p, p, p, i64, i32, i32, p, p, p, p]
         L.ddtree_row_topk.restype = C.c_int
         L.ddtree_row_topk.argtypes = [p, C.c_int, i64, i64, i32, p, p, p, p, sz, p]
+        L.treespark_workspace_size.restype = sz
+        L.treespark_workspace_size.argtypes = [i64, i32, i64, i32, i32, i32, i32]
+        L.treespark_expand.restype = C.c_int
+        L.treespark_expand.argtypes = [p, p, p, p, i64, i32, i64, i32, i32, i32, i32, p, p, p, p,
+                                       p, p, sz, p]
         _lib = L
     return _lib
 
@@ -223,4 +228,37 @@ def ddtree_row_topk(logits: torch.Tensor, K: int, *, out: dict | None = None,
     rc = lib().ddtree_row_topk(_ptr(logits), dt, rows, V, K, _ptr(out["ids"]), _ptr(out["vals"]),
                                _ptr(out["lse"]), _ptr(ws), ws.numel(), _stream(dev))
     _check("ddtree_row_topk", rc)
+    return out
+
+
+_BF16 = (torch.bfloat16,)
+
+
+def treespark_expand(backbone: torch.Tensor, W: torch.Tensor, E: torch.Tensor,
+                     anchor: torch.Tensor, *, k: int = 4, F: int = 4, N: int = 32,
+                     out: dict | None = None, ws: torch.Tensor | None = None) -> dict:
+    """TreeSpark expansion: backbone [batch, D, V], W / E [V, H] (bf16), anchor [batch]."""
+    _arg(backbone, "backbone", _BF16)
+    batch, D, V = backbone.shape
+    _arg(W, "W", _BF16)
+    Vw, H = W.shape
+    if Vw != V:
+        raise ValueError(f"W must have {V} rows, got {Vw}")
+    _arg(E, "E", _BF16, (V, H))
+    _arg(anchor, "anchor", _I32, (batch,))
+    dev = backbone.device
+    if out is None:
+        out = dict(tree_tokens=torch.empty((batch, N), dtype=torch.int32, device=dev),
+                   parents=torch.empty((batch, N), dtype=torch.int32, device=dev),
+                   logq=torch.empty((batch, N), dtype=torch.float32, device=dev),
+                   depths=torch.empty((batch, N), dtype=torch.int32, device=dev),
+                   num_nodes=torch.empty((batch,), dtype=torch.int32, device=dev))
+    size = lib().treespark_workspace_size(batch, D, V, H, k, F, N)
+    if ws is None:
+        ws = workspace("treespark", size, dev, (batch, D, V, H, k, F, N))
+    rc = lib().treespark_expand(_ptr(backbone), _ptr(W), _ptr(E), _ptr(anchor), batch, D, V, H, k,
+                                F, N, _ptr(out["tree_tokens"]), _ptr(out["parents"]),
+                                _ptr(out["logq"]), _ptr(out.get("depths")),
+                                _ptr(out["num_nodes"]), _ptr(ws), ws.numel(), _stream(dev))
+    _check("treespark_expand", rc)
     return out

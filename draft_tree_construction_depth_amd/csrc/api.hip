@@ -6,6 +6,7 @@
 
 #include "select.hpp"
 #include "stage1.hpp"
+#include "treespark.hpp"
 #include "walk.hpp"
 
 namespace {
@@ -217,6 +218,76 @@ int launch_select(const float* vals, const int32_t* ids, const double* lse, int6
   return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
 }
 
+// ---- TreeSpark: per-depth parent counts and the workspace layout ----------
+struct TsShape {
+  int kk;          // children per parent, min(k, V)
+  int Fd[ddt::kTsDMax];  // parents per request at each depth
+  int Fmax;        // largest of them
+  int cmax;        // candidates per request
+  int64_t nvt;     // 128-row tiles of the vocabulary
+  int64_t Mtot;    // partial-record columns (batch * Fmax)
+};
+
+TsShape ts_shape(int64_t batch, int D, int64_t V, int k, int F) {
+  TsShape sh;
+  sh.kk = (int64_t)k < V ? k : (int)V;
+  int fd = 1;
+  sh.Fmax = 1;
+  sh.cmax = 0;
+  for (int d = 0; d < D; ++d) {
+    sh.Fd[d] = fd;
+    sh.Fmax = fd > sh.Fmax ? fd : sh.Fmax;
+    sh.cmax += fd * sh.kk;
+    const int nxt = fd * sh.kk;
+    fd = nxt < F ? nxt : F;
+  }
+  sh.nvt = (V + ddt::kTsBV - 1) / ddt::kTsBV;
+  sh.Mtot = batch * sh.Fmax;
+  return sh;
+}
+
+struct TsLayout {
+  size_t pmax, psum, pval, pid, ctok, cscore, ckey, cpar, cdep, ccount, fcount, ptok[2], pcand[2];
+  size_t total;
+};
+
+TsLayout ts_layout(int64_t batch, const TsShape& sh) {
+  TsLayout l;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  const size_t rec = (size_t)sh.nvt * sh.Mtot;
+  l.pmax = take(rec * 4);
+  l.psum = take(rec * 4);
+  l.pval = take(rec * ddt::kTsKMax * 4);
+  l.pid = take(rec * ddt::kTsKMax * 4);
+  const size_t nc = (size_t)batch * sh.cmax;
+  l.ctok = take(nc * 4);
+  l.cscore = take(nc * 8);
+  l.ckey = take(nc * 8);
+  l.cpar = take(nc * 4);
+  l.cdep = take(nc * 4);
+  l.ccount = take((size_t)batch * 4);
+  l.fcount = take((size_t)batch * 4);
+  for (int q = 0; q < 2; ++q) {
+    l.ptok[q] = take((size_t)sh.Mtot * 4);
+    l.pcand[q] = take((size_t)sh.Mtot * 4);
+  }
+  l.total = o;
+  return l;
+}
+
+int ts_check(int64_t batch, int32_t D, int64_t V, int32_t H, int32_t k, int32_t F, int32_t N) {
+  if (batch < 0 || D <= 0 || V <= 0 || H <= 0 || k <= 0 || F <= 0 || N <= 0) return DDT_EINVAL;
+  if (D > ddt::kTsDMax || k > ddt::kTsKMax || F > ddt::kTsFMax || H % ddt::kTsKT != 0 ||
+      V > 0x7FFFFFFFLL || N > 4096 || batch > 0x7FFFFFFFLL / ddt::kTsFMax)
+    return DDT_ENOTSUP;
+  return DDT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -347,6 +418,101 @@ int ddtree_accept(const int32_t* tree_tokens, const int32_t* parents, const int3
   wp.accept_len = accept_len;
   wp.next_token = next_token;
   hipLaunchKernelGGL(ddt::walk_kernel, dim3((unsigned)batch), dim3(ddt::kWave), 0, stream, wp);
+  return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
+}
+
+size_t treespark_workspace_size(int64_t batch, int32_t D, int64_t V, int32_t H, int32_t k,
+                                int32_t F, int32_t N) {
+  if (ts_check(batch, D, V, H, k, F, N) != DDT_OK || batch == 0) return 0;
+  return ts_layout(batch, ts_shape(batch, D, V, k, F)).total;
+}
+
+int treespark_expand(const void* backbone, const void* W, const void* E, const int32_t* anchor,
+                     int64_t batch, int32_t D, int64_t V, int32_t H, int32_t k, int32_t F,
+                     int32_t N, int32_t* tree_tokens, int32_t* parents, float* logq,
+                     int32_t* depths, int32_t* num_nodes, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  const int chk = ts_check(batch, D, V, H, k, F, N);
+  if (chk != DDT_OK) return chk;
+  if (batch == 0) return DDT_OK;
+  if (!backbone || !W || !E || !anchor || !tree_tokens || !parents || !logq || !num_nodes ||
+      !workspace)
+    return DDT_EINVAL;
+  if (((uintptr_t)W | (uintptr_t)E) % 16 != 0) return DDT_EINVAL;
+  const TsShape sh = ts_shape(batch, D, V, k, F);
+  const TsLayout lay = ts_layout(batch, sh);
+  if (workspace_bytes < lay.total) return DDT_EWORKSPACE;
+  char* ws = (char*)workspace;
+  ddt::TsState st;
+  st.ctok = (int32_t*)(ws + lay.ctok);
+  st.cscore = (double*)(ws + lay.cscore);
+  st.ckey = (uint64_t*)(ws + lay.ckey);
+  st.cpar = (int32_t*)(ws + lay.cpar);
+  st.cdep = (int32_t*)(ws + lay.cdep);
+  st.ccount = (int32_t*)(ws + lay.ccount);
+  st.fcount = (int32_t*)(ws + lay.fcount);
+  for (int q = 0; q < 2; ++q) {
+    st.ptok[q] = (int32_t*)(ws + lay.ptok[q]);
+    st.pcand[q] = (int32_t*)(ws + lay.pcand[q]);
+  }
+  st.cmax = sh.cmax;
+  float* pmax = (float*)(ws + lay.pmax);
+  float* psum = (float*)(ws + lay.psum);
+  float* pval = (float*)(ws + lay.pval);
+  int32_t* pid = (int32_t*)(ws + lay.pid);
+
+  hipLaunchKernelGGL(ddt::ts_init_kernel, dim3((unsigned)((batch + 255) / 256)), dim3(256), 0,
+                     stream, st, anchor, batch);
+  for (int d = 0; d < D; ++d) {
+    const int Fd = sh.Fd[d];
+    const int64_t M = batch * Fd;
+    ddt::TsGemmParams gp;
+    gp.W = (const uint16_t*)W;
+    gp.E = (const uint16_t*)E;
+    gp.bb = (const uint16_t*)backbone;
+    gp.ptok = st.ptok[d & 1];
+    gp.V = V;
+    gp.H = H;
+    gp.D = D;
+    gp.d = d;
+    gp.M = (int32_t)M;
+    gp.Fd = Fd;
+    gp.k = sh.kk;
+    gp.Mtot = (int32_t)sh.Mtot;
+    gp.pmax = pmax;
+    gp.psum = psum;
+    gp.pval = pval;
+    gp.pid = pid;
+    hipLaunchKernelGGL(ddt::ts_gemm_kernel,
+                       dim3((unsigned)sh.nvt, (unsigned)((M + ddt::kTsBM - 1) / ddt::kTsBM)),
+                       dim3(ddt::kTsThreads), 0, stream, gp);
+    ddt::TsMergeParams mp;
+    mp.st = st;
+    mp.pmax = pmax;
+    mp.psum = psum;
+    mp.pval = pval;
+    mp.pid = pid;
+    mp.nvt = (int32_t)sh.nvt;
+    mp.Mtot = (int32_t)sh.Mtot;
+    mp.d = d;
+    mp.D = D;
+    mp.Fd = Fd;
+    mp.Fn = d + 1 < D ? sh.Fd[d + 1] : 1;
+    mp.k = sh.kk;
+    mp.F = F;
+    hipLaunchKernelGGL(ddt::ts_merge_kernel, dim3((unsigned)batch), dim3(ddt::kTsThreads), 0,
+                       stream, mp);
+  }
+  ddt::TsPackParams pp;
+  pp.st = st;
+  pp.N = N;
+  pp.tree_tokens = tree_tokens;
+  pp.parents = parents;
+  pp.logq = logq;
+  pp.depths = depths;
+  pp.num_nodes = num_nodes;
+  hipLaunchKernelGGL(ddt::ts_pack_kernel, dim3((unsigned)batch), dim3(ddt::kTsThreads),
+                     (size_t)sh.cmax * 4, stream, pp);
   return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
 }
 

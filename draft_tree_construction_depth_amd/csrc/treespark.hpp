@@ -1,0 +1,478 @@
+// TreeSpark parent-conditioned tree expansion.
+//
+// TreeSpark README, item 1 ("Parent-Conditioned Tree Drafting from One
+// Backbone Pass"): one backbone pass gives vocabulary logits l_d for every
+// draft depth; a first-order Markov head specialises depth d to a parent
+// token t_u, z_d(u) = l_d + W . e(t_u) with e(t) = E[t]; trees expand with
+// branching factor k per parent, the frontier is pruned by joint path score
+// and a global top-N packing keeps N non-root nodes (item 2 names the policy:
+// per-parent top-k expansion, joint path-score frontier pruning, global
+// top-N packing).
+//
+// Per depth d (all requests at once):
+//  ts_gemm_kernel   Z[v, m] = sum_h W[v, h] E[t_m, h] for every vocabulary
+//                   row v and every frontier parent m, on MFMA (bf16 in,
+//                   float32 accumulate), with the epilogue fused: z = Z + l_d,
+//                   then per parent column the tile's max, sum of exp and
+//                   top-k -> one partial record per (128-row tile, parent).
+//                   W (V x H bf16, 778 MB at the README shape) streams from
+//                   HBM once per depth; the parents' embedding rows are
+//                   shared by the four waves through LDS.
+//  ts_merge_kernel  per request: each parent's log-sum-exp (float64) and
+//                   top-k from the partials; children scored parent score +
+//                   z - lse; the frontier for d+1 = the best F children.
+// Then ts_pack_kernel ranks every candidate and keeps the best N.
+// Order everywhere: score desc, then rank tuple lexicographic asc, the rank
+// tuple held as 4-bit digits (j + 1) from the top of a 64-bit key so that a
+// prefix precedes its extensions. Ties of z inside a parent: lower token id.
+#pragma once
+
+#include "common.hpp"
+
+namespace ddt {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTsThreads = 256;
+constexpr int kTsBV = 128;     // W rows per workgroup (4 waves x 32)
+constexpr int kTsBM = 128;     // parent columns per workgroup (4 MFMA tiles of 32)
+constexpr int kTsKT = 64;      // reduction elements per step
+constexpr int kTsGPad = 8;     // LDS row padding (bf16) against bank conflicts
+constexpr int kTsKMax = 8;     // largest branching factor k
+constexpr int kTsFMax = 8;     // largest frontier width F
+constexpr int kTsDMax = 16;    // largest depth (4-bit digits in a 64-bit key)
+
+struct TsGemmParams {
+  const uint16_t* W;       // [V][H] bf16
+  const uint16_t* E;       // [V][H] bf16
+  const uint16_t* bb;      // [batch][D][V] bf16 backbone logits
+  const int32_t* ptok;     // [M] parent tokens
+  int64_t V;
+  int32_t H, D, d;         // d: 0-based depth
+  int32_t M, Fd, k;        // parents, parents per request, branching factor
+  int32_t Mtot;            // column stride of the partial records
+  float* pmax;             // [nvt][Mtot]
+  float* psum;             // [nvt][Mtot] sum of exp(z - pmax)
+  float* pval;             // [nvt][Mtot][kTsKMax] top-k z, best first
+  int32_t* pid;            // [nvt][Mtot][kTsKMax]
+};
+
+// Insert (x, id) into a best-first list of length k (z desc, id asc),
+// branch-free: with better(i) = (x, id) precedes entry i (monotone along the
+// sorted list), entry i becomes entry i-1 if better(i-1), else x if better(i).
+__device__ __forceinline__ void ts_insert(float (&val)[kTsKMax], int (&ids)[kTsKMax], int k, float x,
+                                          int id) {
+  bool bt[kTsKMax];
+#pragma unroll
+  for (int i = 0; i < kTsKMax; ++i) bt[i] = i < k && (x > val[i] || (x == val[i] && id < ids[i]));
+#pragma unroll
+  for (int i = kTsKMax - 1; i >= 0; --i) {
+    const bool shift = i > 0 && bt[i > 0 ? i - 1 : 0];
+    const float pv = i > 0 ? val[i > 0 ? i - 1 : 0] : x;
+    const int pi = i > 0 ? ids[i > 0 ? i - 1 : 0] : id;
+    val[i] = shift ? pv : (bt[i] ? x : val[i]);
+    ids[i] = shift ? pi : (bt[i] ? id : ids[i]);
+  }
+}
+
+struct TsGemmSmem {
+  union {
+    uint16_t g[2][kTsBM][kTsKT + kTsGPad];  // parents' embedding rows, double buffered
+    struct {
+      float mx[4][kTsBM];
+      float sm[4][kTsBM];
+      float val[4][kTsBM][kTsKMax];
+      int id[4][kTsBM][kTsKMax];
+    } red;  // per-wave partials of the epilogue
+  };
+};
+
+__global__ __launch_bounds__(kTsThreads) void ts_gemm_kernel(TsGemmParams p) {
+  __shared__ TsGemmSmem sm;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int vt = blockIdx.x;
+  const int m0 = blockIdx.y * kTsBM;
+  const int H = p.H, K = p.k;
+  const int64_t V = p.V;
+  const int ncols = p.M - m0 < kTsBM ? p.M - m0 : kTsBM;
+  const int nct = (ncols + 31) >> 5;  // MFMA column tiles in use
+
+  // this lane's W row (A operand: row l % 32 of the wave's 32 rows)
+  const int64_t vrow = (int64_t)vt * kTsBV + w * 32 + (l & 31);
+  const int64_t vload = vrow < V ? vrow : V - 1;  // rows past V load row V-1, masked later
+  const uint16_t* wrow = p.W + vload * H + 8 * (l >> 5);
+
+  // embedding-row staging: thread t copies 16-byte chunk (t % 8) of rows t/8 + 32 i
+  const int gch = tid & 7, grow0 = tid >> 3;
+  const uint16_t* erow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = grow0 + 32 * i;
+    const int m = m0 + (r < ncols ? r : 0);
+    erow[i] = p.E + (int64_t)p.ptok[m] * H + 8 * gch;
+  }
+
+  const int nks = H / kTsKT;
+  u32x4 wa[4], wb[4], ga[4];
+  auto load_w = [&](u32x4 (&dst)[4], int ks) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dst[s] = *(const u32x4*)(wrow + ks * kTsKT + 16 * s);
+  };
+  auto load_g = [&](int ks) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ga[i] = *(const u32x4*)(erow[i] + ks * kTsKT);
+  };
+  auto store_g = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(u32x4*)&sm.g[buf][grow0 + 32 * i][8 * gch] = ga[i];
+  };
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+
+  load_w(wa, 0);
+  load_g(0);
+  store_g(0);
+  __syncthreads();
+  for (int ks = 0; ks < nks; ++ks) {
+    const int buf = ks & 1;
+    const bool more = ks + 1 < nks;
+    if (more) {
+      load_w(wb, ks + 1);
+      load_g(ks + 1);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, wa[s]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (c < nct) {
+          const u32x4 braw = *(const u32x4*)&sm.g[buf][c * 32 + (l & 31)][16 * s + 8 * (l >> 5)];
+          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, braw),
+                                                           acc[c], 0, 0, 0);
+        }
+      }
+    }
+    if (more) {
+      store_g(buf ^ 1);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) wa[s] = wb[s];
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: z = Z + l_d; per column the wave's max, exp sum and top-k
+  // acc[c][r] holds row 8 (r / 4) + 4 (l / 32) + r % 4 of the wave's 32 rows,
+  // column c * 32 + l % 32; lanes l and l ^ 32 share a column.
+  const int64_t vbase = (int64_t)vt * kTsBV + w * 32;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (c >= nct) continue;
+    const int col = c * 32 + (l & 31);
+    const bool colok = col < ncols;
+    const int m = m0 + (colok ? col : 0);
+    const int req = m / p.Fd;
+    const uint16_t* lrow = p.bb + ((int64_t)req * p.D + p.d) * V;
+    float z[16];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t v = vbase + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+      const bool ok = v < V;
+      const float lv = __uint_as_float((uint32_t)lrow[ok ? v : V - 1] << 16);  // in-bounds read
+      z[r] = ok ? acc[c][r] + lv : -INFINITY;
+      mx = fmaxf(mx, z[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float s = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += z[r] == -INFINITY ? 0.0f : __expf(z[r] - mx);
+    s += __shfl_xor(s, 32);
+    float tv[kTsKMax];
+    int ti[kTsKMax];
+#pragma unroll
+    for (int i = 0; i < kTsKMax; ++i) {
+      tv[i] = -INFINITY;
+      ti[i] = 0x7FFFFFFF;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t v = vbase + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+      if (v < V) ts_insert(tv, ti, K, z[r], (int)v);
+    }
+    // merge the partner lane's list
+    float ov[kTsKMax];
+    int oi[kTsKMax];
+#pragma unroll
+    for (int i = 0; i < kTsKMax; ++i) {
+      ov[i] = __shfl_xor(tv[i], 32);
+      oi[i] = __shfl_xor(ti[i], 32);
+    }
+#pragma unroll
+    for (int i = 0; i < kTsKMax; ++i)
+      if (i < K && oi[i] != 0x7FFFFFFF) ts_insert(tv, ti, K, ov[i], oi[i]);
+    if (l < 32) {
+      sm.red.mx[w][col] = mx;
+      sm.red.sm[w][col] = s;
+#pragma unroll
+      for (int i = 0; i < kTsKMax; ++i) {
+        sm.red.val[w][col][i] = tv[i];
+        sm.red.id[w][col][i] = ti[i];
+      }
+    }
+  }
+  __syncthreads();
+  // combine the four waves: one thread per column
+  if (tid < ncols) {
+    const int col = tid;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mx = fmaxf(mx, sm.red.mx[q][col]);
+    float s = 0.0f;
+    float tv[kTsKMax];
+    int ti[kTsKMax];
+#pragma unroll
+    for (int i = 0; i < kTsKMax; ++i) {
+      tv[i] = -INFINITY;
+      ti[i] = 0x7FFFFFFF;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float mq = sm.red.mx[q][col];
+      if (mq != -INFINITY) s += sm.red.sm[q][col] * __expf(mq - mx);
+#pragma unroll
+      for (int i = 0; i < kTsKMax; ++i) {
+        const int id = sm.red.id[q][col][i];
+        if (i < K && id != 0x7FFFFFFF) ts_insert(tv, ti, K, sm.red.val[q][col][i], id);
+      }
+    }
+    const size_t o = (size_t)vt * p.Mtot + m0 + col;
+    p.pmax[o] = mx;
+    p.psum[o] = s;
+#pragma unroll
+    for (int i = 0; i < kTsKMax; ++i) {
+      p.pval[o * kTsKMax + i] = tv[i];
+      p.pid[o * kTsKMax + i] = ti[i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Candidate store and per-depth parent lists (workspace).
+struct TsState {
+  int32_t* ctok;    // [batch][cmax] candidate tokens
+  double* cscore;   // [batch][cmax] path scores
+  uint64_t* ckey;   // [batch][cmax] rank-tuple keys
+  int32_t* cpar;    // [batch][cmax] parent candidate (-1: the anchor)
+  int32_t* cdep;    // [batch][cmax] depth (1-based)
+  int32_t* ccount;  // [batch]
+  int32_t* fcount;  // [batch] parents of the current depth
+  int32_t* ptok[2];   // [batch * F] parent tokens, by depth parity
+  int32_t* pcand[2];  // [batch * F] parent candidate index (-1: anchor)
+  int32_t cmax;
+};
+
+__global__ void ts_init_kernel(TsState st, const int32_t* anchor, int64_t batch) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= batch) return;
+  st.ccount[b] = 0;
+  st.fcount[b] = 1;
+  st.ptok[0][b] = anchor[b];
+  st.pcand[0][b] = -1;
+}
+
+struct TsMergeParams {
+  TsState st;
+  const float* pmax;
+  const float* psum;
+  const float* pval;
+  const int32_t* pid;
+  int32_t nvt, Mtot;
+  int32_t d, D;       // 0-based depth, depths
+  int32_t Fd, Fn;     // parents per request at this depth / the next
+  int32_t k, F;
+};
+
+__device__ __forceinline__ uint64_t ts_zkey(float x, int id) {
+  return ((uint64_t)order_key(__float_as_uint(x)) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id);
+}
+
+__global__ __launch_bounds__(kTsThreads) void ts_merge_kernel(TsMergeParams p) {
+  __shared__ double red_d[kTsThreads / kWave];
+  __shared__ uint64_t red_k[kTsThreads / kWave];
+  __shared__ double lse_s;
+  __shared__ uint64_t win[kTsKMax];
+  __shared__ int32_t ch_tok[kTsFMax * kTsKMax];
+  __shared__ double ch_score[kTsFMax * kTsKMax];
+  __shared__ uint64_t ch_key[kTsFMax * kTsKMax];
+  __shared__ int32_t ch_cand[kTsFMax * kTsKMax];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int64_t b = blockIdx.x;
+  TsState& st = p.st;
+  const int par = p.d & 1;
+  const int nf = st.fcount[b];
+  const int K = p.k;
+  const int base = st.ccount[b];
+  const int shift = 4 * (kTsDMax - 1 - p.d);  // this depth's digit
+  for (int i = 0; i < nf; ++i) {
+    const int m = (int)b * p.Fd + i;
+    // log-sum-exp over the partials, float64
+    double mx = -INFINITY;
+    for (int t = tid; t < p.nvt; t += kTsThreads) {
+      const double x = p.pmax[(size_t)t * p.Mtot + m];
+      mx = x > mx ? x : mx;
+    }
+    mx = wave_max(mx);
+    if (lane == 0) red_d[w] = mx;
+    __syncthreads();
+    double M = red_d[0];
+    for (int q = 1; q < kTsThreads / kWave; ++q) M = red_d[q] > M ? red_d[q] : M;
+    __syncthreads();
+    double s = 0.0;
+    for (int t = tid; t < p.nvt; t += kTsThreads) {
+      const size_t o = (size_t)t * p.Mtot + m;
+      const double x = p.pmax[o];
+      if (x != -INFINITY) s += (double)p.psum[o] * exp(x - M);
+    }
+    s = wave_sum(s);
+    if (lane == 0) red_d[w] = s;
+    __syncthreads();
+    if (tid == 0) {
+      double tot = 0.0;
+      for (int q = 0; q < kTsThreads / kWave; ++q) tot += red_d[q];
+      lse_s = M + log(tot);
+    }
+    // top-k over the partial lists: k rounds of a block-wide max of keys
+    // (value key << 32 | ~id); each thread offers its best key not yet taken
+    float tv[kTsKMax];
+    int ti[kTsKMax];
+#pragma unroll
+    for (int j = 0; j < kTsKMax; ++j) {
+      tv[j] = -INFINITY;
+      ti[j] = 0x7FFFFFFF;
+    }
+    for (int t = tid; t < p.nvt; t += kTsThreads) {
+      const size_t o = ((size_t)t * p.Mtot + m) * kTsKMax;
+#pragma unroll
+      for (int j = 0; j < kTsKMax; ++j) {
+        const int id = p.pid[o + j];
+        if (j < K && id != 0x7FFFFFFF) ts_insert(tv, ti, K, p.pval[o + j], id);
+      }
+    }
+    int head = 0;
+    for (int r = 0; r < K; ++r) {
+      uint64_t mine = 0;
+#pragma unroll
+      for (int j = 0; j < kTsKMax; ++j)
+        if (j == head && ti[j] != 0x7FFFFFFF) mine = ts_zkey(tv[j], ti[j]);
+      const uint64_t wmax = wave_max(mine);
+      __syncthreads();
+      if (lane == 0) red_k[w] = wmax;
+      __syncthreads();
+      uint64_t best = red_k[0];
+      for (int q = 1; q < kTsThreads / kWave; ++q) best = red_k[q] > best ? red_k[q] : best;
+      if (mine == best && best != 0) ++head;  // keys are unique: one owner
+      if (tid == 0) win[r] = best;
+    }
+    __syncthreads();
+    if (tid < K) {
+      const uint64_t kk = win[tid];
+      const int c = i * K + tid;
+      const int pc = st.pcand[par][m];
+      const double pscore = pc < 0 ? 0.0 : st.cscore[b * st.cmax + pc];
+      const uint64_t pkey = pc < 0 ? 0ull : st.ckey[b * st.cmax + pc];
+      const float zval = key_value((uint32_t)(kk >> 32));
+      ch_tok[c] = (int32_t)(0xFFFFFFFFu - (uint32_t)kk);
+      ch_score[c] = pscore + ((double)zval - lse_s);
+      ch_key[c] = pkey | ((uint64_t)(tid + 1) << shift);
+      ch_cand[c] = pc;
+    }
+    __syncthreads();
+  }
+  // append the children; the frontier for the next depth = the best F of them
+  const int nch = nf * K;
+  if (tid < nch) {
+    const size_t o = (size_t)b * st.cmax + base + tid;
+    st.ctok[o] = ch_tok[tid];
+    st.cscore[o] = ch_score[tid];
+    st.ckey[o] = ch_key[tid];
+    st.cpar[o] = ch_cand[tid];
+    st.cdep[o] = p.d + 1;
+    if (p.d + 1 < p.D) {
+      int rank = 0;
+      for (int j = 0; j < nch; ++j) {
+        const bool before = ch_score[j] > ch_score[tid] ||
+                            (ch_score[j] == ch_score[tid] && ch_key[j] < ch_key[tid]);
+        rank += before ? 1 : 0;
+      }
+      if (rank < p.F) {
+        st.ptok[par ^ 1][(size_t)b * p.Fn + rank] = ch_tok[tid];
+        st.pcand[par ^ 1][(size_t)b * p.Fn + rank] = base + tid;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    st.ccount[b] = base + nch;
+    st.fcount[b] = nch < p.F ? nch : p.F;
+  }
+}
+
+struct TsPackParams {
+  TsState st;
+  int32_t N;
+  int32_t* tree_tokens;  // [batch][N]
+  int32_t* parents;
+  float* logq;
+  int32_t* depths;
+  int32_t* num_nodes;
+};
+
+// Global top-N packing: each candidate's rank is the number of candidates
+// before it; the best N take positions 1..N (0 = the anchor).
+__global__ __launch_bounds__(kTsThreads) void ts_pack_kernel(TsPackParams p) {
+  const int64_t b = blockIdx.x;
+  const TsState& st = p.st;
+  const int n = st.ccount[b];
+  const size_t cb = (size_t)b * st.cmax;
+  const int N = p.N;
+  const int nsel = n < N ? n : N;
+  extern __shared__ int32_t rank_s[];  // [cmax]
+  for (int i = threadIdx.x; i < n; i += kTsThreads) {
+    const double si = st.cscore[cb + i];
+    const uint64_t ki = st.ckey[cb + i];
+    int r = 0;
+    for (int j = 0; j < n; ++j) {
+      const double sj = st.cscore[cb + j];
+      r += (sj > si || (sj == si && st.ckey[cb + j] < ki)) ? 1 : 0;
+    }
+    rank_s[i] = r;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += kTsThreads) {
+    const int r = rank_s[i];
+    if (r < nsel) {
+      const size_t o = (size_t)b * N + r;
+      const int pc = st.cpar[cb + i];
+      p.tree_tokens[o] = st.ctok[cb + i];
+      p.parents[o] = pc < 0 ? 0 : rank_s[pc] + 1;
+      p.logq[o] = (float)st.cscore[cb + i];
+      if (p.depths) p.depths[o] = st.cdep[cb + i];
+    }
+  }
+  for (int j = nsel + threadIdx.x; j < N; j += kTsThreads) {
+    const size_t o = (size_t)b * N + j;
+    p.tree_tokens[o] = -1;
+    p.parents[o] = -1;
+    p.logq[o] = -INFINITY;
+    if (p.depths) p.depths[o] = 0;
+  }
+  if (threadIdx.x == 0) p.num_nodes[b] = nsel;
+}
+
+}  // namespace ddt

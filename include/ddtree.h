@@ -18,6 +18,10 @@
  *  - ddtree_accept: the greedy verifier walk. DDTree explainer, section 5;
  *    TreeSpark README, item 4 (argmax-following acceptance walk).
  *  - ddtree_row_topk: stage 1 alone (row log-sum-exp and sorted top-K).
+ *  - treespark_expand: TreeSpark's parent-conditioned tree. TreeSpark README,
+ *    item 1 (z_d(u) = l_d + W e(t_u), branching k over depths, global top-N
+ *    packing) and item 2 (per-parent top-k expansion, joint path-score
+ *    frontier pruning, global top-N packing).
  *    SparklingTree post, section "Step 1".
  *  - ddtree_select: stage 2 alone, from stage 1's tables. DDTree explainer,
  *    sections 3-4; SparklingTree post, section "Step 3".
@@ -173,6 +177,37 @@ int ddtree_accept(const int32_t* tree_tokens, const int32_t* parents, const int3
 int ddtree_row_topk(const void* logits, int dtype, int64_t rows, int64_t V, int32_t K,
                     int32_t* ids, float* vals, double* lse, void* workspace,
                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * treespark_expand -- TreeSpark's parent-conditioned expansion (TreeSpark
+ * README, items 1-2). For request b with anchor token a_b (the root, score
+ * 0) and depths d = 1..D: every frontier parent u (token t_u) gets
+ *   z = backbone[b][d-1] + W . E[t_u]          (over the whole vocabulary)
+ * and its top k = min(k, V) tokens by (z desc, id asc) become children
+ * scored score(u) + z[t] - logsumexp(z), rank tuple = u's + (j). The frontier
+ * of depth d+1 is the best F children of depth d; after depth D the best N
+ * of all candidates are packed. Order: score desc, then rank tuple
+ * lexicographic asc (a prefix before its extensions).
+ * backbone [batch][D][V] bf16 backbone logits; W, E [V][H] bf16 (head weight
+ *          and embedding table, 16-byte aligned); anchor [batch] int32 in
+ *          [0, V) (not validated on the device).
+ * Outputs [batch][N]: tree_tokens, parents (packed position of the parent,
+ *          0 = the anchor), logq (float path log-prob), depths (nullable);
+ *          num_nodes [batch] = min(N, candidates); the tail is padded with
+ *          -1, -1, -inf, 0. ddtree_mask builds the mask from parents.
+ * z accumulates in float32 (bf16 MFMA), log-sum-exp combines in float64.
+ * Supported: 1 <= D <= 16, 1 <= k <= 8, 1 <= F <= 8, 1 <= N <= 4096,
+ * H a positive multiple of 64, V < 2^31; otherwise DDT_ENOTSUP.
+ * The workspace (treespark_workspace_size bytes, no zero-fill needed) holds
+ * per-depth partial records and the candidates.
+ */
+size_t treespark_workspace_size(int64_t batch, int32_t D, int64_t V, int32_t H, int32_t k,
+                                int32_t F, int32_t N);
+int treespark_expand(const void* backbone, const void* W, const void* E, const int32_t* anchor,
+                     int64_t batch, int32_t D, int64_t V, int32_t H, int32_t k, int32_t F,
+                     int32_t N, int32_t* tree_tokens, int32_t* parents, float* logq,
+                     int32_t* depths, int32_t* num_nodes, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

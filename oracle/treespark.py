@@ -60,9 +60,10 @@ def _order_key(node):
     return (-node["score"], node["ranks"])
 
 
-def expand_request(bb: np.ndarray, W: np.ndarray, E: np.ndarray, anchor: int, *, k: int, F: int,
+def expand_request(bb: np.ndarray, W: np.ndarray, E, anchor: int, *, k: int, F: int,
                    N: int, diag: dict | None = None):
-    """One request. bb [D, V] float64 backbone logits, W / E [V, H] float64.
+    """One request. bb [D, V] float64 backbone logits, W [V, H] float64, E(t) the
+    float64 embedding row of token t.
 
     Returns (tree_tokens [N], parents [N], logq [N], depths [N], num_nodes);
     entries past num_nodes hold -1, -1, -inf, 0.
@@ -73,8 +74,9 @@ def expand_request(bb: np.ndarray, W: np.ndarray, E: np.ndarray, anchor: int, *,
     frontier = [root]
     candidates = []
     gaps = []  # per-parent k-th minus (k+1)-th z (excuse boundaries)
+    fgaps = []  # per depth: F-th minus (F+1)-th child score (frontier boundary)
     for d in range(1, D + 1):
-        E_rows = np.stack([E[u["token"]] for u in frontier])
+        E_rows = np.stack([E(u["token"]) for u in frontier])
         Z = parent_logits(bb[d - 1], W, E_rows)
         children = []
         for m, u in enumerate(frontier):
@@ -89,6 +91,8 @@ def expand_request(bb: np.ndarray, W: np.ndarray, E: np.ndarray, anchor: int, *,
         candidates.extend(children)
         if d < D:
             children.sort(key=_order_key)
+            if len(children) > F:
+                fgaps.append(children[F - 1]["score"] - children[F]["score"])
             frontier = children[:F]
     candidates.sort(key=_order_key)
     packed = candidates[:N]
@@ -107,6 +111,7 @@ def expand_request(bb: np.ndarray, W: np.ndarray, E: np.ndarray, anchor: int, *,
     if diag is not None:
         diag["candidates"] = len(candidates)
         diag["topk_gaps"] = gaps
+        diag["frontier_gaps"] = fgaps
         diag["pack_gap"] = (candidates[N - 1]["score"] - candidates[N]["score"]
                             if len(candidates) > N else np.inf)
         diag["scores"] = [c["score"] for c in candidates]
@@ -121,7 +126,7 @@ def expand(backbone_bits: np.ndarray, W_bits: np.ndarray, E_bits: np.ndarray, an
     """
     reqs = range(backbone_bits.shape[0]) if requests is None else list(requests)
     W = bf16_to_f64(W_bits)
-    E = bf16_to_f64(E_bits)
+    E = lambda t: bf16_to_f64(E_bits[t])
     out = dict(tree_tokens=[], parents=[], logq=[], depths=[], num_nodes=[])
     for b in reqs:
         dg = {} if diags is not None else None
