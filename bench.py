@@ -74,6 +74,62 @@ def cpu_baseline(x, Y, B, L):
             "sample": f"all {n} requests of one batch (build + mask + accept), {secs:.2f} s"}, o
 
 
+def treespark_bench(args) -> int:
+    """TreeSpark parent-conditioned expansion: 32 requests x 7 depths over
+    V = 151936 with a 2560-wide head; one step = one treespark_expand call."""
+    import numpy as np
+    import torch
+
+    import draft_tree_construction_depth_amd as pkg
+    from draft_tree_construction_depth_amd import gen
+
+    c = gen.TREESPARK
+    batch, D, V, H, k, F, N = (c[x] for x in ("batch", "D", "V", "H", "k", "F", "N"))
+    bb, W, E, anc = gen.treespark_inputs(0)
+    dev = torch.device("cuda:0")
+    as_bf16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
+        torch.bfloat16)
+    bbd, Wd, Ed = as_bf16(bb), as_bf16(W), as_bf16(E)
+    ancd = torch.from_numpy(anc).to(dev)
+    out = pkg.treespark_expand(bbd, Wd, Ed, ancd, k=k, F=F, N=N)
+    for _ in range(args.warmup):
+        pkg.treespark_expand(bbd, Wd, Ed, ancd, k=k, F=F, N=N, out=out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(args.steps):
+        pkg.treespark_expand(bbd, Wd, Ed, ancd, k=k, F=F, N=N, out=out)
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = a.elapsed_time(b) / args.steps
+    # parents per depth: 1 per request at depth 1, then min(F, previous * k)
+    fd, Ms = 1, []
+    for _ in range(D):
+        Ms.append(batch * fd)
+        fd = min(F, fd * k)
+    w_bytes = V * H * 2
+    alg_bytes = D * w_bytes + batch * D * V * 2 + sum(Ms) * H * 2
+    flops = sum(2.0 * V * H * m for m in Ms)
+    res = {
+        "metric": "TreeSpark trees/sec at batch 32, 7 depths, V=151936, H=2560, k=4, N=32",
+        "value": round(batch / (ms / 1e3), 1), "unit": "trees/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16/f32",
+        "data": "synthetic",
+        "config": {"workload": "treespark_batch32_D7_V151936_H2560_k4_F4_N32", "batch": batch,
+                   "D": D, "V": V, "H": H, "k": k, "F": F, "N": N},
+        "algorithmic_gbps": round(alg_bytes / (ms / 1e3) / 1e9, 1),
+        "hbm_frac": round(alg_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "mfma_tflops": round(flops / (ms / 1e3) / 1e12, 1),
+        "mfma_frac_bf16": round(flops / (ms / 1e3) / 2.5e15, 4),
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -81,6 +137,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--buffers", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--treespark", action="store_true",
+                    help="time treespark_expand on the TreeSpark workload instead (own JSON line)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 3 device-to-device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -107,6 +165,9 @@ def main() -> int:
 
     import draft_tree_construction_depth_amd as pkg
     from draft_tree_construction_depth_amd import gen
+
+    if args.treespark:
+        return treespark_bench(args)
 
     c = gen.CONFIGS[3]
     batch, L, V, B = c["batch"], c["L"], c["V"], c["B"]

@@ -500,8 +500,12 @@ int treespark_expand(const void* backbone, const void* W, const void* E, const i
     mp.Fn = d + 1 < D ? sh.Fd[d + 1] : 1;
     mp.k = sh.kk;
     mp.F = F;
-    hipLaunchKernelGGL(ddt::ts_merge_kernel, dim3((unsigned)batch), dim3(ddt::kTsThreads), 0,
-                       stream, mp);
+    if (sh.kk <= 4)
+      hipLaunchKernelGGL(ddt::ts_merge_kernel<4>, dim3((unsigned)batch),
+                         dim3(ddt::kTsMergeThreads), 0, stream, mp);
+    else
+      hipLaunchKernelGGL(ddt::ts_merge_kernel<8>, dim3((unsigned)batch),
+                         dim3(ddt::kTsMergeThreads), 0, stream, mp);
   }
   ddt::TsPackParams pp;
   pp.st = st;

@@ -115,7 +115,8 @@ __global__ __launch_bounds__(kTsThreads) void ts_gemm_kernel(TsGemmParams p) {
   }
 
   const int nks = H / kTsKT;
-  u32x4 wa[4], wb[4], ga[4];
+  // W k-steps ks+1 and ks+2 are in flight while ks is multiplied
+  u32x4 wa[4], wb[4], wc[4], ga[4];
   auto load_w = [&](u32x4 (&dst)[4], int ks) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) dst[s] = *(const u32x4*)(wrow + ks * kTsKT + 16 * s);
@@ -136,16 +137,16 @@ __global__ __launch_bounds__(kTsThreads) void ts_gemm_kernel(TsGemmParams p) {
     for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
 
   load_w(wa, 0);
+  load_w(wb, nks > 1 ? 1 : 0);
   load_g(0);
   store_g(0);
   __syncthreads();
   for (int ks = 0; ks < nks; ++ks) {
     const int buf = ks & 1;
     const bool more = ks + 1 < nks;
-    if (more) {
-      load_w(wb, ks + 1);
-      load_g(ks + 1);
-    }
+    // always issue (a valid k-step when past the end) so wait counts stay static
+    load_w(wc, ks + 2 < nks ? ks + 2 : nks - 1);
+    if (more) load_g(ks + 1);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const bf16x8 a = __builtin_bit_cast(bf16x8, wa[s]);
@@ -158,10 +159,11 @@ __global__ __launch_bounds__(kTsThreads) void ts_gemm_kernel(TsGemmParams p) {
         }
       }
     }
-    if (more) {
-      store_g(buf ^ 1);
+    if (more) store_g(buf ^ 1);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) wa[s] = wb[s];
+    for (int s = 0; s < 4; ++s) {
+      wa[s] = wb[s];
+      wb[s] = wc[s];
     }
     __syncthreads();
   }
@@ -302,16 +304,26 @@ __device__ __forceinline__ uint64_t ts_zkey(float x, int id) {
   return ((uint64_t)order_key(__float_as_uint(x)) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id);
 }
 
-__global__ __launch_bounds__(kTsThreads) void ts_merge_kernel(TsMergeParams p) {
-  __shared__ double red_d[kTsThreads / kWave];
-  __shared__ uint64_t red_k[kTsThreads / kWave];
-  __shared__ double lse_s;
-  __shared__ uint64_t win[kTsKMax];
+// One 1024-thread workgroup per request; the four waves of group g merge
+// parents g, g + 4, ...: a pass over the tiles' maxima, then one over their
+// exp sums (float32 terms relative to the parent's maximum, float64 total)
+// and their top-KK lists; groups combine through LDS.
+constexpr int kTsMergeThreads = 1024;
+constexpr int kTsMergeGroups = 4;
+constexpr int kTsGroupWaves = kTsMergeThreads / kWave / kTsMergeGroups;
+
+template <int KK>
+__global__ __launch_bounds__(kTsMergeThreads) void ts_merge_kernel(TsMergeParams p) {
   __shared__ int32_t ch_tok[kTsFMax * kTsKMax];
   __shared__ double ch_score[kTsFMax * kTsKMax];
   __shared__ uint64_t ch_key[kTsFMax * kTsKMax];
   __shared__ int32_t ch_cand[kTsFMax * kTsKMax];
+  __shared__ double red_d[kTsMergeGroups][kTsGroupWaves];
+  __shared__ uint64_t red_k[kTsMergeGroups][kTsGroupWaves][KK];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int g = w / kTsGroupWaves, gw = w - g * kTsGroupWaves;
+  const int gt = gw * kWave + lane;  // thread index within the group
+  constexpr int GT = kTsGroupWaves * kWave;
   const int64_t b = blockIdx.x;
   TsState& st = p.st;
   const int par = p.d & 1;
@@ -319,77 +331,110 @@ __global__ __launch_bounds__(kTsThreads) void ts_merge_kernel(TsMergeParams p) {
   const int K = p.k;
   const int base = st.ccount[b];
   const int shift = 4 * (kTsDMax - 1 - p.d);  // this depth's digit
-  for (int i = 0; i < nf; ++i) {
-    const int m = (int)b * p.Fd + i;
-    // log-sum-exp over the partials, float64
-    double mx = -INFINITY;
-    for (int t = tid; t < p.nvt; t += kTsThreads) {
-      const double x = p.pmax[(size_t)t * p.Mtot + m];
-      mx = x > mx ? x : mx;
-    }
+  const int rounds = (nf + kTsMergeGroups - 1) / kTsMergeGroups;
+  for (int rd = 0; rd < rounds; ++rd) {  // uniform trip count: every group reaches each barrier
+    const int i = rd * kTsMergeGroups + g;
+    const bool act = i < nf;
+    const int m = (int)b * p.Fd + (act ? i : 0);
+    // pass 1: the parent's maximum z
+    float mx = -INFINITY;
+    for (int t = gt; t < p.nvt; t += GT) mx = fmaxf(mx, p.pmax[(size_t)t * p.Mtot + m]);
     mx = wave_max(mx);
-    if (lane == 0) red_d[w] = mx;
+    if (lane == 0) red_d[g][gw] = mx;
     __syncthreads();
-    double M = red_d[0];
-    for (int q = 1; q < kTsThreads / kWave; ++q) M = red_d[q] > M ? red_d[q] : M;
-    __syncthreads();
-    double s = 0.0;
-    for (int t = tid; t < p.nvt; t += kTsThreads) {
-      const size_t o = (size_t)t * p.Mtot + m;
-      const double x = p.pmax[o];
-      if (x != -INFINITY) s += (double)p.psum[o] * exp(x - M);
-    }
-    s = wave_sum(s);
-    if (lane == 0) red_d[w] = s;
-    __syncthreads();
-    if (tid == 0) {
-      double tot = 0.0;
-      for (int q = 0; q < kTsThreads / kWave; ++q) tot += red_d[q];
-      lse_s = M + log(tot);
-    }
-    // top-k over the partial lists: k rounds of a block-wide max of keys
-    // (value key << 32 | ~id); each thread offers its best key not yet taken
-    float tv[kTsKMax];
-    int ti[kTsKMax];
+    float M = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kTsKMax; ++j) {
+    for (int q = 0; q < kTsGroupWaves; ++q) M = fmaxf(M, (float)red_d[g][q]);
+    __syncthreads();
+    // pass 2: exp sums and top-KK lists
+    double s = 0.0;
+    float tv[KK];
+    int ti[KK];
+#pragma unroll
+    for (int j = 0; j < KK; ++j) {
       tv[j] = -INFINITY;
       ti[j] = 0x7FFFFFFF;
     }
-    for (int t = tid; t < p.nvt; t += kTsThreads) {
-      const size_t o = ((size_t)t * p.Mtot + m) * kTsKMax;
+    for (int t = gt; t < p.nvt; t += GT) {
+      const size_t o = (size_t)t * p.Mtot + m;
+      const float x = p.pmax[o];
+      const float y = p.psum[o];
+      float pv[KK];
+      int pi[KK];
 #pragma unroll
-      for (int j = 0; j < kTsKMax; ++j) {
-        const int id = p.pid[o + j];
-        if (j < K && id != 0x7FFFFFFF) ts_insert(tv, ti, K, p.pval[o + j], id);
+      for (int j = 0; j < KK; ++j) {
+        pv[j] = p.pval[o * kTsKMax + j];
+        pi[j] = p.pid[o * kTsKMax + j];
+      }
+      if (x != -INFINITY) s += (double)(y * __expf(x - M));
+#pragma unroll
+      for (int j = 0; j < KK; ++j) {
+        if (j < K && pi[j] != 0x7FFFFFFF) {
+          // (val, id) into the sorted list, branch-free
+          const float xv = pv[j];
+          const int id = pi[j];
+          bool bt[KK];
+#pragma unroll
+          for (int q = 0; q < KK; ++q) bt[q] = q < K && (xv > tv[q] || (xv == tv[q] && id < ti[q]));
+#pragma unroll
+          for (int q = KK - 1; q >= 0; --q) {
+            const bool sh = q > 0 && bt[q > 0 ? q - 1 : 0];
+            const float v1 = q > 0 ? tv[q > 0 ? q - 1 : 0] : xv;
+            const int i1 = q > 0 ? ti[q > 0 ? q - 1 : 0] : id;
+            tv[q] = sh ? v1 : (bt[q] ? xv : tv[q]);
+            ti[q] = sh ? i1 : (bt[q] ? id : ti[q]);
+          }
+        }
       }
     }
+    s = wave_sum(s);
+    // the group's top-KK: KK rounds of a max over each lane's best untaken key
     int head = 0;
-    for (int r = 0; r < K; ++r) {
+    uint64_t wbest[KK];
+#pragma unroll
+    for (int r = 0; r < KK; ++r) {
       uint64_t mine = 0;
 #pragma unroll
-      for (int j = 0; j < kTsKMax; ++j)
+      for (int j = 0; j < KK; ++j)
         if (j == head && ti[j] != 0x7FFFFFFF) mine = ts_zkey(tv[j], ti[j]);
-      const uint64_t wmax = wave_max(mine);
-      __syncthreads();
-      if (lane == 0) red_k[w] = wmax;
-      __syncthreads();
-      uint64_t best = red_k[0];
-      for (int q = 1; q < kTsThreads / kWave; ++q) best = red_k[q] > best ? red_k[q] : best;
-      if (mine == best && best != 0) ++head;  // keys are unique: one owner
-      if (tid == 0) win[r] = best;
+      const uint64_t best = wave_max(mine);
+      if (mine == best && best != 0) ++head;
+      wbest[r] = best;
+    }
+    if (lane == 0) {
+      red_d[g][gw] = s;
+#pragma unroll
+      for (int r = 0; r < KK; ++r) red_k[g][gw][r] = wbest[r];
     }
     __syncthreads();
-    if (tid < K) {
-      const uint64_t kk = win[tid];
-      const int c = i * K + tid;
+    if (act && gw == 0 && lane < K) {
+      // lane r picks the r-th best of the group's waves' lists (keys unique)
+      uint64_t all[kTsGroupWaves * KK];
+#pragma unroll
+      for (int q = 0; q < kTsGroupWaves; ++q)
+#pragma unroll
+        for (int r = 0; r < KK; ++r) all[q * KK + r] = red_k[g][q][r];
+      double tot = 0.0;
+#pragma unroll
+      for (int q = 0; q < kTsGroupWaves; ++q) tot += red_d[g][q];
+      const double lse = (double)M + log(tot);
+      uint64_t pick = 0;
+      for (int r = 0; r <= lane; ++r) {
+        uint64_t bst = 0;
+#pragma unroll
+        for (int q = 0; q < kTsGroupWaves * KK; ++q) {
+          const uint64_t x = all[q];
+          if (x > bst && (r == 0 || x < pick)) bst = x;
+        }
+        pick = bst;
+      }
       const int pc = st.pcand[par][m];
       const double pscore = pc < 0 ? 0.0 : st.cscore[b * st.cmax + pc];
       const uint64_t pkey = pc < 0 ? 0ull : st.ckey[b * st.cmax + pc];
-      const float zval = key_value((uint32_t)(kk >> 32));
-      ch_tok[c] = (int32_t)(0xFFFFFFFFu - (uint32_t)kk);
-      ch_score[c] = pscore + ((double)zval - lse_s);
-      ch_key[c] = pkey | ((uint64_t)(tid + 1) << shift);
+      const int c = i * K + lane;
+      ch_tok[c] = (int32_t)(0xFFFFFFFFu - (uint32_t)pick);
+      ch_score[c] = pscore + ((double)key_value((uint32_t)(pick >> 32)) - lse);
+      ch_key[c] = pkey | ((uint64_t)(lane + 1) << shift);
       ch_cand[c] = pc;
     }
     __syncthreads();
