@@ -29,8 +29,13 @@
 //    the row's table and log-sum-exp (float64).
 //  stage1_row_kernel (many rows): one workgroup walks all chunks of its row
 //    with double-buffered register loads (chunk i+1 in flight while chunk i
-//    is processed), raises the row threshold chunk by chunk and finishes the
-//    row itself in the same way: no records, no second launch.
+//    is processed), raises the row threshold on a schedule of chunks, keeps
+//    whole 16-byte vectors that reach it in LDS (compacting a wave's region
+//    against the current threshold when it would overflow) and finishes the
+//    row itself: the kept vectors' elements at or above the final threshold
+//    become candidates, ranked for bf16 rows by a histogram over their value
+//    codes (ties by id inside a code), else by counting larger keys. No
+//    records, no second launch.
 #pragma once
 
 #include "common.hpp"
@@ -520,6 +525,14 @@ __global__ __launch_bounds__(kWave* kMergeWaves) void stage1_merge_kernel(Stage1
 constexpr int kVecCap = 448;          // kept vectors per wave
 constexpr int kKeyCap = 2 * kVecCap;  // candidate keys per wave (in the wave's vector region)
 constexpr int kListRegs = 2;          // list of 64 * kListRegs group maxima per wave (>= ceil(K/4))
+// Claim schedule: chunks 0 .. kClaimDense-1 update the wave's claim, later
+// chunks only every kClaimEvery-th; in between, each lane folds its group
+// maxima into a pending maximum per group slot (the maximum of several groups
+// is still one element, so the certificate stays valid, only looser). The
+// looser threshold keeps more vectors; a wave whose region would overflow
+// first compacts it against its current threshold (compact_kept).
+constexpr int kClaimDense = 4;
+constexpr int kClaimEvery = 3;
 
 // 37.1 KiB: four workgroups fit in one CU's 160 KiB.
 struct RowSmem {
@@ -531,9 +544,17 @@ struct RowSmem {
   uint32_t lst[kS1Waves][kWave * kListRegs];  // list compaction
   uint32_t claim[kS1Waves];
   uint32_t red_u[kS1Waves];
+  uint32_t red_k[kS1Waves];
+  int scan[kS1Waves];
   double red_d[kS1Waves];
   int wn[kS1Waves];
 };
+
+// Bins of the bf16 rank histogram (one per bf16 value between the row's
+// threshold and its maximum) and candidates per thread it handles.
+constexpr int kHistBins = 1024;
+constexpr int kHistCPT = 4;
+static_assert(kHistBins <= kS1Waves * kVecCap, "the histogram lives in vpos");
 
 __device__ __forceinline__ float fmax3(float a, float b, float c) {
   float r;
@@ -667,6 +688,40 @@ __device__ __forceinline__ uint32_t claim_update(uint32_t (&lst)[kListRegs],
   return T;
 }
 
+// Keep, in order, only the wave's kept vectors whose maximum reaches tf
+// (wave-local; a write never passes the vectors still to be read). Returns
+// the new count.
+template <int DT>
+__device__ __forceinline__ int compact_kept(RowSmem& sm, int w, int n, float tf) {
+  constexpr int EPV = DT == 0 ? 8 : 4;
+  const int lane = threadIdx.x & 63;
+  int kept = 0;
+  for (int b = 0; b < n; b += kWave) {
+    const int i = b + lane;
+    const bool valid = i < n;
+    const v4u32 v = valid ? sm.vec[w][i] : v4u32{0u, 0u, 0u, 0u};
+    const uint32_t ps = valid ? sm.vpos[w][i] : 0u;
+    float m = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) m = fmaxf(m, __uint_as_float(elem_bits<DT>(v, e)));
+    const bool keep = valid && m >= tf;
+    const uint64_t M = __ballot(keep);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (keep) {
+      const int pos = kept + lanes_below(M);
+      sm.vec[w][pos] = v;
+      sm.vpos[w][pos] = ps;
+    }
+    kept += __popcll(M);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  return kept;
+}
+
 struct RowRun {
   float m;       // running maximum of the thread's elements
   float mc;      // integer offset ceil(m * c) of s (-inf while m = -inf)
@@ -674,13 +729,19 @@ struct RowRun {
   uint32_t thr;  // running threshold (value key; 0 = none yet)
   int wn;        // vectors kept by this wave (uniform)
   uint32_t lst[kListRegs];
+  uint32_t pend[4];  // group maxima not yet in the list (0 = none)
 };
+
+__device__ __forceinline__ bool claim_due(int c) {
+  return c < kClaimDense || (c - kClaimDense) % kClaimEvery == kClaimEvery - 1;
+}
 
 template <int DT, int NV, int GS, bool FIRST>
 __device__ __forceinline__ void row_chunk(v4u32 (&raw)[NV], RowSmem& sm, int64_t c0, int64_t nvec,
-                                          int need, int lregs, RowRun& st) {
+                                          int need, int lregs, RowRun& st, bool upd) {
   constexpr int EPV = DT == 0 ? 8 : 4;
   constexpr int G = NV / GS;
+  static_assert(G <= 4, "pending slots");
   constexpr uint32_t NEG_INF_DW = DT == 0 ? 0xFF80FF80u : 0xFF800000u;
   static_assert(GS == 4, "group = 4 vectors");
   const int tid = threadIdx.x, w = tid >> 6;
@@ -711,9 +772,19 @@ __device__ __forceinline__ void row_chunk(v4u32 (&raw)[NV], RowSmem& sm, int64_t
   }
 
   // claims
-  const uint32_t Tw = claim_update<DT, G>(st.lst, gk, need, lregs, &sm.lst[w][0]);
-  if ((tid & 63) == 0)
-    __hip_atomic_store(&sm.claim[w], Tw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (FIRST || upd) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      gk[g] = gk[g] > st.pend[g] ? gk[g] : st.pend[g];
+      st.pend[g] = 0;
+    }
+    const uint32_t Tw = claim_update<DT, G>(st.lst, gk, need, lregs, &sm.lst[w][0]);
+    if ((tid & 63) == 0)
+      __hip_atomic_store(&sm.claim[w], Tw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g) st.pend[g] = st.pend[g] > gk[g] ? st.pend[g] : gk[g];
+  }
   if (FIRST) __syncthreads();
   uint32_t t0 = 0xFFFFFFFFu;
 #pragma unroll
@@ -725,18 +796,28 @@ __device__ __forceinline__ void row_chunk(v4u32 (&raw)[NV], RowSmem& sm, int64_t
   // normaliser terms
   st.s += (double)exp_pass<DT, NV>(raw, st.m == -INFINITY ? 0.0f : st.mc);
 
-  // keep the vectors that reach the threshold
+  // keep the vectors that reach the threshold; if they would not fit, first
+  // drop the kept vectors that the (since raised) threshold excludes
+  uint64_t KM[NV];
+  int add = 0;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const bool keep = vmax[j] >= tf;
-    const uint64_t M = __ballot(keep);
-    if (M) {
-      const int pos = st.wn + lanes_below(M);
-      if (keep && pos < kVecCap) {
-        sm.vec[w][pos] = raw[j];
-        sm.vpos[w][pos] = (uint32_t)c0 + (uint32_t)((j * kS1Threads + tid) * EPV);
+    KM[j] = __ballot(vmax[j] >= tf);
+    add += __popcll(KM[j]);
+  }
+  if (add) {
+    if (st.wn + add > kVecCap && st.wn <= kVecCap) st.wn = compact_kept<DT>(sm, w, st.wn, tf);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const uint64_t M = KM[j];
+      if (M) {
+        const int pos = st.wn + lanes_below(M);
+        if (((M >> (tid & 63)) & 1) && pos < kVecCap) {
+          sm.vec[w][pos] = raw[j];
+          sm.vpos[w][pos] = (uint32_t)c0 + (uint32_t)((j * kS1Threads + tid) * EPV);
+        }
+        st.wn += __popcll(M);
       }
-      st.wn += __popcll(M);
     }
   }
 }
@@ -776,6 +857,11 @@ __device__ __noinline__ int exact_row_select(const char* rowp, int64_t V, int K,
   return sm.wn[0];
 }
 
+// Start of wave 1, 2, 3's candidates in the flat candidate order.
+__device__ __forceinline__ int b1_of(const int (&k)[kS1Waves]) { return k[0]; }
+__device__ __forceinline__ int b2_of(const int (&k)[kS1Waves]) { return k[0] + k[1]; }
+__device__ __forceinline__ int b3_of(const int (&k)[kS1Waves]) { return k[0] + k[1] + k[2]; }
+
 template <int DT, int NV, int GS>
 __global__ __launch_bounds__(kS1Threads, 4) void stage1_row_kernel(Stage1Params p) {
   constexpr int EPV = DT == 0 ? 8 : 4;
@@ -801,25 +887,31 @@ __global__ __launch_bounds__(kS1Threads, 4) void stage1_row_kernel(Stage1Params 
   st.wn = 0;
 #pragma unroll
   for (int r = 0; r < kListRegs; ++r) st.lst[r] = 0;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) st.pend[g] = 0;
 
   v4u32 A[NV], Bf[NV];
   load_chunk_buf<NV>(A, rowp, 0, rowbytes);
   load_chunk_buf<NV>(Bf, rowp, CB, rowbytes);
-  row_chunk<DT, NV, GS, true>(A, sm, 0, nvec_of(0), need, lregs, st);
+  row_chunk<DT, NV, GS, true>(A, sm, 0, nvec_of(0), need, lregs, st, true);
   load_chunk_buf<NV>(A, rowp, 2 * CB, rowbytes);
   for (int c = 1; c < S; c += 2) {
-    row_chunk<DT, NV, GS, false>(Bf, sm, (int64_t)c * CH, nvec_of(c), need, lregs, st);
+    row_chunk<DT, NV, GS, false>(Bf, sm, (int64_t)c * CH, nvec_of(c), need, lregs, st,
+                                 claim_due(c));
     load_chunk_buf<NV>(Bf, rowp, (int64_t)(c + 2) * CB, rowbytes);
     if (c + 1 < S)
-      row_chunk<DT, NV, GS, false>(A, sm, (int64_t)(c + 1) * CH, nvec_of(c + 1), need, lregs, st);
+      row_chunk<DT, NV, GS, false>(A, sm, (int64_t)(c + 1) * CH, nvec_of(c + 1), need, lregs, st,
+                                   claim_due(c + 1));
     load_chunk_buf<NV>(A, rowp, (int64_t)(c + 3) * CB, rowbytes);
   }
 
   // row normaliser: per thread s * 2^(mc + m*(log2 e - c)), float64
   const double off = st.m == -INFINITY ? -INFINITY : (double)st.mc + (double)st.m * kLog2eErr;
   const double off_w = wave_max(off);
+  const uint32_t top_w = wave_max(st.m == -INFINITY ? 0u : order_key(__float_as_uint(st.m)));
   if (lane == 0) {
     sm.red_d[w] = off_w;
+    sm.red_k[w] = top_w;
     sm.wn[w] = st.wn;
   }
   __syncthreads();  // claims, kept vectors and counts are final
@@ -827,11 +919,12 @@ __global__ __launch_bounds__(kS1Threads, 4) void stage1_row_kernel(Stage1Params 
 #pragma unroll
   for (int i = 1; i < kS1Waves; ++i) OFF = OFF > sm.red_d[i] ? OFF : sm.red_d[i];
   const double part_w = wave_sum(st.m == -INFINITY ? 0.0 : st.s * exp2(off - OFF));
-  uint32_t T = 0xFFFFFFFFu;
+  uint32_t T = 0xFFFFFFFFu, TOP = 0;
   int ovf = 0;
 #pragma unroll
   for (int i = 0; i < kS1Waves; ++i) {
     T = min(T, sm.claim[i]);
+    TOP = max(TOP, sm.red_k[i]);
     ovf |= sm.wn[i] > kVecCap;
   }
   __syncthreads();
@@ -856,22 +949,41 @@ __global__ __launch_bounds__(kS1Threads, 4) void stage1_row_kernel(Stage1Params 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // per lane: which elements of its vectors reach the threshold; then one
+    // wave prefix of the counts places them
+    uint32_t km[VR];
+    int cnt = 0;
 #pragma unroll
     for (int r = 0; r < VR; ++r) {
+      uint32_t m = 0;
       if (r * kWave < nvk) {
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          const uint32_t bits = elem_bits<DT>(kv[r], e);
-          const bool keep = (r * kWave + lane) < nvk && __uint_as_float(bits) >= tf;
-          const uint64_t M = __ballot(keep);
-          if (M) {
-            const int pos = kn + lanes_below(M);
-            if (keep && pos < kKeyCap) sm.keys[w][pos] = cand_key(order_key(bits), kp[r] + e);
-            kn += __popcll(M);
-          }
-        }
+        for (int e = 0; e < EPV; ++e)
+          m |= (__uint_as_float(elem_bits<DT>(kv[r], e)) >= tf ? 1u : 0u) << e;
+        m = (r * kWave + lane) < nvk ? m : 0u;
+      }
+      km[r] = m;
+      cnt += __popc(m);
+    }
+    int pos = 0, tot = 0;
+#pragma unroll
+    for (int bit = 0; bit < 6; ++bit) {  // cnt <= 7 * 8 < 64
+      const uint64_t M = __ballot((cnt >> bit) & 1);
+      pos += lanes_below(M) << bit;
+      tot += __popcll(M) << bit;
+    }
+#pragma unroll
+    for (int r = 0; r < VR; ++r) {
+      uint32_t m = km[r];
+      while (m) {
+        const int e = __builtin_ctz(m);
+        m &= m - 1;
+        if (pos < kKeyCap)
+          sm.keys[w][pos] = cand_key(order_key(elem_bits<DT>(kv[r], e)), kp[r] + e);
+        ++pos;
       }
     }
+    kn = tot;
   }
   if (lane == 0) sm.wn[w] = kn;
   __syncthreads();
@@ -903,6 +1015,49 @@ __global__ __launch_bounds__(kS1Threads, 4) void stage1_row_kernel(Stage1Params 
       const uint64_t k = a[i];
       oid[i] = (int32_t)cand_id(k);
       oval[i] = key_value(cand_vkey(k));
+    }
+    return;
+  }
+  // >= K distinct candidates. bf16 rows: a histogram over the value codes
+  // between the threshold and the row maximum gives each candidate the number
+  // of larger values (an exclusive scan), and only equal values are compared
+  // one by one (by id). Otherwise each rank is the number of larger keys.
+  const int R = (T != 0 && TOP >= T) ? (int)((TOP - T) >> 16) + 1 : kHistBins + 1;
+  if (DT == 0 && ntot <= kHistCPT * kS1Threads && R <= kHistBins) {
+    int* hist = (int*)&sm.vpos[0][0];  // the kept vectors' positions are dead
+    for (int i = tid; i < R; i += kS1Threads) hist[i] = 0;
+    uint64_t mk[kHistCPT];
+    int bin[kHistCPT], slot[kHistCPT];
+#pragma unroll
+    for (int c = 0; c < kHistCPT; ++c) {
+      const int i = tid + c * kS1Threads;
+      const int ww = (i >= b1_of(kcnt)) + (i >= b2_of(kcnt)) + (i >= b3_of(kcnt));
+      const int off0 = ww == 0 ? 0 : ww == 1 ? b1_of(kcnt) : ww == 2 ? b2_of(kcnt) : b3_of(kcnt);
+      mk[c] = i < ntot ? sm.keys[ww][i - off0] : 0ull;
+      bin[c] = (int)((TOP - cand_vkey(mk[c])) >> 16);
+    }
+    __syncthreads();  // every source key is in registers; the histogram is zero
+#pragma unroll
+    for (int c = 0; c < kHistCPT; ++c)
+      if (tid + c * kS1Threads < ntot) slot[c] = atomicAdd(&hist[bin[c]], 1);
+    __syncthreads();
+    block_excl_scan<kS1Threads>(hist, R, sm.scan);  // hist[b]: candidates in bins < b
+    uint64_t* sorted = &sm.keys[0][0];
+#pragma unroll
+    for (int c = 0; c < kHistCPT; ++c)
+      if (tid + c * kS1Threads < ntot) sorted[hist[bin[c]] + slot[c]] = mk[c];
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < kHistCPT; ++c) {
+      if (tid + c * kS1Threads < ntot) {
+        const int lo = hist[bin[c]], hi = bin[c] + 1 < R ? hist[bin[c] + 1] : ntot;
+        int rank = lo;
+        for (int q = lo; q < hi; ++q) rank += sorted[q] > mk[c] ? 1 : 0;
+        if (rank < K) {
+          oid[rank] = (int32_t)cand_id(mk[c]);
+          oval[rank] = key_value(cand_vkey(mk[c]));
+        }
+      }
     }
     return;
   }

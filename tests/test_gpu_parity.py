@@ -65,6 +65,15 @@ ROW_CASES = [
     (6, 3000, 1, BF16, "gauss"),
     (1, 7, 7, F32, "ints"),             # K == V
     (40, 151936, 128, BF16, "gauss"),
+    # >= 512 rows of 16-byte multiples: one workgroup per row
+    (512, 8192, 128, BF16, "gauss"),
+    (520, 6000, 64, BF16, "straddle"),
+    (512, 4096, 256, BF16, "neg"),
+    (600, 20000, 100, BF16, "ints"),
+    (512, 2048, 128, BF16, "const"),   # more tied vectors than fit: exact path
+    (512, 4096, 128, F32, "gauss"),
+    (512, 151936, 256, BF16, "straddle"),
+    (512, 151936, 256, BF16, "trend"),
 ]
 
 
@@ -72,6 +81,15 @@ def _rows(rows, V, dt, kind, seed=0):
     rng = np.random.default_rng(seed)
     if kind == "gauss":
         x = (rng.uniform(0.5, 8, (rows, 1)) * rng.standard_normal((rows, V))).astype(np.float32)
+    elif kind in ("straddle", "neg"):
+        # the top K values cross zero (straddle) or are all negative (neg)
+        sig = rng.uniform(0.5, 8, (rows, 1))
+        shift = 3.1 if kind == "straddle" else 40.0
+        x = (sig * (rng.standard_normal((rows, V)) - shift)).astype(np.float32)
+    elif kind == "trend":
+        # rising along the row: early kept vectors go stale and get compacted
+        sig = rng.uniform(0.5, 8, (rows, 1))
+        x = (sig * (rng.standard_normal((rows, V)) + 8.0 * np.arange(V) / V)).astype(np.float32)
     elif kind == "ints":
         x = rng.integers(-3, 4, (rows, V)).astype(np.float32)
         x[:, :5] = -0.0
