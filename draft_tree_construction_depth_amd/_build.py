@@ -15,6 +15,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # No packed-FP32 instructions anywhere in the device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # A wave's atomic add of per-lane amounts to one address: one DPP scan and
+    # one atomic instead of a scalar loop over the active lanes.
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=DPP",
 ]
 
 

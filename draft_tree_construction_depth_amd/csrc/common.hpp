@@ -63,6 +63,42 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
+// Inclusive scan of one int per lane over the 64 lanes, by DPP: shifts by
+// 1, 2, 4, 8 inside each row of 16 lanes, then row 0's last lane added to
+// rows 1 and 3 and lane 31 to rows 2 and 3. Every lane of the wave must be
+// active.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+// Exclusive scan of one int per thread over the block (every thread calls
+// it); total gets the block sum. wsum: NT/64 ints of LDS, 16-byte aligned.
+// One barrier; a later call reusing wsum needs a barrier in between.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan_reg(int x, int* wsum, int& total) {
+  constexpr int NW = NT / kWave;
+  static_assert(NW % 4 == 0, "int4 reads of the wave totals");
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int inc = wave_incl_scan(x);
+  if (lane == kWave - 1) wsum[w] = inc;
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; i += 4) {
+    const int4 t = *(const int4*)&wsum[i];
+    pre += (i < w ? t.x : 0) + (i + 1 < w ? t.y : 0) + (i + 2 < w ? t.z : 0) + (i + 3 < w ? t.w : 0);
+    tot += t.x + t.y + t.z + t.w;
+  }
+  total = tot;
+  return pre + inc - x;
+}
+
 // In-place exclusive scan of a[0..n) (LDS) by NT threads; returns the total.
 // wsum needs NT/64 ints of LDS. Ends with a barrier.
 template <int NT>
@@ -73,12 +109,7 @@ __device__ int block_excl_scan(int* a, int n, int* wsum) {
   const int b0 = min(tid * seg, n), b1 = min(b0 + seg, n);
   int s = 0;
   for (int i = b0; i < b1; ++i) s += a[i];
-  int x = s;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(s);
   if (lane == kWave - 1) wsum[w] = x;
   __syncthreads();
   int pre = 0, total = 0;

@@ -16,10 +16,9 @@
 // workgroup per request (four waves per SIMD: a lone wave issues only about
 // a quarter of the SIMD's vector rate, and every step here is short):
 //  1. Threshold. tau = the B-th best score among the L*K prefixes that
-//     deviate from the all-rank-0 spine only in their last position: exact,
-//     by a merge tree over the rows (each row's scores are sorted); for
-//     shapes whose first merge level would not fit, to 8^-8 of their range
-//     by an 8-ary search whose counts are ballots.
+//     deviate from the all-rank-0 spine only in their last position, exact:
+//     a histogram of those scores above a lower bound, one scan for the bin
+//     holding the B-th, exact ranking inside that bin.
 //     These are B valid prefixes, so every one of the true top B scores at
 //     least tau.
 //  2. Enumerate E = {prefixes with score >= tau} by "chains": a chain is an
@@ -27,7 +26,7 @@
 //     extensions, which one thread walks in registers. Generation g holds
 //     the chains with g nonzero ranks; a generation's deviating children
 //     are counted by binary search over the sorted row, allocated by a block
-//     scan and walked in parallel. Drafter trees have <= 3 deviations per
+//     scan (DPP inside waves) and walked in parallel. Drafter trees have <= 3 deviations per
 //     path in practice, so this needs a few block-synchronous steps instead
 //     of one per tree level.
 //  3. Histogram E's scores into bins over [tau, best]; the first bins that
@@ -112,13 +111,11 @@ struct SelectSmem {
     } mt;
   } u;
   int opar[kMaxB];  // parent node number of output node j+1
-  int wsum[kSelWaves];
-  int redI[2][kSelWaves];
-  int cnt8[2][8][kSelWaves];  // [parity][pivot][wave]
+  alignas(16) int wsum[kSelWaves];
+  int kexc;  // entries before the threshold's bin
   int n2;
   int kcut;
   int hist[kSelThreads];
-  double redD[kSelWaves];
   double tau;
   int nE;
   int ovf;
@@ -134,54 +131,6 @@ __device__ __forceinline__ void lex_set_digit(uint64_t& hi, uint64_t& lo, int d,
   const uint64_t l = s >= 64 ? 0ull : v << s;
   hi |= h;
   lo |= l;
-}
-
-// Block sum of per-wave (uniform) counts; alternating buffers need one barrier.
-__device__ __forceinline__ int sel_block_sum(int v, SelectSmem& sm, int& parity) {
-  static_assert(kSelWaves % 4 == 0, "16-byte reads");
-  if ((threadIdx.x & 63) == 0) sm.redI[parity][threadIdx.x >> 6] = v;
-  __syncthreads();
-  const int4* r = (const int4*)sm.redI[parity];
-  int t = 0;
-#pragma unroll
-  for (int i = 0; i < kSelWaves / 4; ++i) {
-    const int4 q = r[i];
-    t += q.x + q.y + q.z + q.w;
-  }
-  parity ^= 1;
-  return t;
-}
-
-__device__ __forceinline__ double sel_block_min(double v, SelectSmem& sm) {
-  v = wave_min(v);
-  if ((threadIdx.x & 63) == 0) sm.redD[threadIdx.x >> 6] = v;
-  __syncthreads();
-  const double2* r = (const double2*)sm.redD;
-  double m = INFINITY;
-#pragma unroll
-  for (int i = 0; i < kSelWaves / 2; ++i) {
-    const double2 q = r[i];
-    m = q.x < m ? q.x : m;
-    m = q.y < m ? q.y : m;
-  }
-  __syncthreads();
-  return m;
-}
-
-__device__ __forceinline__ double sel_block_max(double v, SelectSmem& sm) {
-  v = wave_max(v);
-  if ((threadIdx.x & 63) == 0) sm.redD[threadIdx.x >> 6] = v;
-  __syncthreads();
-  const double2* r = (const double2*)sm.redD;
-  double m = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kSelWaves / 2; ++i) {
-    const double2 q = r[i];
-    m = q.x > m ? q.x : m;
-    m = q.y > m ? q.y : m;
-  }
-  __syncthreads();
-  return m;
 }
 
 // e1 strictly before e2 in the output order (PAD = 0xFFFF is last).
@@ -284,133 +233,85 @@ __device__ void heap_fallback(const SelectParams& p, SelectSmem& sm, int64_t b) 
 }
 
 // ---------------------------------------------------------------------------
-// Largest lo (to 8^-8 of the value range, from below) with >= B of the
-// block's scores (NS per thread, -inf = none) at or above it: an 8-ary
-// search, seven pivots and one barrier per step; lane q sums pivot q's
-// per-wave counts.
-template <int NS>
-__device__ __forceinline__ double sel_kth(const double (&sc)[NS], double lo_l, double hi_l, int B,
-                          SelectSmem& sm, int& parity) {
-  auto count_ge = [&](double t) -> int {
-    int c = 0;
-#pragma unroll
-    for (int i = 0; i < NS; ++i) c += __popcll(__ballot(sc[i] >= t));
-    return c;
-  };
-  double lo = sel_block_min(lo_l, sm), hi = sel_block_max(hi_l, sm);
-  if (sel_block_sum(count_ge(hi), sm, parity) >= B) return hi;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int it = 0; it < 8; ++it) {
-    const double step = (hi - lo) * 0.125;
-    if (!(step > 0.0)) break;
-    int cq = 0;
-#pragma unroll
-    for (int q = 1; q < 8; ++q) {
-      const int c = count_ge(lo + step * q);
-      if (lane == q) cq = c;
-    }
-    if (lane >= 1 && lane < 8) sm.cnt8[parity][lane][w] = cq;
-    __syncthreads();
-    int tot = 0;
-    if (lane >= 1 && lane < 8) {
-      const int4* r = (const int4*)sm.cnt8[parity][lane];
-#pragma unroll
-      for (int i = 0; i < kSelWaves / 4; ++i) {
-        const int4 q = r[i];
-        tot += q.x + q.y + q.z + q.w;
-      }
-    }
-    parity ^= 1;
-    // counts fall with the pivot: the last pivot with >= B becomes lo
-    const uint64_t ok = __ballot(lane >= 1 && lane < 8 && tot >= B);
-    const int best = ok ? 63 - __builtin_clzll(ok) : 0;
-    const double nlo = lo + step * best;
-    const double nhi = best == 7 ? hi : lo + step * (best + 1);
-    lo = nlo;
-    hi = nhi;
-  }
-  return lo;
-}
-
-// Exact B-th best one-deviation score by a merge tree. Row d's scores
-// s_d(r) = min(sig_d, P0_d + v_d[r] - Z_d) do not increase with r, so the
-// rows are sorted lists; each level merges pairs of lists (merge-path search
-// per output position) and keeps the best B of each merge. ceil(log2 L)
-// levels, one barrier each. Requires L * K >= B and a first level of at
-// most kMergeCap entries.
-__device__ double sel_tau_merge(SelectSmem& sm, int L, int K, int B) {
-  auto onedev = [&](int d, int r) -> double {
-    const double raw = (sm.P0[d] + (double)sm.v[d * K + r]) - sm.Z[d];
+// Exact B-th best one-deviation score (requires L * K >= B). Row d's scores
+// s_d(r) = min(sig_d, P0_d + v_d[r] - Z_d) do not increase with r. Lower
+// bound mn: the q-th score of every row, q = min(ceil(B / L), K), leaves
+// >= B scores at or above the smallest of them. The scores in [mn, best]
+// fall into kSelThreads bins (index monotone in the score, equal scores share
+// a bin); one scan finds the bin holding the B-th, whose few members are
+// ranked exactly. Members beyond kMergeCap (flat rows) return mn instead, a
+// valid lower bound.
+__device__ double sel_tau_hist(SelectSmem& sm, int L, int K, int B) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int LK = L * K;
+  auto onedev = [&](int i) -> double {
+    const int d = i / K;
+    const double raw = (sm.P0[d] + (double)sm.v[i]) - sm.Z[d];
     return raw > sm.sig[d] ? sm.sig[d] : raw;
   };
-  if (L == 1) return onedev(0, B - 1);
-  double* src = sm.u.mt.a;
-  double* dst = sm.u.mt.b;
-  int m = L, len = K;  // m lists, each of length len except possibly the last
-  int last = K;        // length of the last list
-  bool rows = true;
-  while (m > 1) {
-    const int mo = (m + 1) >> 1;
-    const int lo_len = len + len < B ? len + len : B;                // merged pair
-    const int last_pair = (m & 1) ? last : (len + last < B ? len + last : B);
-    const int total = (mo - 1) * lo_len + last_pair;
-    for (int o = threadIdx.x; o < total; o += kSelThreads) {
-      const int i = o / lo_len, k = o - i * lo_len;
-      const int ia = 2 * i, ib = 2 * i + 1;
-      const int nA = ia == m - 1 ? last : len;
-      const int nB = ib < m ? (ib == m - 1 ? last : len) : 0;
-      auto A = [&](int x) -> double { return rows ? onedev(ia, x) : src[ia * len + x]; };
-      auto Bv = [&](int x) -> double { return rows ? onedev(ib, x) : src[ib * len + x]; };
-      // a = elements of A among the best k+1
-      int lo = k + 1 - nB > 0 ? k + 1 - nB : 0, hi = k + 1 < nA ? k + 1 : nA;
-      while (lo < hi) {
-        const int a = (lo + hi + 1) >> 1, b = k + 1 - a;
-        if (b < nB && A(a - 1) < Bv(b)) hi = a - 1;  // too many from A
-        else lo = a;
-      }
-      // lo is the largest a whose last A element still beats B's next one
-      const int a = lo, b = k + 1 - a;
-      double out;
-      if (a == 0) out = Bv(b - 1);
-      else if (b == 0) out = A(a - 1);
-      else {
-        const double x = A(a - 1), y = Bv(b - 1);
-        out = x < y ? x : y;
-      }
-      dst[i * lo_len + k] = out;
-    }
-    __syncthreads();
-    double* t = src;
-    src = dst;
-    dst = t;
-    m = mo;
-    len = lo_len;
-    last = last_pair;
-    rows = false;
-  }
-  return src[B - 1];
-}
-
-// B-th best score among the one-deviation prefixes (NS per thread).
-template <int NS>
-__device__ __forceinline__ double sel_threshold(SelectSmem& sm, int L, int K, int B, int& parity) {
-  const int tid = threadIdx.x, LK = L * K;
-  double sc1[NS];
-  double lo_l = INFINITY, hi_l = -INFINITY;
+  const int q = (B + L - 1) / L < K ? (B + L - 1) / L : K;
+  sm.hist[tid] = 0;
+  if (w == 0) {
+    double x = lane < L ? onedev(lane * K + q - 1) : INFINITY;
 #pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const int c = tid + i * kSelThreads;
-    sc1[i] = -INFINITY;
-    if (c < LK) {
-      const int d = c / K + 1;
-      const double raw = (sm.P0[d - 1] + (double)sm.v[c]) - sm.Z[d - 1];
-      const double sc = raw > sm.sig[d - 1] ? sm.sig[d - 1] : raw;
-      sc1[i] = sc;
-      lo_l = sc < lo_l ? sc : lo_l;
-      hi_l = sc > hi_l ? sc : hi_l;
+    for (int o = 32; o > 0; o >>= 1) {
+      const double y = __shfl_xor(x, o);
+      x = y < x ? y : x;
+    }
+    if (lane == 0) {
+      sm.tau = x;
+      sm.n2 = 0;
     }
   }
-  return sel_kth<NS>(sc1, lo_l, hi_l, B, sm, parity);
+  __syncthreads();
+  const double mn = sm.tau, top = sm.sig[1];
+  const double span = top - mn;
+  const double scale = span > 0.0 ? (double)kSelThreads / span : 0.0;
+  auto bin_of = [&](double sc) -> int {
+    const double t = (top - sc) * scale;
+    return t >= (double)(kSelThreads - 1) ? kSelThreads - 1 : (t > 0.0 ? (int)t : 0);
+  };
+  for (int i = tid; i < LK; i += kSelThreads) {
+    const double sc = onedev(i);
+    if (sc >= mn) atomicAdd(&sm.hist[bin_of(sc)], 1);
+  }
+  __syncthreads();
+  const int h = sm.hist[tid];
+  const int x = wave_incl_scan(h);
+  if (lane == kWave - 1) sm.wsum[w] = x;
+  __syncthreads();
+  int pre = 0;
+  for (int i = 0; i < w; ++i) pre += sm.wsum[i];
+  const int inc = pre + x, exc = inc - h;
+  if (inc >= B && exc < B) {
+    sm.kcut = tid;
+    sm.kexc = exc;
+  }
+  __syncthreads();
+  const int kb = sm.kcut, t = B - 1 - sm.kexc;  // the B-th is member t of bin kb
+  double* mem = sm.u.mt.a;
+  for (int i = tid; i < LK; i += kSelThreads) {
+    const double sc = onedev(i);
+    if (sc >= mn && bin_of(sc) == kb) {
+      const int k = atomicAdd(&sm.n2, 1);
+      if (k < kMergeCap) mem[k] = sc;
+    }
+  }
+  __syncthreads();
+  const int m = sm.n2;
+  if (m > kMergeCap) return mn;
+  for (int k = tid; k < m; k += kSelThreads) {
+    const double v = mem[k];
+    int gt = 0, ge = 0;
+    for (int j = 0; j < m; ++j) {
+      const double u = mem[j];
+      gt += u > v ? 1 : 0;
+      ge += u >= v ? 1 : 0;
+    }
+    if (gt <= t && t < ge) sm.tau = v;  // every such member holds the same value
+  }
+  __syncthreads();
+  return sm.tau;
 }
 
 // Position in the output order (score desc, then lexicographic rank key asc;
@@ -475,7 +376,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   const int64_t b = blockIdx.x;
   const int L = p.L, K = p.K, B = p.B, LK = L * K, bpd = p.bpd;
   const float* vals = p.vals + (size_t)b * LK;
-  int parity = 0;
 
   for (int i = tid; i < LK; i += kSelThreads) sm.v[i] = vals[i];
   if (tid < L) sm.lse[tid] = p.lse[(size_t)b * L + tid];
@@ -501,19 +401,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
 
   // ---- 1. threshold from the one-deviation prefixes -------------------------
   double tau = -INFINITY;
-  if (LK >= B) {
-    const int lvl1 = ((L + 1) >> 1) * (2 * K < B ? 2 * K : B);
-    if (lvl1 <= kMergeCap) {
-      tau = sel_tau_merge(sm, L, K, B);
-    } else {
-      const int nslot = (LK + kSelThreads - 1) / kSelThreads;
-      static_assert(kMaxLK <= 8 * kSelThreads, "eight one-deviation prefixes per thread at most");
-      if (nslot <= 1) tau = sel_threshold<1>(sm, L, K, B, parity);
-      else if (nslot <= 2) tau = sel_threshold<2>(sm, L, K, B, parity);
-      else if (nslot <= 4) tau = sel_threshold<4>(sm, L, K, B, parity);
-      else tau = sel_threshold<8>(sm, L, K, B, parity);
-    }
-  }
+  if (LK >= B) tau = sel_tau_hist(sm, L, K, B);
 
   // ---- 2. enumerate E = {score >= tau} by chains ----------------------------
   int D0 = 0;
@@ -538,32 +426,44 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
       __syncthreads();
       break;
     }
-    for (int i = tid; i < np; i += kSelThreads) {
-      double S = 0.0;
-      int d = 0;
-      if (!(root && i == 0)) {
-        const int e = g0 + i - root;
-        S = en.eS[e];
-        d = en.eDep[e];
-      }
-      int c = 0;
-      if (d < L) {
-        // number of ranks r >= 1 of row d+1 whose child scores >= tau
-        const float* row = sm.v + d * K;
-        const double Zd = sm.Z[d];
-        int lo = 1, hi = K;  // first failing rank lies in [lo, hi]
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if ((S + (double)row[mid]) - Zd >= tau) lo = mid + 1;
-          else hi = mid;
+    // deviating children (rank >= 1) of each parent that reach tau, counted
+    // by binary search in the sorted row; parents per thread: 1, or 2 when
+    // np > kSelThreads (consecutive, so the offsets follow parent order)
+    const int ppt = np > kSelThreads ? 2 : 1;
+    int cpar[2] = {0, 0};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid * ppt + k;
+      if (k < ppt && i < np) {
+        double S = 0.0;
+        int d = 0;
+        if (!(root && i == 0)) {
+          const int e = g0 + i - root;
+          S = en.eS[e];
+          d = en.eDep[e];
         }
-        c = lo - 1;
+        if (d < L) {
+          const float* row = sm.v + d * K;
+          const double Zd = sm.Z[d];
+          int lo = 1, hi = K;  // first failing rank lies in [lo, hi]
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if ((S + (double)row[mid]) - Zd >= tau) lo = mid + 1;
+            else hi = mid;
+          }
+          cpar[k] = lo - 1;
+        }
       }
-      en.cnt[i] = c;
+    }
+    int A;
+    const int off = block_excl_scan_reg<kSelThreads>(cpar[0] + cpar[1], sm.wsum, A);
+    if (A == 0) break;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid * ppt + k;
+      if (k < ppt && i < np) en.cnt[i] = off + (k ? cpar[0] : 0);
     }
     __syncthreads();
-    const int A = block_excl_scan<kSelThreads>(en.cnt, np, sm.wsum);
-    if (A == 0) break;
     for (int a = tid; a < A; a += kSelThreads) {
       // parent = largest u with offset[u] <= a
       int lo = 0, hi = np - 1;
@@ -590,12 +490,22 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
       const double raw = S - sm.Z[d - 1];
       const double sc = raw > scu ? scu : raw;
       lex_set_digit(lh, ll, d, (uint32_t)r, bpd);
+      // chain length: the anchor, then rank-0 extensions while they reach
+      // tau (the spine values are read at addresses common to all threads)
+      // chain length: the anchor, then rank-0 extensions while they reach
+      // tau (the next depth's spine values are read one step ahead)
       int ell = 1;
       {
         double S2 = S, sc2 = sc;
+        float vn = sm.v[(d < L ? d : L - 1) * K];
+        double zn = sm.Z[d < L ? d : L - 1];
         for (int dd = d + 1; dd <= L; ++dd) {
-          S2 += (double)sm.v[(dd - 1) * K];
-          const double raw2 = S2 - sm.Z[dd - 1];
+          const double v0 = (double)vn, Zm = zn;
+          const int nx = dd < L ? dd : L - 1;
+          vn = sm.v[nx * K];
+          zn = sm.Z[nx];
+          S2 += v0;
+          const double raw2 = S2 - Zm;
           sc2 = raw2 > sc2 ? sc2 : raw2;
           if (sc2 < tau) break;
           ++ell;
@@ -613,19 +523,30 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
       en.eDep[pos] = (uint8_t)d;
       en.eLh[pos] = lh;
       en.eLl[pos] = ll | (uint64_t)d;
-      double S2 = S, sc2 = sc;
-      for (int i = 1; i < ell; ++i) {
-        const int dd = d + i;
-        S2 += (double)sm.v[(dd - 1) * K];
-        const double raw2 = S2 - sm.Z[dd - 1];
-        sc2 = raw2 > sc2 ? sc2 : raw2;
-        en.eS[pos + i] = S2;
-        en.eSc[pos + i] = sc2;
-        en.ePar[pos + i] = (int16_t)(pos + i - 1);
-        en.eRank[pos + i] = 0;
-        en.eDep[pos + i] = (uint8_t)dd;
-        en.eLh[pos + i] = lh;
-        en.eLl[pos + i] = ll | (uint64_t)dd;
+      {
+        double S2 = S, sc2 = sc;
+        float vn = sm.v[(d < L ? d : L - 1) * K];
+        double zn = sm.Z[d < L ? d : L - 1];
+        for (int i = 1; i < ell; ++i) {
+          const int dd = d + i;
+          const double v0 = (double)vn, Zm = zn;
+          const int nx = dd < L ? dd : L - 1;
+          vn = sm.v[nx * K];
+          zn = sm.Z[nx];
+          S2 += v0;
+          const double raw2 = S2 - Zm;
+          sc2 = raw2 > sc2 ? sc2 : raw2;
+          {
+            const int q = pos + i;
+            en.eS[q] = S2;
+            en.eSc[q] = sc2;
+            en.ePar[q] = (int16_t)(q - 1);
+            en.eRank[q] = 0;
+            en.eDep[q] = (uint8_t)dd;
+            en.eLh[q] = lh;
+            en.eLl[q] = ll | (uint64_t)dd;
+          }
+        }
       }
     }
     __syncthreads();
@@ -663,13 +584,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
       for (int i = tid; i < nE; i += kSelThreads) atomicAdd(&sm.hist[bin_of(en.eSc[i])], 1);
       __syncthreads();
       // inclusive scan of the bins; the first bin reaching B is the cut
-      int x = sm.hist[tid];
+      const int x = wave_incl_scan(sm.hist[tid]);
       const int lane = tid & 63, w = tid >> 6;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-      }
       if (lane == kWave - 1) sm.wsum[w] = x;
       __syncthreads();
       int pre = 0;
