@@ -116,6 +116,7 @@ struct SelectSmem {
   int n2;
   int kcut;
   int hist[kSelThreads];
+  int hexc[kSelThreads];  // entries in the bins before each bin
   double tau;
   int nE;
   int ovf;
@@ -133,15 +134,6 @@ __device__ __forceinline__ void lex_set_digit(uint64_t& hi, uint64_t& lo, int d,
   lo |= l;
 }
 
-// e1 strictly before e2 in the output order (PAD = 0xFFFF is last).
-__device__ __forceinline__ bool sel_before(const SelEnum& en, int e1, int e2) {
-  if (e1 == 0xFFFF) return false;
-  if (e2 == 0xFFFF) return true;
-  const double a = en.eSc[e1], b = en.eSc[e2];
-  if (a != b) return a > b;
-  if (en.eLh[e1] != en.eLh[e2]) return en.eLh[e1] < en.eLh[e2];
-  return en.eLl[e1] < en.eLl[e2];
-}
 
 // ---------------------------------------------------------------------------
 // Fallback: best-first heap over rank tuples in one thread (LDS).
@@ -312,60 +304,6 @@ __device__ double sel_tau_hist(SelectSmem& sm, int L, int K, int B) {
   }
   __syncthreads();
   return sm.tau;
-}
-
-// Position in the output order (score desc, then lexicographic rank key asc;
-// keys are unique) of every entry listed in ord[0..n2), left in cnt: the
-// number of listed entries before it. The listed scores sit compactly in
-// s2. Each entry's count is split over P lanes (P a power of two, P * n2 <=
-// the block size when it fits) and summed by shuffles; equal scores (rare:
-// log-probabilities only tie exactly) take the lexicographic keys.
-__device__ void sel_rank(SelEnum& en, const double* s2, int n2) {
-  int P = 1;
-  while (P < kWave && 2 * P * n2 <= kSelThreads) P *= 2;
-  const int groups = kSelThreads / P;
-  const int tid = threadIdx.x, g = tid / P, part = tid - g * P;
-  const int per = (n2 + P - 1) / P;
-  for (int k0 = 0; k0 < n2; k0 += groups) {  // uniform trip count
-    const int k = k0 + g;
-    int rank = 0;
-    int i = 0;
-    if (k < n2) {
-      const double si = s2[k];
-      i = en.ord[k];
-      const uint64_t hi_i = en.eLh[i], lo_i = en.eLl[i];
-      const int j0 = part * per, j1 = j0 + per < n2 ? j0 + per : n2;
-      auto before = [&](int j, double sj) -> int {
-        const int e = en.ord[j];
-        const uint64_t hj = en.eLh[e], lj = en.eLl[e];
-        return (sj == si && j != k && (hj < hi_i || (hj == hi_i && lj < lo_i))) ? 1 : 0;
-      };
-      constexpr int U = 8;
-      int j = j0;
-      for (; j + U <= j1; j += U) {
-        double sj[U];
-        bool tie = false;
-#pragma unroll
-        for (int u = 0; u < U; ++u) sj[u] = s2[j + u];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          rank += sj[u] > si ? 1 : 0;
-          tie |= sj[u] == si && j + u != k;
-        }
-        if (tie) {
-#pragma unroll
-          for (int u = 0; u < U; ++u) rank += before(j + u, sj[u]);
-        }
-      }
-      for (; j < j1; ++j) {
-        const double sj = s2[j];
-        rank += (sj > si ? 1 : 0) + before(j, sj);
-      }
-    }
-    for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o);
-    if (k < n2 && part == 0) en.cnt[i] = rank;
-  }
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -563,57 +501,90 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     __syncthreads();
   } else {
     // ---- 3. order E, emit the first B ----------------------------------------
-    // Second cut: E's scores fall into kSelThreads bins over [tau, best]
-    // (bin index monotone in the score, so equal scores share a bin); E2 =
-    // the entries of the first bins that hold >= B of them. E2 is closed
-    // upwards in the order, so it holds the output, and it is ranked alone.
+    // E's scores fall into kSelThreads bins over [tau, best] (bin index
+    // monotone in the score, so equal scores share a bin and a lower bin
+    // holds only better scores). E2 = the entries of the first bins that
+    // hold >= B of them (all of E when nE <= B); it is closed upwards in the
+    // order, so it holds the output. E2 is placed in bin order, and an
+    // entry's position is its bin's offset plus the members of its own bin
+    // before it (score, then the 128-bit lexicographic rank key).
     const int nE = sm.nE;
     static_assert(kECap <= 2 * kSelThreads, "two entries per thread at most");
     const double top = sm.sig[1];  // the best prefix: depth 1, rank 0
     const double span = top - tau;
-    const bool cut = nE > B && span > 0.0;
-    const double scale = cut ? (double)kSelThreads / span : 0.0;
+    const double scale = span > 0.0 ? (double)kSelThreads / span : 0.0;
     auto bin_of = [&](double sc) -> int {
       const double t = (top - sc) * scale;
       return t >= (double)(kSelThreads - 1) ? kSelThreads - 1 : (t > 0.0 ? (int)t : 0);
     };
-    int kcut = kSelThreads - 1;
-    if (cut) {
-      sm.hist[tid] = 0;
-      __syncthreads();
-      for (int i = tid; i < nE; i += kSelThreads) atomicAdd(&sm.hist[bin_of(en.eSc[i])], 1);
-      __syncthreads();
-      // inclusive scan of the bins; the first bin reaching B is the cut
-      const int x = wave_incl_scan(sm.hist[tid]);
+    sm.hist[tid] = 0;
+    __syncthreads();
+    int ebin[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + k * kSelThreads;
+      ebin[k] = i < nE ? bin_of(en.eSc[i]) : kSelThreads;
+      if (i < nE) atomicAdd(&sm.hist[ebin[k]], 1);
+    }
+    __syncthreads();
+    {
+      const int h = sm.hist[tid];
+      const int x = wave_incl_scan(h);
       const int lane = tid & 63, w = tid >> 6;
       if (lane == kWave - 1) sm.wsum[w] = x;
       __syncthreads();
       int pre = 0;
       for (int q = 0; q < w; ++q) pre += sm.wsum[q];
-      const int inc = pre + x, exc = inc - sm.hist[tid];
-      if (inc >= B && exc < B) sm.kcut = tid;
-      __syncthreads();
-      kcut = sm.kcut;
+      const int inc = pre + x, exc = inc - h;
+      // the first bin reaching B is the cut (the last bin when nE <= B)
+      if (nE > B ? (inc >= B && exc < B) : tid == kSelThreads - 1) {
+        sm.kcut = tid;
+        sm.n2 = inc;
+      }
+      sm.hexc[tid] = exc;
+      sm.hist[tid] = 0;  // now the bins' fill counters (only this thread read it)
     }
-    if (tid == 0) sm.n2 = 0;
     __syncthreads();
-    double* s2 = en.eS;  // dead after the enumeration
-    for (int i0 = 0; i0 < nE; i0 += kSelThreads) {
-      const int i = i0 + tid;
-      const bool keep = i < nE && (!cut || bin_of(en.eSc[i]) <= kcut);
-      const uint64_t M = __ballot(keep);
-      int base = 0;
-      if ((tid & 63) == 0 && M) base = atomicAdd(&sm.n2, __popcll(M));
-      base = __shfl(base, 0);
-      if (keep) {
-        const int k = base + lanes_below(M);
-        en.ord[k] = (uint16_t)i;
-        s2[k] = en.eSc[i];
+    const int kcut = sm.kcut, n2 = sm.n2;
+    // E2 in bin order, with compact copies of the order keys: scores in eS,
+    // rank keys in the (dead) table of row values
+    double* s2 = en.eS;
+    uint64_t* h2 = (uint64_t*)sm.v;
+    uint64_t* l2 = h2 + kECap;
+    static_assert(2 * kECap * sizeof(uint64_t) <= sizeof(sm.v), "rank keys fit the row table");
+    int epos[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + k * kSelThreads;
+      epos[k] = -1;
+      if (i < nE && ebin[k] <= kcut) {
+        const int q = sm.hexc[ebin[k]] + atomicAdd(&sm.hist[ebin[k]], 1);
+        epos[k] = q;
+        en.ord[q] = (uint16_t)i;
+        s2[q] = en.eSc[i];
+        h2[q] = en.eLh[i];
+        l2[q] = en.eLl[i];
       }
     }
     __syncthreads();
-    const int n2 = sm.n2;
-    sel_rank(en, s2, n2);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + k * kSelThreads;
+      if (epos[k] >= 0) {
+        const int bb = ebin[k], me = epos[k];
+        const int lo = sm.hexc[bb], hi = bb + 1 < kSelThreads ? sm.hexc[bb + 1] : nE;
+        const double si = s2[me];
+        const uint64_t hi_i = h2[me], lo_i = l2[me];
+        int rank = lo;
+        for (int q = lo; q < hi; ++q) {
+          const double sq = s2[q];
+          const uint64_t hq = h2[q], lq = l2[q];
+          rank += (sq > si || (sq == si && (hq < hi_i || (hq == hi_i && lq < lo_i)))) ? 1 : 0;
+        }
+        en.cnt[i] = rank;
+      }
+    }
+    __syncthreads();
     const int nsel = nE < B ? nE : B;
     for (int k = tid; k < n2; k += kSelThreads) {
       const int i = en.ord[k];
