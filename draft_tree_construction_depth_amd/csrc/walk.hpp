@@ -76,45 +76,47 @@ __global__ __launch_bounds__(kWave) void walk_kernel(WalkParams p) {
   const int64_t b = blockIdx.x;
   const int lane = threadIdx.x;
   const int B = p.B, L = p.L;
-  int n = p.num_nodes[b];
-  n = n < 0 ? 0 : (n > B ? B : n);
   const int32_t* tgt = p.target_tokens + (size_t)b * (B + 1);
   // node j+1 lives in lane j % 64, slot j / 64, with its parent, token and
-  // target token; every load is issued before the walk starts
+  // target token. Every load (bounded by B, not by the node count) is issued
+  // together with the node count's; nodes past the count are masked after.
   int par[kWalkMaxPerLane], tok[kWalkMaxPerLane], tg[kWalkMaxPerLane];
 #pragma unroll
   for (int t = 0; t < kWalkMaxPerLane; ++t) {
     const int j = lane + t * kWave;
-    const bool ok = j < n;
-    par[t] = ok ? p.parents[(size_t)b * B + j] : -2;
-    tok[t] = ok ? p.tree_tokens[(size_t)b * B + j] : 0;
-    tg[t] = ok ? tgt[j + 1] : 0;
+    const bool in = j < B;
+    par[t] = in ? p.parents[(size_t)b * B + j] : -2;
+    tok[t] = in ? p.tree_tokens[(size_t)b * B + j] : 0;
+    tg[t] = in ? tgt[j + 1] : 0;
   }
   const int root_tgt = tgt[0];
-  // target token of node u (uniform): the root's, or a read of the owner lane
-  auto target_of = [&](int u) -> int {
-    if (u == 0) return root_tgt;
-    const int j = u - 1, t = j >> 6, src = j & 63;
-    int v = 0;
+  int n = p.num_nodes[b];
+  n = n < 0 ? 0 : (n > B ? B : n);
+  const int slots = (n + kWave - 1) / kWave;  // uniform
 #pragma unroll
-    for (int q = 0; q < kWalkMaxPerLane; ++q)
-      if (q == t) v = __shfl(tg[q], src);
-    return v;
-  };
+  for (int t = 0; t < kWalkMaxPerLane; ++t)
+    if (lane + t * kWave >= n) par[t] = -2;  // never a child
   int cur = 0, len = 0, want = root_tgt;
   while (len < L) {
-    // the child of cur carrying the wanted token (lowest node number if several)
-    int found = 0;
+    // the child of cur carrying the wanted token (lowest node number if
+    // several); its target token is read from its lane
+    int found = 0, next = 0;
 #pragma unroll
     for (int t = 0; t < kWalkMaxPerLane; ++t) {
-      const uint64_t M = __ballot(par[t] == cur && tok[t] == want);
-      if (found == 0 && M) found = t * kWave + __builtin_ctzll(M) + 1;
+      if (t < slots && found == 0) {
+        const uint64_t M = __ballot(par[t] == cur && tok[t] == want);
+        if (M) {
+          const int src = __builtin_ctzll(M);
+          found = t * kWave + src + 1;
+          next = __builtin_amdgcn_readlane(tg[t], src);
+        }
+      }
     }
     if (found == 0) break;
     if (lane == 0) p.accepted_nodes[(size_t)b * L + len] = found;
     ++len;
     cur = found;
-    want = target_of(cur);
+    want = next;
   }
   for (int i = len + lane; i < L; i += kWave) p.accepted_nodes[(size_t)b * L + i] = -1;
   if (lane == 0) {
