@@ -483,9 +483,11 @@ int treespark_expand(const void* backbone, const void* W, const void* E, const i
     gp.psum = psum;
     gp.pval = pval;
     gp.pid = pid;
-    hipLaunchKernelGGL(ddt::ts_gemm_kernel,
-                       dim3((unsigned)sh.nvt, (unsigned)((M + ddt::kTsBM - 1) / ddt::kTsBM)),
-                       dim3(ddt::kTsThreads), 0, stream, gp);
+    const dim3 ggrid((unsigned)sh.nvt, (unsigned)((M + ddt::kTsBM - 1) / ddt::kTsBM));
+    if (sh.kk <= 4)
+      hipLaunchKernelGGL(ddt::ts_gemm_kernel<4>, ggrid, dim3(ddt::kTsThreads), 0, stream, gp);
+    else
+      hipLaunchKernelGGL(ddt::ts_gemm_kernel<8>, ggrid, dim3(ddt::kTsThreads), 0, stream, gp);
     ddt::TsMergeParams mp;
     mp.st = st;
     mp.pmax = pmax;

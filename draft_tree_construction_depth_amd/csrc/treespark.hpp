@@ -59,24 +59,6 @@ struct TsGemmParams {
   int32_t* pid;            // [nvt][Mtot][kTsKMax]
 };
 
-// Insert (x, id) into a best-first list of length k (z desc, id asc),
-// branch-free: with better(i) = (x, id) precedes entry i (monotone along the
-// sorted list), entry i becomes entry i-1 if better(i-1), else x if better(i).
-__device__ __forceinline__ void ts_insert(float (&val)[kTsKMax], int (&ids)[kTsKMax], int k, float x,
-                                          int id) {
-  bool bt[kTsKMax];
-#pragma unroll
-  for (int i = 0; i < kTsKMax; ++i) bt[i] = i < k && (x > val[i] || (x == val[i] && id < ids[i]));
-#pragma unroll
-  for (int i = kTsKMax - 1; i >= 0; --i) {
-    const bool shift = i > 0 && bt[i > 0 ? i - 1 : 0];
-    const float pv = i > 0 ? val[i > 0 ? i - 1 : 0] : x;
-    const int pi = i > 0 ? ids[i > 0 ? i - 1 : 0] : id;
-    val[i] = shift ? pv : (bt[i] ? x : val[i]);
-    ids[i] = shift ? pi : (bt[i] ? id : ids[i]);
-  }
-}
-
 struct TsGemmSmem {
   union {
     uint16_t g[2][kTsBM][kTsKT + kTsGPad];  // parents' embedding rows, double buffered
@@ -89,45 +71,127 @@ struct TsGemmSmem {
   };
 };
 
+constexpr int kTsPad = 0x7FFFFFFF;  // id of an empty list slot (value -inf)
+
+// (x, i) before (y, j) in the order value desc, id asc.
+__device__ __forceinline__ bool ts_before(float x, int i, float y, int j) {
+  return x > y || (x == y && i < j);
+}
+
+__device__ __forceinline__ void ts_cas(float& av, int& ai, float& bv, int& bi) {
+  const bool sw = ts_before(bv, bi, av, ai);
+  const float tv = av;
+  const int ti = ai;
+  av = sw ? bv : av;
+  ai = sw ? bi : ai;
+  bv = sw ? tv : bv;
+  bi = sw ? ti : bi;
+}
+
+// Sort KK entries best first (odd-even transposition, KK rounds).
+template <int KK>
+__device__ __forceinline__ void ts_sort(float (&v)[KK], int (&id)[KK]) {
+#pragma unroll
+  for (int r = 0; r < KK; ++r)
+#pragma unroll
+    for (int i = r & 1; i + 1 < KK; i += 2) ts_cas(v[i], id[i], v[i + 1], id[i + 1]);
+}
+
+// Insert into a best-first list a value whose id exceeds every id in it (rows
+// visited in increasing order, list already full of real entries): it
+// precedes entry i exactly when its value is larger.
+template <int KK>
+__device__ __forceinline__ void ts_insert_inc(float (&val)[KK], int (&ids)[KK], float x, int id) {
+  bool bt[KK];
+#pragma unroll
+  for (int i = 0; i < KK; ++i) bt[i] = x > val[i];
+#pragma unroll
+  for (int i = KK - 1; i >= 0; --i) {
+    const bool shift = i > 0 && bt[i > 0 ? i - 1 : 0];
+    const float pv = i > 0 ? val[i > 0 ? i - 1 : 0] : x;
+    const int pi = i > 0 ? ids[i > 0 ? i - 1 : 0] : id;
+    val[i] = shift ? pv : (bt[i] ? x : val[i]);
+    ids[i] = shift ? pi : (bt[i] ? id : ids[i]);
+  }
+}
+
+// Best KK of two best-first lists: a[i] vs b[KK-1-i] keeps the best KK as a
+// bitonic sequence, then log2(KK) half-cleaner stages sort it.
+template <int KK>
+__device__ __forceinline__ void ts_merge_sorted(float (&av)[KK], int (&ai)[KK], const float (&bv)[KK],
+                                                const int (&bi)[KK]) {
+#pragma unroll
+  for (int i = 0; i < KK; ++i) {
+    const bool t = ts_before(bv[KK - 1 - i], bi[KK - 1 - i], av[i], ai[i]);
+    av[i] = t ? bv[KK - 1 - i] : av[i];
+    ai[i] = t ? bi[KK - 1 - i] : ai[i];
+  }
+#pragma unroll
+  for (int d = KK / 2; d > 0; d >>= 1)
+#pragma unroll
+    for (int i = 0; i < KK; ++i)
+      if ((i & d) == 0) ts_cas(av[i], ai[i], av[i + d], ai[i + d]);
+}
+
+template <int KK>
 __global__ __launch_bounds__(kTsThreads) void ts_gemm_kernel(TsGemmParams p) {
   __shared__ TsGemmSmem sm;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int vt = blockIdx.x;
   const int m0 = blockIdx.y * kTsBM;
-  const int H = p.H, K = p.k;
+  const int H = p.H;
   const int64_t V = p.V;
   const int ncols = p.M - m0 < kTsBM ? p.M - m0 : kTsBM;
   const int nct = (ncols + 31) >> 5;  // MFMA column tiles in use
 
-  // this lane's W row (A operand: row l % 32 of the wave's 32 rows)
-  const int64_t vrow = (int64_t)vt * kTsBV + w * 32 + (l & 31);
-  const int64_t vload = vrow < V ? vrow : V - 1;  // rows past V load row V-1, masked later
-  const uint16_t* wrow = p.W + vload * H + 8 * (l >> 5);
+  // W through a buffer resource over this workgroup's rows: the lane's byte
+  // offset is fixed, the k-step's goes in a scalar, so no address arithmetic
+  // per step (A operand: row l % 32 of the wave's 32 rows; rows past V read
+  // row V-1 and are masked later)
+  const int64_t vt0 = (int64_t)vt * kTsBV;
+  const int64_t vrow = vt0 + w * 32 + (l & 31);
+  const int64_t vload = vrow < V ? vrow : V - 1;
+  const int64_t wbytes = (V - vt0) * H * 2;
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.W + vt0 * H), (short)0, (int)(wbytes < 0x7FFFFFFF ? wbytes : 0x7FFFFFFF), 0x00020000);
+  const int woff = (int)((vload - vt0) * H * 2 + 16 * (l >> 5));
 
   // embedding-row staging: thread t copies 16-byte chunk (t % 8) of rows t/8 + 32 i
   const int gch = tid & 7, grow0 = tid >> 3;
-  const uint16_t* erow[4];
+  const int64_t ebytes = V * H * 2;
+  const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.E, (short)0, (int)(ebytes < 0x7FFFFFFF ? ebytes : 0x7FFFFFFF), 0x00020000);
+  int eoff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = grow0 + 32 * i;
     const int m = m0 + (r < ncols ? r : 0);
-    erow[i] = p.E + (int64_t)p.ptok[m] * H + 8 * gch;
+    eoff[i] = (int)((int64_t)p.ptok[m] * H * 2 + 16 * gch);
   }
 
   const int nks = H / kTsKT;
-  // W k-steps ks+1 and ks+2 are in flight while ks is multiplied
-  u32x4 wa[4], wb[4], wc[4], ga[4];
+  u32x4 wx0[4], wx1[4], wx2[4], gy0[4], gy1[4];
   auto load_w = [&](u32x4 (&dst)[4], int ks) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) dst[s] = *(const u32x4*)(wrow + ks * kTsKT + 16 * s);
+    for (int s = 0; s < 4; ++s)
+      dst[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             wrs, woff, ks * kTsKT * 2 + 32 * s, 0));
   };
-  auto load_g = [&](int ks) {
+  auto load_g = [&](u32x4 (&dst)[4], int ks) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ga[i] = *(const u32x4*)(erow[i] + ks * kTsKT);
+    for (int i = 0; i < 4; ++i)
+      dst[i] = __builtin_bit_cast(u32x4,
+                                  __builtin_amdgcn_raw_buffer_load_b128(ers, eoff[i], ks * kTsKT * 2, 0));
   };
-  auto store_g = [&](int buf) {
+  auto store_g = [&](const u32x4 (&src)[4], int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4*)&sm.g[buf][grow0 + 32 * i][8 * gch] = ga[i];
+    for (int i = 0; i < 4; ++i) *(u32x4*)&sm.g[buf][grow0 + 32 * i][8 * gch] = src[i];
+  };
+  // Workgroup barrier for the LDS double buffer only: waits for this wave's
+  // LDS traffic, not for its global loads in flight (a full __syncthreads
+  // fence would drain them and undo the prefetch).
+  auto lds_barrier = [&]() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
   f32x16 acc[4];
@@ -136,20 +200,19 @@ __global__ __launch_bounds__(kTsThreads) void ts_gemm_kernel(TsGemmParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
 
-  load_w(wa, 0);
-  load_w(wb, nks > 1 ? 1 : 0);
-  load_g(0);
-  store_g(0);
-  __syncthreads();
-  for (int ks = 0; ks < nks; ++ks) {
+  // Step ks multiplies W(ks) with the parents' chunk in LDS buffer ks & 1,
+  // issues the loads of W(ks+2) and of the parents' chunk ks+2, and stores
+  // chunk ks+1 (loaded during step ks-1) into the other buffer: two steps of
+  // latency hidden for both streams. Three W and two chunk register sets
+  // rotate by name (six steps unrolled), so no copy waits on a load.
+  auto step = [&](int ks, u32x4 (&wu)[4], u32x4 (&wl)[4], u32x4 (&gs)[4], u32x4 (&gl)[4]) {
     const int buf = ks & 1;
-    const bool more = ks + 1 < nks;
-    // always issue (a valid k-step when past the end) so wait counts stay static
-    load_w(wc, ks + 2 < nks ? ks + 2 : nks - 1);
-    if (more) load_g(ks + 1);
+    const int kn = ks + 2 < nks ? ks + 2 : nks - 1;  // always issue, so wait counts stay static
+    load_w(wl, kn);
+    load_g(gl, kn);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, wa[s]);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, wu[s]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         if (c < nct) {
@@ -159,14 +222,30 @@ __global__ __launch_bounds__(kTsThreads) void ts_gemm_kernel(TsGemmParams p) {
         }
       }
     }
-    if (more) store_g(buf ^ 1);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      wa[s] = wb[s];
-      wb[s] = wc[s];
-    }
-    __syncthreads();
+    if (ks + 1 < nks) store_g(gs, buf ^ 1);
+    lds_barrier();
+  };
+
+  load_w(wx0, 0);
+  load_w(wx1, nks > 1 ? 1 : 0);
+  load_g(gy0, 0);
+  load_g(gy1, nks > 1 ? 1 : 0);
+  store_g(gy0, 0);
+  lds_barrier();
+  for (int ks = 0; ks < nks; ks += 6) {
+    step(ks, wx0, wx2, gy1, gy0);
+    if (ks + 1 >= nks) break;
+    step(ks + 1, wx1, wx0, gy0, gy1);
+    if (ks + 2 >= nks) break;
+    step(ks + 2, wx2, wx1, gy1, gy0);
+    if (ks + 3 >= nks) break;
+    step(ks + 3, wx0, wx2, gy0, gy1);
+    if (ks + 4 >= nks) break;
+    step(ks + 4, wx1, wx0, gy1, gy0);
+    if (ks + 5 >= nks) break;
+    step(ks + 5, wx2, wx1, gy0, gy1);
   }
+  __syncthreads();
 
   // ---- epilogue: z = Z + l_d; per column the wave's max, exp sum and top-k
   // acc[c][r] holds row 8 (r / 4) + 4 (l / 32) + r % 4 of the wave's 32 rows,
@@ -195,34 +274,36 @@ __global__ __launch_bounds__(kTsThreads) void ts_gemm_kernel(TsGemmParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += z[r] == -INFINITY ? 0.0f : __expf(z[r] - mx);
     s += __shfl_xor(s, 32);
-    float tv[kTsKMax];
-    int ti[kTsKMax];
+    // the lane's best KK of its 16 rows (ids increase with r): the first KK
+    // sorted, the rest inserted; rows past V are empty slots
+    float tv[KK];
+    int ti[KK];
 #pragma unroll
-    for (int i = 0; i < kTsKMax; ++i) {
-      tv[i] = -INFINITY;
-      ti[i] = 0x7FFFFFFF;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < KK; ++r) {
       const int64_t v = vbase + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-      if (v < V) ts_insert(tv, ti, K, z[r], (int)v);
+      tv[r] = z[r];
+      ti[r] = v < V ? (int)v : kTsPad;
+    }
+    ts_sort<KK>(tv, ti);
+#pragma unroll
+    for (int r = KK; r < 16; ++r) {
+      const int64_t v = vbase + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+      if (v < V) ts_insert_inc<KK>(tv, ti, z[r], (int)v);
     }
     // merge the partner lane's list
-    float ov[kTsKMax];
-    int oi[kTsKMax];
+    float ov[KK];
+    int oi[KK];
 #pragma unroll
-    for (int i = 0; i < kTsKMax; ++i) {
+    for (int i = 0; i < KK; ++i) {
       ov[i] = __shfl_xor(tv[i], 32);
       oi[i] = __shfl_xor(ti[i], 32);
     }
-#pragma unroll
-    for (int i = 0; i < kTsKMax; ++i)
-      if (i < K && oi[i] != 0x7FFFFFFF) ts_insert(tv, ti, K, ov[i], oi[i]);
+    ts_merge_sorted<KK>(tv, ti, ov, oi);
     if (l < 32) {
       sm.red.mx[w][col] = mx;
       sm.red.sm[w][col] = s;
 #pragma unroll
-      for (int i = 0; i < kTsKMax; ++i) {
+      for (int i = 0; i < KK; ++i) {
         sm.red.val[w][col][i] = tv[i];
         sm.red.id[w][col][i] = ti[i];
       }
@@ -236,28 +317,33 @@ __global__ __launch_bounds__(kTsThreads) void ts_gemm_kernel(TsGemmParams p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) mx = fmaxf(mx, sm.red.mx[q][col]);
     float s = 0.0f;
-    float tv[kTsKMax];
-    int ti[kTsKMax];
+    float tv[KK];
+    int ti[KK];
 #pragma unroll
-    for (int i = 0; i < kTsKMax; ++i) {
-      tv[i] = -INFINITY;
-      ti[i] = 0x7FFFFFFF;
+    for (int i = 0; i < KK; ++i) {
+      tv[i] = sm.red.val[0][col][i];
+      ti[i] = sm.red.id[0][col][i];
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float mq = sm.red.mx[q][col];
       if (mq != -INFINITY) s += sm.red.sm[q][col] * __expf(mq - mx);
+      if (q > 0) {
+        float bv[KK];
+        int bi[KK];
 #pragma unroll
-      for (int i = 0; i < kTsKMax; ++i) {
-        const int id = sm.red.id[q][col][i];
-        if (i < K && id != 0x7FFFFFFF) ts_insert(tv, ti, K, sm.red.val[q][col][i], id);
+        for (int i = 0; i < KK; ++i) {
+          bv[i] = sm.red.val[q][col][i];
+          bi[i] = sm.red.id[q][col][i];
+        }
+        ts_merge_sorted<KK>(tv, ti, bv, bi);
       }
     }
     const size_t o = (size_t)vt * p.Mtot + m0 + col;
     p.pmax[o] = mx;
     p.psum[o] = s;
 #pragma unroll
-    for (int i = 0; i < kTsKMax; ++i) {
+    for (int i = 0; i < KK; ++i) {
       p.pval[o * kTsKMax + i] = tv[i];
       p.pid[o * kTsKMax + i] = ti[i];
     }
