@@ -283,7 +283,8 @@ TsLayout ts_layout(int64_t batch, const TsShape& sh) {
 int ts_check(int64_t batch, int32_t D, int64_t V, int32_t H, int32_t k, int32_t F, int32_t N) {
   if (batch < 0 || D <= 0 || V <= 0 || H <= 0 || k <= 0 || F <= 0 || N <= 0) return DDT_EINVAL;
   if (D > ddt::kTsDMax || k > ddt::kTsKMax || F > ddt::kTsFMax || H % ddt::kTsKT != 0 ||
-      V > 0x7FFFFFFFLL || N > 4096 || batch > 0x7FFFFFFFLL / ddt::kTsFMax)
+      V > 0x7FFFFFFFLL || N > 4096 || batch > 0x7FFFFFFFLL / ddt::kTsFMax ||
+      V * (int64_t)H * 2 > 0xFFFFFFFFLL)  // byte offsets into E are 32-bit
     return DDT_ENOTSUP;
   return DDT_OK;
 }

@@ -154,19 +154,21 @@ __global__ __launch_bounds__(kTsThreads) void ts_gemm_kernel(TsGemmParams p) {
   const int64_t wbytes = (V - vt0) * H * 2;
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.W + vt0 * H), (short)0, (int)(wbytes < 0x7FFFFFFF ? wbytes : 0x7FFFFFFF), 0x00020000);
-  const int woff = (int)((vload - vt0) * H * 2 + 16 * (l >> 5));
+  const uint32_t woff = (uint32_t)((vload - vt0) * H * 2 + 16 * (l >> 5));  // < V * H * 2 < 2^32
 
   // embedding-row staging: thread t copies 16-byte chunk (t % 8) of rows t/8 + 32 i
   const int gch = tid & 7, grow0 = tid >> 3;
-  const int64_t ebytes = V * H * 2;
-  const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)p.E, (short)0, (int)(ebytes < 0x7FFFFFFF ? ebytes : 0x7FFFFFFF), 0x00020000);
-  int eoff[4];
+  // E as one buffer resource: byte offsets are unsigned 32-bit (the host
+  // rejects tables of 4 GiB or more)
+  const uint32_t ebytes = (uint32_t)(V * H * 2);
+  const __amdgpu_buffer_rsrc_t ers =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.E, (short)0, (int)ebytes, 0x00020000);
+  uint32_t eoff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = grow0 + 32 * i;
     const int m = m0 + (r < ncols ? r : 0);
-    eoff[i] = (int)((int64_t)p.ptok[m] * H * 2 + 16 * gch);
+    eoff[i] = (uint32_t)p.ptok[m] * (uint32_t)H * 2u + 16u * (uint32_t)gch;
   }
 
   const int nks = H / kTsKT;
@@ -175,13 +177,13 @@ __global__ __launch_bounds__(kTsThreads) void ts_gemm_kernel(TsGemmParams p) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       dst[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             wrs, woff, ks * kTsKT * 2 + 32 * s, 0));
+                                             wrs, (int)woff, ks * kTsKT * 2 + 32 * s, 0));
   };
   auto load_g = [&](u32x4 (&dst)[4], int ks) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      dst[i] = __builtin_bit_cast(u32x4,
-                                  __builtin_amdgcn_raw_buffer_load_b128(ers, eoff[i], ks * kTsKT * 2, 0));
+      dst[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ers, (int)eoff[i], ks * kTsKT * 2, 0));
   };
   auto store_g = [&](const u32x4 (&src)[4], int buf) {
 #pragma unroll

@@ -197,7 +197,8 @@ int ddtree_row_topk(const void* logits, int dtype, int64_t rows, int64_t V, int3
  *          -1, -1, -inf, 0. ddtree_mask builds the mask from parents.
  * z accumulates in float32 (bf16 MFMA), log-sum-exp combines in float64.
  * Supported: 1 <= D <= 16, 1 <= k <= 8, 1 <= F <= 8, 1 <= N <= 4096,
- * H a positive multiple of 64, V < 2^31; otherwise DDT_ENOTSUP.
+ * H a positive multiple of 64, V < 2^31, V * H * 2 < 2^32 (the embedding
+ * table is addressed with 32-bit byte offsets); otherwise DDT_ENOTSUP.
  * The workspace (treespark_workspace_size bytes, no zero-fill needed) holds
  * per-depth partial records and the candidates.
  */

@@ -62,6 +62,18 @@ def test_workspace_sizes(L):
     assert L.ddtree_build_workspace_size(256, 15, 151936, 256, 0) >= s3
 
 
+def test_treespark_workspace_and_limits(L):
+    ws = L.treespark_workspace_size
+    ws.restype = C.c_size_t
+    ws.argtypes = [C.c_int64, C.c_int32, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int32]
+    assert ws(32, 7, 151936, 2560, 4, 4, 32) > 0              # the README shape
+    assert ws(32, 7, 151936, 8192, 4, 4, 32) > 0              # 2.5 GB tables: 32-bit offsets
+    assert ws(32, 7, 151936, 14144, 4, 4, 32) == 0            # V * H * 2 >= 2^32: unsupported
+    assert ws(32, 7, 151936, 2500, 4, 4, 32) == 0             # H not a multiple of 64
+    assert ws(32, 17, 151936, 2560, 4, 4, 32) == 0            # D > 16
+    assert ws(32, 7, 151936, 2560, 9, 4, 32) == 0             # k > 8
+
+
 FAKE = C.c_void_p(0x100000)      # never dereferenced: every call below fails validation
 MISALIGNED = C.c_void_p(0x100004)
 
