@@ -7,12 +7,15 @@ include/ddtree.h); this package only binds it:
     ddtree_select    stage 2 alone, from stage-1 tables (+ mask)
     ddtree_mask      parents -> bit-packed ancestor-only attention mask
     ddtree_accept    tree + target tokens -> accepted path, new bonus token
+    ddtree_compact_kv  KV caches keep only the accepted path's rows (in place)
     ddtree_row_topk  stage 1 alone: per-row sorted top-K and log-sum-exp
     treespark_expand TreeSpark parent-conditioned tree (bf16 MFMA head)
 """
 
-from ._lib import (DDT_BF16, DDT_F32, DDTreeError, ddtree_accept, ddtree_build, ddtree_mask,
-                   ddtree_row_topk, ddtree_select, lib, status_string, treespark_expand)
+from ._lib import (DDT_BF16, DDT_F32, DDTreeError, ddtree_accept, ddtree_build, ddtree_compact_kv,
+                   ddtree_mask, ddtree_row_topk, ddtree_select, lib, status_string,
+                   treespark_expand)
 
-__all__ = ["DDT_BF16", "DDT_F32", "DDTreeError", "ddtree_accept", "ddtree_build", "ddtree_mask",
+__all__ = ["DDT_BF16", "DDT_F32", "DDTreeError", "ddtree_accept", "ddtree_build",
+           "ddtree_compact_kv", "ddtree_mask",
            "ddtree_row_topk", "ddtree_select", "lib", "status_string", "treespark_expand"]

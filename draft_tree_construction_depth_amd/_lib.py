@@ -52,6 +52,8 @@ def lib() -> C.CDLL:
         L.ddtree_mask.argtypes = [p, p, i64, i32, p, p]
         L.ddtree_accept.restype = C.c_int
         L.ddtree_accept.argtypes = [p, p, p, p, i64, i32, i32, p, p, p, p]
+        L.ddtree_compact_kv.restype = C.c_int
+        L.ddtree_compact_kv.argtypes = [p, p, i64, i64, i32, i64, i32, p, p, p, i32, p, p]
         L.ddtree_row_topk.restype = C.c_int
         L.ddtree_row_topk.argtypes = [p, C.c_int, i64, i64, i32, p, p, p, p, sz, p]
         L.treespark_workspace_size.restype = sz
@@ -208,6 +210,32 @@ def ddtree_accept(tree_tokens: torch.Tensor, parents: torch.Tensor, num_nodes: t
                              _ptr(out["accept_len"]), _ptr(out["next_token"]), _stream(dev))
     _check("ddtree_accept", rc)
     return out
+
+
+def ddtree_compact_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, past_len: torch.Tensor,
+                      accepted_nodes: torch.Tensor, accept_len: torch.Tensor,
+                      new_len: torch.Tensor | None = None) -> torch.Tensor:
+    """In place: caches [layers, batch, heads, cap, head_dim] keep the accepted path's
+    rows (slots past_len+1 .. past_len+accept_len); returns new_len [batch]."""
+    if not isinstance(k_cache, torch.Tensor) or k_cache.dim() != 5:
+        raise ValueError("k_cache must be a 5-d tensor [layers, batch, heads, cap, head_dim]")
+    _arg(k_cache, "k_cache", (k_cache.dtype,))
+    _arg(v_cache, "v_cache", (k_cache.dtype,), tuple(k_cache.shape))
+    layers, batch, heads, cap, dh = k_cache.shape
+    _arg(past_len, "past_len", _I32, (batch,))
+    _arg(accepted_nodes, "accepted_nodes", _I32)
+    L = accepted_nodes.shape[-1]
+    _arg(accepted_nodes, "accepted_nodes", _I32, (batch, L))
+    _arg(accept_len, "accept_len", _I32, (batch,))
+    dev = k_cache.device
+    if new_len is None:
+        new_len = torch.empty((batch,), dtype=torch.int32, device=dev)
+    rc = lib().ddtree_compact_kv(_ptr(k_cache), _ptr(v_cache), layers, batch, heads, cap,
+                                 dh * k_cache.element_size(), _ptr(past_len),
+                                 _ptr(accepted_nodes), _ptr(accept_len), L, _ptr(new_len),
+                                 _stream(dev))
+    _check("ddtree_compact_kv", rc)
+    return new_len
 
 
 def ddtree_row_topk(logits: torch.Tensor, K: int, *, out: dict | None = None,

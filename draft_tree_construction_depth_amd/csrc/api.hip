@@ -8,6 +8,7 @@
 #include "stage1.hpp"
 #include "treespark.hpp"
 #include "walk.hpp"
+#include "kv.hpp"
 
 namespace {
 
@@ -419,6 +420,38 @@ int ddtree_accept(const int32_t* tree_tokens, const int32_t* parents, const int3
   wp.accept_len = accept_len;
   wp.next_token = next_token;
   hipLaunchKernelGGL(ddt::walk_kernel, dim3((unsigned)batch), dim3(ddt::kWave), 0, stream, wp);
+  return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
+}
+
+int ddtree_compact_kv(void* k_cache, void* v_cache, int64_t layers, int64_t batch,
+                      int32_t heads, int64_t cap, int32_t row_bytes, const int32_t* past_len,
+                      const int32_t* accepted_nodes, const int32_t* accept_len, int32_t L,
+                      int32_t* new_len, hipStream_t stream) {
+  if (layers < 0 || batch < 0 || heads < 0 || cap <= 0 || row_bytes <= 0 || L <= 0)
+    return DDT_EINVAL;
+  if (layers == 0 || batch == 0 || heads == 0) return DDT_OK;
+  if (!k_cache || !v_cache || !past_len || !accepted_nodes || !accept_len) return DDT_EINVAL;
+  if (((uintptr_t)k_cache | (uintptr_t)v_cache) & 15) return DDT_EINVAL;
+  if (row_bytes % 16 != 0 || row_bytes > 1024 || L > DDT_MAX_L) return DDT_ENOTSUP;
+  const int64_t slices = layers * batch * heads;
+  const int64_t per_block = ddt::kKvThreads / ddt::kWave;
+  const int64_t blocks = (slices + per_block - 1) / per_block;
+  if (blocks > 0x7FFFFFFFLL || batch > 0x7FFFFFFFLL) return DDT_ENOTSUP;
+  ddt::KvParams kp;
+  kp.k = (unsigned char*)k_cache;
+  kp.v = (unsigned char*)v_cache;
+  kp.layers = layers;
+  kp.batch = batch;
+  kp.cap = cap;
+  kp.heads = heads;
+  kp.row_bytes = row_bytes;
+  kp.past_len = past_len;
+  kp.accepted = accepted_nodes;
+  kp.accept_len = accept_len;
+  kp.L = L;
+  kp.new_len = new_len;
+  hipLaunchKernelGGL(ddt::kv_compact_kernel, dim3((unsigned)blocks), dim3(ddt::kKvThreads), 0,
+                     stream, kp);
   return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
 }
 

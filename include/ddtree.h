@@ -165,6 +165,30 @@ int ddtree_accept(const int32_t* tree_tokens, const int32_t* parents, const int3
                   hipStream_t stream);
 
 /*
+ * ddtree_compact_kv -- KV-cache compaction to the accepted path (DDTree
+ * explainer, section 5, "KV cache management": after each round only the
+ * accepted path's cache is kept). The verification pass wrote the rows of
+ * the root (the bonus token) and of nodes 1..B at positions past_len[b] + j.
+ * For every layer and KV head, rows past_len[b] + i, i = 1..accept_len[b],
+ * take the rows at past_len[b] + accepted_nodes[b][i-1]; every other row is
+ * left as it was. In place; the caches are not reallocated.
+ * k_cache, v_cache [layers][batch][heads][cap][row_bytes] (row_bytes = head
+ *                  dim x element size; any element type, copied bit for bit),
+ *                  16-byte aligned;
+ * past_len       [batch] int32: cache length before the verified block;
+ * accepted_nodes [batch][L], accept_len [batch]: as written by ddtree_accept
+ *                (node numbers increase along the path, a_i >= i);
+ * new_len        [batch] int32 output (nullable): past_len + accept_len + 1.
+ * Supported: row_bytes a multiple of 16 and <= 1024, 1 <= L <= DDT_MAX_L;
+ * otherwise DDT_ENOTSUP. Device contents are not validated beyond skipping
+ * rows whose source or destination falls outside [0, cap).
+ */
+int ddtree_compact_kv(void* k_cache, void* v_cache, int64_t layers, int64_t batch,
+                      int32_t heads, int64_t cap, int32_t row_bytes, const int32_t* past_len,
+                      const int32_t* accepted_nodes, const int32_t* accept_len, int32_t L,
+                      int32_t* new_len, hipStream_t stream);
+
+/*
  * ddtree_row_topk -- stage 1 alone over `rows` independent rows of length V
  * (logits as in ddtree_build: 16-byte aligned, finite).
  * ids  [rows][K] int32 and vals [rows][K] float: the K largest logits of each

@@ -32,6 +32,7 @@ def declared_functions():
 def test_header_declares_the_four_operations():
     names = declared_functions()
     for n in ("ddtree_build", "ddtree_select", "ddtree_mask", "ddtree_accept", "ddtree_row_topk",
+              "ddtree_compact_kv",
               "ddtree_build_workspace_size", "ddtree_row_topk_workspace_size",
               "ddt_status_string", "ddt_abi_version"):
         assert n in names
@@ -133,3 +134,21 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _lib.lib()
+
+
+def test_compact_kv_validation(L):
+    """Rejected before any launch (the pointers below are never dereferenced)."""
+    f = L.ddtree_compact_kv
+    f.restype = C.c_int
+    f.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_int32, C.c_int64, C.c_int32,
+                  C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p]
+    def call(k=FAKE, layers=2, batch=3, heads=4, cap=100, row=256, Lw=15, past=FAKE):
+        return f(k, FAKE, layers, batch, heads, cap, row, past, FAKE, FAKE, Lw, FAKE, None)
+    assert call(row=100) == -2            # not a multiple of 16 bytes
+    assert call(row=2048) == -2           # more than 1 KiB per row
+    assert call(Lw=33) == -2              # deeper than DDT_MAX_L
+    assert call(Lw=0) == -1
+    assert call(cap=0) == -1
+    assert call(k=MISALIGNED) == -1
+    assert call(past=None) == -1
+    assert call(layers=0) == 0            # nothing to do
