@@ -131,6 +131,75 @@ def treespark_bench(args) -> int:
     return 0
 
 
+# Verifier cache of the KV-compaction workload: Qwen3-8B's attention shape
+# (36 layers, 8 KV heads, head dim 128, bf16), 1024 tokens of context.
+KV_LAYERS, KV_HEADS, KV_DH, KV_PAST = 36, 8, 128, 1024
+
+
+def kv_bench(args) -> int:
+    """KV-cache compaction after a batch-64 round: the trees and accepted paths
+    of the batch-64 workload, a verifier cache of the shape above; one step =
+    one ddtree_compact_kv call (in place)."""
+    import numpy as np
+    import torch
+
+    import draft_tree_construction_depth_amd as pkg
+    from draft_tree_construction_depth_amd import gen
+
+    c = gen.CONFIGS[3]
+    batch, L, B = c["batch"], c["L"], c["B"]
+    dev = torch.device("cuda:0")
+    x = gen.make_logits(3, 0)
+    Y = gen.drafter_draws(3, 0, x, c["dtype"])
+    xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    tree = pkg.ddtree_build(xd, B)
+    torch.cuda.synchronize()
+    tgt = gen.node_targets_from_depths(Y, tree["depths"].cpu().numpy(),
+                                       tree["num_nodes"].cpu().numpy(), B)
+    acc = pkg.ddtree_accept(tree["tree_tokens"], tree["parents"], tree["num_nodes"],
+                            torch.from_numpy(tgt).to(dev), L)
+    cap = KV_PAST + B + 1
+    shape = (KV_LAYERS, batch, KV_HEADS, cap, KV_DH)
+    kc = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    vc = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    past = torch.full((batch,), KV_PAST, dtype=torch.int32, device=dev)
+    new_len = torch.empty((batch,), dtype=torch.int32, device=dev)
+    an, al = acc["accepted_nodes"], acc["accept_len"]
+    for _ in range(args.warmup):
+        pkg.ddtree_compact_kv(kc, vc, past, an, al, new_len)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(args.steps):
+        pkg.ddtree_compact_kv(kc, vc, past, an, al, new_len)
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = a.elapsed_time(b) * 1e3 / args.steps
+    moved = int(al.sum().item())
+    row_bytes = KV_DH * 2
+    alg_bytes = moved * KV_LAYERS * KV_HEADS * 2 * row_bytes * 2  # K and V rows, read + write
+    gbps = alg_bytes / (us / 1e6) / 1e9
+    res = {
+        "metric": "KV-cache compaction time per round at batch 64 (accepted paths of the "
+                  "batch-64 draft-tree workload)",
+        "value": round(us, 2), "unit": "us", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (bit copy)", "data": "synthetic",
+        "config": {"workload": "kv_compact_batch64_layers36_kvheads8_dh128_past1024",
+                   "batch": batch, "layers": KV_LAYERS, "kv_heads": KV_HEADS, "head_dim": KV_DH,
+                   "past": KV_PAST, "cap": cap, "accepted_rows": moved},
+        "roofline": {"bound": "hbm", "kernel": "kv_compact_kernel", "achieved": round(gbps, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "avg_launch_us": round(us, 2), "bytes_per_launch": alg_bytes,
+                     "traffic": None},
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +209,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--treespark", action="store_true",
                     help="time treespark_expand on the TreeSpark workload instead (own JSON line)")
+    ap.add_argument("--kv-compact", action="store_true",
+                    help="time ddtree_compact_kv after a batch-64 round instead (own JSON line)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 3 device-to-device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -169,6 +240,8 @@ def main() -> int:
 
     if args.treespark:
         return treespark_bench(args)
+    if args.kv_compact:
+        return kv_bench(args)
 
     c = gen.CONFIGS[3]
     batch, L, V, B = c["batch"], c["L"], c["V"], c["B"]
