@@ -208,3 +208,42 @@ def treespark_inputs(seed: int = 0, *, batch: int | None = None, first: int = 0,
     E = treespark_matrix(seed, 3, V=V, H=H, wscale=wscale)
     anchor = np.array([treespark_anchor(seed, first + b, V=V) for b in range(batch)], dtype=np.int32)
     return bb, W, E, anchor
+
+
+# SparklingTree (SparklingTree post): the batch-64 drafter rows, a top-C
+# pre-filter of C = 128 and a node budget of 64 (the post's reported setting),
+# and a first-order Markov head in low-rank form: delta(p, v) = W1[p] . W2t[v]
+# with rank R = 256 (extraction W1 and projection W2, the latter stored
+# transposed). No trained head exists here: the factors are random with
+# std(delta) ~ 0.5, a bias small beside the logits' spread.
+SPARKLING = dict(batch=64, L=15, V=151936, B=64, C=128, R=256, wscale=0.177)
+CFG_SPARKLING = 6
+
+
+def sparkling_factor(seed: int, which: int, *, V: int, R: int, wscale: float) -> np.ndarray:
+    """W1 (which = 1) or W2t (which = 2): [V, R] bf16 bits, N(0, wscale^2)."""
+    assert which in (1, 2)
+    rng = _rng(CFG_SPARKLING, seed, 0, stream=which)
+    out = np.empty((V, R), dtype=np.uint16)
+    step = 16384
+    for r0 in range(0, V, step):
+        r1 = min(V, r0 + step)
+        out[r0:r1] = f32_to_bf16_bits(
+            (rng.standard_normal((r1 - r0, R), dtype=np.float32) * np.float32(wscale)).astype(np.float32))
+    return out
+
+
+def sparkling_inputs(seed: int = 0, *, batch: int | None = None, first: int = 0, L: int | None = None,
+                     V: int | None = None, R: int | None = None, wscale: float | None = None):
+    """(logits [batch, L, V] bf16 bits (the batch-64 workload's rows), W1 [V, R], W2t [V, R] bf16 bits)."""
+    c = SPARKLING
+    batch = c["batch"] if batch is None else batch
+    L = c["L"] if L is None else L
+    V = c["V"] if V is None else V
+    R = c["R"] if R is None else R
+    wscale = c["wscale"] if wscale is None else wscale
+    c3 = CONFIGS[3]
+    x = np.stack([request_rows(CFG_SPARKLING, seed, first + b, L=L, V=V, sigma=c3["sigma"],
+                               peak=c3["peak"], dtype=c3["dtype"]) for b in range(batch)])
+    return x, sparkling_factor(seed, 1, V=V, R=R, wscale=wscale), sparkling_factor(seed, 2, V=V, R=R,
+                                                                                 wscale=wscale)
