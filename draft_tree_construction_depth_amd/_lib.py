@@ -61,6 +61,11 @@ def lib() -> C.CDLL:
         L.treespark_expand.restype = C.c_int
         L.treespark_expand.argtypes = [p, p, p, p, i64, i32, i64, i32, i32, i32, i32, p, p, p, p,
                                        p, p, sz, p]
+        L.sparkling_build_workspace_size.restype = sz
+        L.sparkling_build_workspace_size.argtypes = [i64, i32, i64, i32, i32, i32, C.c_int]
+        L.sparkling_build.restype = C.c_int
+        L.sparkling_build.argtypes = [p, C.c_int, p, p, i64, i32, i64, i32, i32, i32, p, p, p, p,
+                                      p, p, p, sz, p]
         _lib = L
     return _lib
 
@@ -289,4 +294,33 @@ def treespark_expand(backbone: torch.Tensor, W: torch.Tensor, E: torch.Tensor,
                                 _ptr(out["logq"]), _ptr(out.get("depths")),
                                 _ptr(out["num_nodes"]), _ptr(ws), ws.numel(), _stream(dev))
     _check("treespark_expand", rc)
+    return out
+
+
+def sparkling_build(logits: torch.Tensor, W1: torch.Tensor, W2t: torch.Tensor, B: int, *,
+                    C: int = 128, with_mask: bool = True, out: dict | None = None,
+                    ws: torch.Tensor | None = None) -> dict:
+    """SparklingTree: logits [batch, L, V] (bf16/f32), Markov head W1 / W2t [V, R] (bf16)
+    -> tree tensors (as ddtree_build)."""
+    _arg(logits, "logits", _LOGITS)
+    if logits.dim() != 3:
+        raise ValueError("logits must be [batch, L, V]")
+    batch, L, V = logits.shape
+    _arg(W1, "W1", _BF16)
+    if W1.dim() != 2 or W1.shape[0] != V:
+        raise ValueError(f"W1 must be [{V}, R]")
+    R = W1.shape[1]
+    _arg(W2t, "W2t", _BF16, (V, R))
+    dev = logits.device
+    dt = _dtype_code(logits)
+    if out is None:
+        out = _tree_out(batch, B, dev, with_mask)
+    size = lib().sparkling_build_workspace_size(batch, L, V, C, R, B, dt)
+    if ws is None:
+        ws = workspace("sparkling", size, dev, (batch, L, V, C, R, B, dt))
+    rc = lib().sparkling_build(_ptr(logits), dt, _ptr(W1), _ptr(W2t), batch, L, V, C, R, B,
+                               _ptr(out["tree_tokens"]), _ptr(out["parents"]), _ptr(out["logq"]),
+                               _ptr(out.get("depths")), _ptr(out["num_nodes"]),
+                               _ptr(out.get("mask")), _ptr(ws), ws.numel(), _stream(dev))
+    _check("sparkling_build", rc)
     return out

@@ -9,6 +9,7 @@
 #include "treespark.hpp"
 #include "walk.hpp"
 #include "kv.hpp"
+#include "sparkling.hpp"
 
 namespace {
 
@@ -214,6 +215,9 @@ int launch_select(const float* vals, const int32_t* ids, const double* lse, int6
   sp.num_nodes = num_nodes;
   sp.mask = mask;
   sp.W = (B + 1 + 63) / 64;
+  sp.sp_lp = nullptr;
+  sp.sp_best = nullptr;
+  sp.sp_blp = nullptr;
   hipLaunchKernelGGL(ddt::select_kernel, dim3((unsigned)batch), dim3(ddt::kSelThreads), 0, stream,
                      sp);
   return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
@@ -287,6 +291,46 @@ int ts_check(int64_t batch, int32_t D, int64_t V, int32_t H, int32_t k, int32_t 
       V > 0x7FFFFFFFLL || N > 4096 || batch > 0x7FFFFFFFLL / ddt::kTsFMax ||
       V * (int64_t)H * 2 > 0xFFFFFFFFLL)  // byte offsets into E are 32-bit
     return DDT_ENOTSUP;
+  return DDT_OK;
+}
+
+// ---- SparklingTree: workspace layout ---------------------------------------
+struct SpLayout {
+  S1Layout s1;
+  size_t vals, ids, lse, lp, best, blp, end;
+};
+
+SpLayout sp_layout(int64_t batch, int32_t L, int64_t V, int32_t C, int dtype) {
+  const int64_t rows = batch * L;
+  SpLayout l;
+  l.s1 = s1_layout(rows, plan_stage1(rows, V, dtype, C), 0);
+  size_t off = l.s1.end;
+  l.vals = off;
+  off = align_up(off + (size_t)rows * C * sizeof(float));
+  l.ids = off;
+  off = align_up(off + (size_t)rows * C * sizeof(int32_t));
+  l.lse = off;
+  off = align_up(off + (size_t)rows * sizeof(double));
+  const size_t prow = (size_t)batch * (L - 1) * C;  // conditioned rows
+  l.lp = off;
+  off = align_up(off + prow * C * sizeof(float));
+  l.best = off;
+  off = align_up(off + prow * sizeof(uint8_t));
+  l.blp = off;
+  off = align_up(off + prow * sizeof(float));
+  l.end = off;
+  return l;
+}
+
+int sp_check(int dtype, int64_t batch, int32_t L, int64_t V, int32_t C, int32_t R, int32_t B) {
+  if (!valid_dtype(dtype) || batch < 0 || L <= 0 || V <= 0 || C <= 0 || R <= 0 || B <= 0)
+    return DDT_EINVAL;
+  if (C > V) return DDT_EINVAL;
+  if (C > ddt::kSpC || R % ddt::kSpKT != 0 || R > ddt::kSpRMax) return DDT_ENOTSUP;
+  if (B > DDT_MAX_B || L > DDT_MAX_L || V > 0x7FFFFFFFLL || batch > 0x7FFFFFFFLL)
+    return DDT_ENOTSUP;
+  const int bpd = ceil_log2(C) < 1 ? 1 : ceil_log2(C);
+  if (L * bpd > 122) return DDT_ENOTSUP;
   return DDT_OK;
 }
 
@@ -553,6 +597,82 @@ int treespark_expand(const void* backbone, const void* W, const void* E, const i
   pp.num_nodes = num_nodes;
   hipLaunchKernelGGL(ddt::ts_pack_kernel, dim3((unsigned)batch), dim3(ddt::kTsThreads),
                      (size_t)sh.cmax * 4, stream, pp);
+  return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
+}
+
+size_t sparkling_build_workspace_size(int64_t batch, int32_t L, int64_t V, int32_t C,
+                                      int32_t R, int32_t B, int dtype) {
+  if (batch <= 0 || sp_check(dtype, batch, L, V, C, R, B) != DDT_OK) return 0;
+  if (!plan_stage1(batch * L, V, dtype, C).ok) return 0;
+  return sp_layout(batch, L, V, C, dtype).end;
+}
+
+int sparkling_build(const void* logits, int dtype, const uint16_t* W1, const uint16_t* W2t,
+                    int64_t batch, int32_t L, int64_t V, int32_t C, int32_t R, int32_t B,
+                    int32_t* tree_tokens, int32_t* parents, float* logq, int32_t* depths,
+                    int32_t* num_nodes, uint64_t* mask, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  const int chk = sp_check(dtype, batch, L, V, C, R, B);
+  if (chk != DDT_OK) return chk;
+  if (batch == 0) return DDT_OK;
+  if (!logits || !W1 || !W2t || !tree_tokens || !parents || !logq || !num_nodes || !workspace)
+    return DDT_EINVAL;
+  if ((uintptr_t)logits % 16 != 0 || (uintptr_t)W1 % 16 != 0 || (uintptr_t)W2t % 16 != 0)
+    return DDT_EINVAL;
+  const int64_t rows = batch * L;
+  const S1Plan pl = plan_stage1(rows, V, dtype, C);
+  if (!pl.ok || rows * pl.S > 0x7FFFFFFFLL) return DDT_ENOTSUP;
+  const SpLayout lay = sp_layout(batch, L, V, C, dtype);
+  if (workspace_bytes < lay.end) return DDT_EWORKSPACE;
+  char* ws = (char*)workspace;
+  float* tv = (float*)(ws + lay.vals);
+  int32_t* ti = (int32_t*)(ws + lay.ids);
+  double* tz = (double*)(ws + lay.lse);
+  float* lp = (float*)(ws + lay.lp);
+  uint8_t* best = (uint8_t*)(ws + lay.best);
+  float* blp = (float*)(ws + lay.blp);
+  // 1. every drafter row cut to its top C (value desc, id asc)
+  hipError_t e = launch_stage1(dtype, pl, logits, rows, V, C, lay.s1, ws, ti, tv, tz, stream);
+  if (e != hipSuccess) return DDT_EHIP;
+  // 2. the conditioned child rows: Markov deltas on MFMA, log-probs, best child
+  if (L > 1) {
+    ddt::SpTableParams tp;
+    tp.W1 = W1;
+    tp.W2t = W2t;
+    tp.ids = ti;
+    tp.vals = tv;
+    tp.L = L;
+    tp.C = C;
+    tp.R = R;
+    tp.lp = lp;
+    tp.best = best;
+    tp.blp = blp;
+    hipLaunchKernelGGL(ddt::sp_table_kernel, dim3((unsigned)batch, (unsigned)(L - 1)),
+                       dim3(ddt::kSpThreads), 0, stream, tp);
+    if (hipGetLastError() != hipSuccess) return DDT_EHIP;
+  }
+  // 3. best-first selection on the conditioned rows, then the mask
+  ddt::SelectParams sp;
+  sp.vals = tv;
+  sp.ids = ti;
+  sp.lse = tz;
+  sp.batch = batch;
+  sp.L = L;
+  sp.K = C;
+  sp.B = B;
+  sp.bpd = ceil_log2(C) < 1 ? 1 : ceil_log2(C);
+  sp.tree_tokens = tree_tokens;
+  sp.parents = parents;
+  sp.logq = logq;
+  sp.depths = depths;
+  sp.num_nodes = num_nodes;
+  sp.mask = mask;
+  sp.W = (B + 1 + 63) / 64;
+  sp.sp_lp = lp;
+  sp.sp_best = best;
+  sp.sp_blp = blp;
+  hipLaunchKernelGGL(ddt::sp_select_kernel, dim3((unsigned)batch), dim3(ddt::kSelThreads), 0,
+                     stream, sp);
   return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
 }
 

@@ -69,6 +69,10 @@ struct SelectParams {
   int32_t* num_nodes;
   uint64_t* mask;  // may be null; [batch][B+1][W]
   int32_t W;
+  // conditioned rows (SparklingTree; null for independent rows)
+  const float* sp_lp;      // [batch][L-1][K][K] child row d, parent candidate, child candidate
+  const uint8_t* sp_best;  // [batch][L-1][K] each row's best child
+  const float* sp_blp;     // [batch][L-1][K] its log-prob
 };
 
 struct SelEnum {
@@ -92,6 +96,8 @@ struct SelHeap {
   uint8_t dep[kHeapCap];
   uint16_t ranks[kHeapCap][kMaxL];
   uint16_t heap[kHeapCap];  // heap of pool indices
+  uint8_t cand[kHeapCap];   // conditioned rows: the entry's candidate index
+  uint8_t pcand[kHeapCap];  // and its parent's (the row its siblings come from)
   // emitted nodes
   int16_t out_e[kMaxB];
 };
@@ -233,18 +239,15 @@ __device__ void heap_fallback(const SelectParams& p, SelectSmem& sm, int64_t b) 
 // a bin); one scan finds the bin holding the B-th, whose few members are
 // ranked exactly. Members beyond kMergeCap (flat rows) return mn instead, a
 // valid lower bound.
-__device__ double sel_tau_hist(SelectSmem& sm, int L, int K, int B) {
+// onedev(i) gives the i-th of the LK scores; lane_bound(lane) a per-lane
+// value whose minimum over wave 0 is a lower bound with >= B scores at or
+// above it.
+template <class OD, class LB>
+__device__ double sel_tau_hist(SelectSmem& sm, int LK, int B, OD onedev, LB lane_bound) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int LK = L * K;
-  auto onedev = [&](int i) -> double {
-    const int d = i / K;
-    const double raw = (sm.P0[d] + (double)sm.v[i]) - sm.Z[d];
-    return raw > sm.sig[d] ? sm.sig[d] : raw;
-  };
-  const int q = (B + L - 1) / L < K ? (B + L - 1) / L : K;
   sm.hist[tid] = 0;
   if (w == 0) {
-    double x = lane < L ? onedev(lane * K + q - 1) : INFINITY;
+    double x = lane_bound(lane);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const double y = __shfl_xor(x, o);
@@ -307,6 +310,159 @@ __device__ double sel_tau_hist(SelectSmem& sm, int L, int K, int B) {
 }
 
 // ---------------------------------------------------------------------------
+// Phase 3 (after an enumeration without overflow): order E, emit the
+// first B (tokens, parents, log-probs, depths, node count). en.eRank holds
+// each entry's index into its row's candidate table.
+__device__ __forceinline__ void sel_order_emit(const SelectParams& p, SelectSmem& sm, int64_t b,
+                                               double tau) {
+  SelEnum& en = sm.u.en;
+  const int tid = threadIdx.x;
+  const int L = p.L, K = p.K, B = p.B, LK = L * K;
+  (void)L;
+  // ---- 3. order E, emit the first B ----------------------------------------
+  // E's scores fall into kSelThreads bins over [tau, best] (bin index
+  // monotone in the score, so equal scores share a bin and a lower bin
+  // holds only better scores). E2 = the entries of the first bins that
+  // hold >= B of them (all of E when nE <= B); it is closed upwards in the
+  // order, so it holds the output. E2 is placed in bin order, and an
+  // entry's position is its bin's offset plus the members of its own bin
+  // before it (score, then the 128-bit lexicographic rank key).
+  const int nE = sm.nE;
+  static_assert(kECap <= 2 * kSelThreads, "two entries per thread at most");
+  const double top = sm.sig[1];  // the best prefix: depth 1, rank 0
+  const double span = top - tau;
+  const double scale = span > 0.0 ? (double)kSelThreads / span : 0.0;
+  auto bin_of = [&](double sc) -> int {
+    const double t = (top - sc) * scale;
+    return t >= (double)(kSelThreads - 1) ? kSelThreads - 1 : (t > 0.0 ? (int)t : 0);
+  };
+  sm.hist[tid] = 0;
+  __syncthreads();
+  int ebin[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = tid + k * kSelThreads;
+    ebin[k] = i < nE ? bin_of(en.eSc[i]) : kSelThreads;
+    if (i < nE) atomicAdd(&sm.hist[ebin[k]], 1);
+  }
+  __syncthreads();
+  {
+    const int h = sm.hist[tid];
+    const int x = wave_incl_scan(h);
+    const int lane = tid & 63, w = tid >> 6;
+    if (lane == kWave - 1) sm.wsum[w] = x;
+    __syncthreads();
+    int pre = 0;
+    for (int q = 0; q < w; ++q) pre += sm.wsum[q];
+    const int inc = pre + x, exc = inc - h;
+    // the first bin reaching B is the cut (the last bin when nE <= B)
+    if (nE > B ? (inc >= B && exc < B) : tid == kSelThreads - 1) {
+      sm.kcut = tid;
+      sm.n2 = inc;
+    }
+    sm.hexc[tid] = exc;
+    sm.hist[tid] = 0;  // now the bins' fill counters (only this thread read it)
+  }
+  __syncthreads();
+  const int kcut = sm.kcut, n2 = sm.n2;
+  // E2 in bin order, with compact copies of the order keys: scores in eS,
+  // rank keys in the (dead) table of row values
+  double* s2 = en.eS;
+  uint64_t* h2 = (uint64_t*)sm.v;
+  uint64_t* l2 = h2 + kECap;
+  static_assert(2 * kECap * sizeof(uint64_t) <= sizeof(sm.v), "rank keys fit the row table");
+  int epos[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = tid + k * kSelThreads;
+    epos[k] = -1;
+    if (i < nE && ebin[k] <= kcut) {
+      const int q = sm.hexc[ebin[k]] + atomicAdd(&sm.hist[ebin[k]], 1);
+      epos[k] = q;
+      en.ord[q] = (uint16_t)i;
+      s2[q] = en.eSc[i];
+      h2[q] = en.eLh[i];
+      l2[q] = en.eLl[i];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = tid + k * kSelThreads;
+    if (epos[k] >= 0) {
+      const int bb = ebin[k], me = epos[k];
+      const int lo = sm.hexc[bb], hi = bb + 1 < kSelThreads ? sm.hexc[bb + 1] : nE;
+      const double si = s2[me];
+      const uint64_t hi_i = h2[me], lo_i = l2[me];
+      int rank = lo;
+      for (int q = lo; q < hi; ++q) {
+        const double sq = s2[q];
+        const uint64_t hq = h2[q], lq = l2[q];
+        rank += (sq > si || (sq == si && (hq < hi_i || (hq == hi_i && lq < lo_i)))) ? 1 : 0;
+      }
+      en.cnt[i] = rank;
+    }
+  }
+  __syncthreads();
+  const int nsel = nE < B ? nE : B;
+  for (int k = tid; k < n2; k += kSelThreads) {
+    const int i = en.ord[k];
+    const int j = en.cnt[i];
+    if (j < nsel) {
+      const size_t o = (size_t)b * B + j;
+      const int d = en.eDep[i], r = en.eRank[i], pe = en.ePar[i];
+      const int par = pe < 0 ? 0 : en.cnt[pe] + 1;
+      p.tree_tokens[o] = p.ids[(size_t)b * LK + (size_t)(d - 1) * K + r];
+      p.parents[o] = par;
+      p.logq[o] = (float)en.eSc[i];
+      if (p.depths) p.depths[o] = d;
+      sm.opar[j] = par;
+    }
+  }
+  for (int j = nsel + tid; j < B; j += kSelThreads) {
+    const size_t o = (size_t)b * B + j;
+    p.tree_tokens[o] = -1;
+    p.parents[o] = -1;
+    p.logq[o] = -INFINITY;
+    if (p.depths) p.depths[o] = 0;
+  }
+  if (tid == 0) {
+    p.num_nodes[b] = nsel;
+    sm.nsel = nsel;
+  }
+  __syncthreads();
+}
+
+// Phase 4: the bit-packed ancestor mask from the emitted parents.
+__device__ __forceinline__ void sel_mask(const SelectParams& p, SelectSmem& sm, int64_t b) {
+  const int tid = threadIdx.x;
+  const int B = p.B;
+  // ---- 4. ancestor mask ------------------------------------------------------
+  if (p.mask) {
+    const int nsel = sm.nsel, W = p.W;
+    for (int i = tid; i <= B; i += kSelThreads) {
+      uint64_t m[kMaxW];
+#pragma unroll
+      for (int q = 0; q < kMaxW; ++q) m[q] = 0;
+      if (i <= nsel) {
+        int u = i;
+        for (int step = 0; step <= kMaxL + 1; ++step) {
+          const int wq = u >> 6;
+          const uint64_t bit = 1ull << (u & 63);
+#pragma unroll
+          for (int q = 0; q < kMaxW; ++q) m[q] |= (q == wq) ? bit : 0ull;
+          if (u == 0) break;
+          u = sm.opar[u - 1];
+        }
+      }
+      uint64_t* dst = p.mask + ((size_t)b * (B + 1) + i) * W;
+#pragma unroll
+      for (int q = 0; q < kMaxW; ++q)
+        if (q < W) dst[q] = m[q];
+    }
+  }
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   __shared__ SelectSmem sm;
   SelEnum& en = sm.u.en;
@@ -339,7 +495,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
 
   // ---- 1. threshold from the one-deviation prefixes -------------------------
   double tau = -INFINITY;
-  if (LK >= B) tau = sel_tau_hist(sm, L, K, B);
+  if (LK >= B) {
+    // rows' one-deviation scores; lower bound: the q-th of every row,
+    // q = min(ceil(B / L), K), leaves >= B scores at or above the smallest
+    auto onedev = [&](int i) -> double {
+      const int d = i / K;
+      const double raw = (sm.P0[d] + (double)sm.v[i]) - sm.Z[d];
+      return raw > sm.sig[d] ? sm.sig[d] : raw;
+    };
+    const int q = (B + L - 1) / L < K ? (B + L - 1) / L : K;
+    tau = sel_tau_hist(sm, LK, B, onedev,
+                       [&](int lane) { return lane < L ? onedev(lane * K + q - 1) : INFINITY; });
+  }
 
   // ---- 2. enumerate E = {score >= tau} by chains ----------------------------
   int D0 = 0;
@@ -500,144 +667,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     if (tid == 0) heap_fallback(p, sm, b);
     __syncthreads();
   } else {
-    // ---- 3. order E, emit the first B ----------------------------------------
-    // E's scores fall into kSelThreads bins over [tau, best] (bin index
-    // monotone in the score, so equal scores share a bin and a lower bin
-    // holds only better scores). E2 = the entries of the first bins that
-    // hold >= B of them (all of E when nE <= B); it is closed upwards in the
-    // order, so it holds the output. E2 is placed in bin order, and an
-    // entry's position is its bin's offset plus the members of its own bin
-    // before it (score, then the 128-bit lexicographic rank key).
-    const int nE = sm.nE;
-    static_assert(kECap <= 2 * kSelThreads, "two entries per thread at most");
-    const double top = sm.sig[1];  // the best prefix: depth 1, rank 0
-    const double span = top - tau;
-    const double scale = span > 0.0 ? (double)kSelThreads / span : 0.0;
-    auto bin_of = [&](double sc) -> int {
-      const double t = (top - sc) * scale;
-      return t >= (double)(kSelThreads - 1) ? kSelThreads - 1 : (t > 0.0 ? (int)t : 0);
-    };
-    sm.hist[tid] = 0;
-    __syncthreads();
-    int ebin[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int i = tid + k * kSelThreads;
-      ebin[k] = i < nE ? bin_of(en.eSc[i]) : kSelThreads;
-      if (i < nE) atomicAdd(&sm.hist[ebin[k]], 1);
-    }
-    __syncthreads();
-    {
-      const int h = sm.hist[tid];
-      const int x = wave_incl_scan(h);
-      const int lane = tid & 63, w = tid >> 6;
-      if (lane == kWave - 1) sm.wsum[w] = x;
-      __syncthreads();
-      int pre = 0;
-      for (int q = 0; q < w; ++q) pre += sm.wsum[q];
-      const int inc = pre + x, exc = inc - h;
-      // the first bin reaching B is the cut (the last bin when nE <= B)
-      if (nE > B ? (inc >= B && exc < B) : tid == kSelThreads - 1) {
-        sm.kcut = tid;
-        sm.n2 = inc;
-      }
-      sm.hexc[tid] = exc;
-      sm.hist[tid] = 0;  // now the bins' fill counters (only this thread read it)
-    }
-    __syncthreads();
-    const int kcut = sm.kcut, n2 = sm.n2;
-    // E2 in bin order, with compact copies of the order keys: scores in eS,
-    // rank keys in the (dead) table of row values
-    double* s2 = en.eS;
-    uint64_t* h2 = (uint64_t*)sm.v;
-    uint64_t* l2 = h2 + kECap;
-    static_assert(2 * kECap * sizeof(uint64_t) <= sizeof(sm.v), "rank keys fit the row table");
-    int epos[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int i = tid + k * kSelThreads;
-      epos[k] = -1;
-      if (i < nE && ebin[k] <= kcut) {
-        const int q = sm.hexc[ebin[k]] + atomicAdd(&sm.hist[ebin[k]], 1);
-        epos[k] = q;
-        en.ord[q] = (uint16_t)i;
-        s2[q] = en.eSc[i];
-        h2[q] = en.eLh[i];
-        l2[q] = en.eLl[i];
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int i = tid + k * kSelThreads;
-      if (epos[k] >= 0) {
-        const int bb = ebin[k], me = epos[k];
-        const int lo = sm.hexc[bb], hi = bb + 1 < kSelThreads ? sm.hexc[bb + 1] : nE;
-        const double si = s2[me];
-        const uint64_t hi_i = h2[me], lo_i = l2[me];
-        int rank = lo;
-        for (int q = lo; q < hi; ++q) {
-          const double sq = s2[q];
-          const uint64_t hq = h2[q], lq = l2[q];
-          rank += (sq > si || (sq == si && (hq < hi_i || (hq == hi_i && lq < lo_i)))) ? 1 : 0;
-        }
-        en.cnt[i] = rank;
-      }
-    }
-    __syncthreads();
-    const int nsel = nE < B ? nE : B;
-    for (int k = tid; k < n2; k += kSelThreads) {
-      const int i = en.ord[k];
-      const int j = en.cnt[i];
-      if (j < nsel) {
-        const size_t o = (size_t)b * B + j;
-        const int d = en.eDep[i], r = en.eRank[i], pe = en.ePar[i];
-        const int par = pe < 0 ? 0 : en.cnt[pe] + 1;
-        p.tree_tokens[o] = p.ids[(size_t)b * LK + (size_t)(d - 1) * K + r];
-        p.parents[o] = par;
-        p.logq[o] = (float)en.eSc[i];
-        if (p.depths) p.depths[o] = d;
-        sm.opar[j] = par;
-      }
-    }
-    for (int j = nsel + tid; j < B; j += kSelThreads) {
-      const size_t o = (size_t)b * B + j;
-      p.tree_tokens[o] = -1;
-      p.parents[o] = -1;
-      p.logq[o] = -INFINITY;
-      if (p.depths) p.depths[o] = 0;
-    }
-    if (tid == 0) {
-      p.num_nodes[b] = nsel;
-      sm.nsel = nsel;
-    }
-    __syncthreads();
+    sel_order_emit(p, sm, b, tau);
   }
-
-  // ---- 4. ancestor mask ------------------------------------------------------
-  if (p.mask) {
-    const int nsel = sm.nsel, W = p.W;
-    for (int i = tid; i <= B; i += kSelThreads) {
-      uint64_t m[kMaxW];
-#pragma unroll
-      for (int q = 0; q < kMaxW; ++q) m[q] = 0;
-      if (i <= nsel) {
-        int u = i;
-        for (int step = 0; step <= kMaxL + 1; ++step) {
-          const int wq = u >> 6;
-          const uint64_t bit = 1ull << (u & 63);
-#pragma unroll
-          for (int q = 0; q < kMaxW; ++q) m[q] |= (q == wq) ? bit : 0ull;
-          if (u == 0) break;
-          u = sm.opar[u - 1];
-        }
-      }
-      uint64_t* dst = p.mask + ((size_t)b * (B + 1) + i) * W;
-#pragma unroll
-      for (int q = 0; q < kMaxW; ++q)
-        if (q < W) dst[q] = m[q];
-    }
-  }
+  sel_mask(p, sm, b);
 }
 
 }  // namespace ddt

@@ -1,0 +1,560 @@
+// SparklingTree: conditioned best-first tree from a diffusion drafter's rows
+// and a first-order Markov head.
+//
+// SparklingTree post, "Building SparklingTree" and "Solving the candidate
+// tree construction": every drafter row is cut to its top C tokens on the
+// device; a low-rank Markov head biases row d by the token chosen at depth
+// d-1, delta(p, v) = W1[p] . W2[:, v] (extraction W1 [V][R], projection W2
+// [R][V], held transposed as W2t [V][R]); because the head looks back one
+// token, the whole table of deltas between consecutive rows' candidates is
+// computed up front, and the tree grows best first on conditioned rows.
+// Readings (the post leaves them open): depth 1 is not conditioned; a row's
+// log-probs are normalised over its C candidates; ties inside a row go to
+// the lower token id, prefixes order by (score desc, rank tuple asc).
+//
+// sp_table_kernel: per request and child row d >= 1, one workgroup forms
+//   delta[i][j] = W1[c_{d-1}[i]] . W2t[c_d[j]] for all C x C candidate pairs
+//   on MFMA (32x32x16 bf16, float32 accumulate; the C child rows of W2t are
+//   staged in LDS, each wave holds 32 parent rows of W1 in registers), then
+//   per parent row i: s_j = x_d[c_j] + delta[i][j], lp_j = s_j - logsumexp(s)
+//   and the row's best child (lp desc, token asc). Rows stay in candidate
+//   order: the selection counts, ranks and walks them without sorting.
+// The selection itself is sp_select_kernel, below.
+#pragma once
+
+#include "common.hpp"
+#include "select.hpp"
+#include "treespark.hpp"  // MFMA fragment types
+
+namespace ddt {
+
+constexpr int kSpThreads = 256;
+constexpr int kSpC = 128;     // candidates per row, at most (MFMA tiles of 32)
+constexpr int kSpRMax = 256;  // Markov rank, at most (four k-steps of 64 in registers)
+constexpr int kSpKT = 64;
+
+struct SpTableParams {
+  const uint16_t* W1;   // [V][R] bf16
+  const uint16_t* W2t;  // [V][R] bf16
+  const int32_t* ids;   // [batch][L][C] each row's candidate tokens (value desc, id asc)
+  const float* vals;    // [batch][L][C] their logits
+  int32_t L, C, R;
+  float* lp;            // [batch][L-1][C][C]: child row d, parent candidate i, child candidate j
+  uint8_t* best;        // [batch][L-1][C]: the best child j of each parent row
+  float* blp;           // [batch][L-1][C]: its log-prob
+};
+
+struct SpTableSmem {
+  uint16_t w2[kSpC][kSpRMax + 8];  // the child candidates' W2t rows (row pitch padded)
+  float vals[kSpC];
+  int32_t tok[kSpC];
+};
+
+__device__ __forceinline__ bool sp_better(float a, int ta, float b, int tb) {
+  return a > b || (a == b && ta < tb);
+}
+
+__global__ __launch_bounds__(kSpThreads) void sp_table_kernel(SpTableParams p) {
+  __shared__ SpTableSmem sm;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int64_t b = blockIdx.x;
+  const int d = blockIdx.y + 1;  // child row
+  const int C = p.C, R = p.R, L = p.L;
+  const int32_t* pid = p.ids + ((size_t)b * L + d - 1) * C;  // parent candidates
+  const int32_t* cid = p.ids + ((size_t)b * L + d) * C;      // child candidates
+  const int cpr = R >> 3;  // 16-byte chunks per row
+  for (int q = tid; q < kSpC * cpr; q += kSpThreads) {
+    const int j = q / cpr, ch = q - j * cpr;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (j < C) v = *(const u32x4*)(p.W2t + (size_t)cid[j] * R + 8 * ch);
+    *(u32x4*)&sm.w2[j][8 * ch] = v;
+  }
+  if (tid < kSpC) {
+    sm.vals[tid] = tid < C ? p.vals[((size_t)b * L + d) * C + tid] : -INFINITY;
+    sm.tok[tid] = tid < C ? cid[tid] : 0x7FFFFFFF;
+  }
+  // this lane's parent row (A operand: row l % 32 of the wave's 32), all k-steps
+  const int i = 32 * w + (l & 31);
+  const int ptok = pid[i < C ? i : 0];
+  const uint16_t* arow = p.W1 + (size_t)ptok * R + 8 * (l >> 5);
+  const int nks = R / kSpKT;
+  u32x4 a[kSpRMax / kSpKT][4];
+#pragma unroll
+  for (int ks = 0; ks < kSpRMax / kSpKT; ++ks)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      a[ks][s] = ks < nks ? *(const u32x4*)(arow + ks * kSpKT + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  f32x16 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < kSpRMax / kSpKT; ++ks) {
+    if (ks < nks) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, a[ks][s]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const u32x4 braw = *(const u32x4*)&sm.w2[c * 32 + (l & 31)][ks * kSpKT + 16 * s + 8 * (l >> 5)];
+          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, braw),
+                                                           acc[c], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // epilogue: acc[c][r] is parent row 8 (r / 4) + 4 (l / 32) + r % 4 of the
+  // wave's 32, child column c * 32 + l % 32; the 32 lanes of a half share a row
+  const size_t rowbase = ((size_t)b * (L - 1) + (d - 1)) * C;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = 32 * w + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+    float s4[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = c * 32 + (l & 31);
+      s4[c] = j < C ? acc[c][r] + sm.vals[j] : -INFINITY;
+      mx = fmaxf(mx, s4[c]);
+    }
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float sum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sum += s4[c] == -INFINITY ? 0.0f : __expf(s4[c] - mx);
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) sum += __shfl_xor(sum, o);
+    const float lse = mx + __logf(sum);
+    float bv = -INFINITY;
+    int bt = 0x7FFFFFFF, bj = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = c * 32 + (l & 31);
+      const float v = s4[c] - lse;
+      s4[c] = v;
+      if (j < C && sp_better(v, sm.tok[j], bv, bt)) {
+        bv = v;
+        bt = sm.tok[j];
+        bj = j;
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int ot = __shfl_xor(bt, o), oj = __shfl_xor(bj, o);
+      if (sp_better(ov, ot, bv, bt)) {
+        bv = ov;
+        bt = ot;
+        bj = oj;
+      }
+    }
+    if (row < C) {
+      float* dst = p.lp + (rowbase + row) * C;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int j = c * 32 + (l & 31);
+        if (j < C) dst[j] = s4[c];
+      }
+      if ((l & 31) == 0) {
+        p.best[rowbase + row] = (uint8_t)bj;
+        p.blp[rowbase + row] = bv;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Selection on conditioned rows: select_kernel's method (an exact threshold
+// from the one-deviation prefixes, enumeration of E = {score >= tau} by
+// chains, histogram ordering, emission, mask) with a row per (depth, parent
+// token) instead of per depth. A node's children live in the row of its
+// candidate at the next depth (row 0, the first drafter row renormalised
+// over its candidates, for the root); rows are read from global memory in
+// candidate order, the best child of every row comes from LDS tables, so a
+// chain (rank-0 extensions) is walked without memory waits. Entries carry
+// their candidate index in eRank (ranks live in the lexicographic keys).
+
+struct SpTabs {                        // overlays the row-value table (unused here)
+  float lp0[kSpC];                     // row 0: first drafter row over its candidates
+  int32_t spine[kMaxL];                // the spine's candidate at each depth
+  int32_t best0;                       // row 0's best candidate (lp desc, token asc)
+  uint8_t best[(kMaxL - 1) * kSpC];    // best child of (child row d >= 1, parent candidate)
+  float blp[(kMaxL - 1) * kSpC];
+};
+static_assert(sizeof(SpTabs) <= sizeof(float) * kMaxLK, "conditioned tables fit the row table");
+static_assert(kMaxL * kSpC <= kMergeCap, "one-deviation scores fit a merge buffer");
+
+// Conditioned rows of request b: row(d, c) = log-probs of the children at
+// depth index d (0-based) of a node holding candidate c at depth index d-1.
+struct SpRows {
+  const SpTabs* tb;
+  const float* lp;     // [L-1][C][C]
+  const int32_t* tok;  // [L][C] candidate tokens
+  int C;
+  __device__ const float* row(int d, int c) const {
+    return d == 0 ? tb->lp0 : lp + ((size_t)(d - 1) * C + c) * C;
+  }
+  __device__ int best(int d, int c) const { return d == 0 ? tb->best0 : tb->best[(d - 1) * C + c]; }
+  __device__ float best_lp(int d, int c) const {
+    return d == 0 ? tb->lp0[tb->best0] : tb->blp[(d - 1) * C + c];
+  }
+  // position of child j in row (d, c): entries before it by (lp desc, token asc)
+  __device__ int rank(int d, int c, int j) const {
+    const float* r = row(d, c);
+    const int32_t* t = tok + (size_t)d * C;
+    const float v = r[j];
+    const int tj = t[j];
+    int n = 0;
+    for (int q = 0; q < C; ++q) n += (r[q] > v || (r[q] == v && t[q] < tj)) ? 1 : 0;
+    return n;
+  }
+};
+
+// Serial best-first heap (the post's loop) for requests whose enumeration
+// overflows: the next sibling is the best child of the row ordered after
+// the current one.
+__device__ void sp_heap_fallback(const SelectParams& p, SelectSmem& sm, int64_t b, const SpRows& R) {
+  SelHeap& h = sm.u.hp;
+  const int L = p.L, C = p.K, B = p.B;
+  int pool = 0, hn = 0, count = 0;
+  // the child of row (d, pc) ordered right after (v, t) (any child when t < 0)
+  auto next_after = [&](int d, int pc, float v, int t) -> int {
+    const float* r = R.row(d, pc);
+    const int32_t* tk = R.tok + (size_t)d * C;
+    int bj = -1;
+    for (int q = 0; q < C; ++q) {
+      const bool after = t < 0 || r[q] < v || (r[q] == v && tk[q] > t);
+      if (after && (bj < 0 || r[q] > r[bj] || (r[q] == r[bj] && tk[q] < tk[bj]))) bj = q;
+    }
+    return bj;
+  };
+  auto make = [&](int src, double Spar, int d, int rk, int parent_node, int pc, int j) -> int {
+    const int e = pool++;
+    for (int i = 0; i < d - 1; ++i) h.ranks[e][i] = h.ranks[src][i];
+    h.ranks[e][d - 1] = (uint16_t)rk;
+    h.dep[e] = (uint8_t)d;
+    h.parent[e] = (int16_t)parent_node;
+    h.Spar[e] = Spar;
+    h.S[e] = Spar + (double)R.row(d - 1, pc)[j];
+    h.sc[e] = h.S[e];
+    h.cand[e] = (uint8_t)j;
+    h.pcand[e] = (uint8_t)pc;
+    return e;
+  };
+  auto push = [&](int e) {
+    int i = hn++;
+    h.heap[i] = (uint16_t)e;
+    while (i > 0) {
+      const int pi = (i - 1) >> 1;
+      if (!heap_before(h, h.heap[i], h.heap[pi])) break;
+      const uint16_t t = h.heap[i];
+      h.heap[i] = h.heap[pi];
+      h.heap[pi] = t;
+      i = pi;
+    }
+  };
+  auto pop = [&]() -> int {
+    const int top = h.heap[0];
+    h.heap[0] = h.heap[--hn];
+    int i = 0;
+    for (;;) {
+      const int l = 2 * i + 1, r = l + 1;
+      int m = i;
+      if (l < hn && heap_before(h, h.heap[l], h.heap[m])) m = l;
+      if (r < hn && heap_before(h, h.heap[r], h.heap[m])) m = r;
+      if (m == i) break;
+      const uint16_t t = h.heap[i];
+      h.heap[i] = h.heap[m];
+      h.heap[m] = t;
+      i = m;
+    }
+    return top;
+  };
+  push(make(0, 0.0, 1, 0, 0, 0, R.best(0, 0)));
+  while (hn > 0 && count < B) {
+    const int e = pop();
+    const int d = h.dep[e], rk = h.ranks[e][d - 1];
+    h.out_e[count] = (int16_t)e;
+    const int node = ++count;
+    const int j = h.cand[e], pc = h.pcand[e];
+    const int sj = next_after(d - 1, pc, R.row(d - 1, pc)[j], R.tok[(size_t)(d - 1) * C + j]);
+    if (sj >= 0 && rk + 1 < C) push(make(e, h.Spar[e], d, rk + 1, h.parent[e], pc, sj));  // sibling
+    if (d < L) push(make(e, h.S[e], d + 1, 0, node, j, R.best(d, j)));                    // child
+  }
+  sm.nsel = count;
+  for (int q = 0; q < B; ++q) {
+    const size_t o = (size_t)b * B + q;
+    if (q < count) {
+      const int e = h.out_e[q];
+      const int d = h.dep[e];
+      p.tree_tokens[o] = R.tok[(size_t)(d - 1) * C + h.cand[e]];
+      p.parents[o] = h.parent[e];
+      p.logq[o] = (float)h.sc[e];
+      if (p.depths) p.depths[o] = d;
+      sm.opar[q] = h.parent[e];
+    } else {
+      p.tree_tokens[o] = -1;
+      p.parents[o] = -1;
+      p.logq[o] = -INFINITY;
+      if (p.depths) p.depths[o] = 0;
+    }
+  }
+  p.num_nodes[b] = count;
+}
+
+__global__ __launch_bounds__(kSelThreads) void sp_select_kernel(SelectParams p) {
+  __shared__ SelectSmem sm;
+  SelEnum& en = sm.u.en;
+  SpTabs& tb = *reinterpret_cast<SpTabs*>(sm.v);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t b = blockIdx.x;
+  const int L = p.L, C = p.K, B = p.B, LC = L * C, bpd = p.bpd;
+  SpRows R;
+  R.tb = &tb;
+  R.lp = p.sp_lp + (size_t)b * (L - 1) * C * C;
+  R.tok = p.ids + (size_t)b * LC;
+  R.C = C;
+  for (int i = tid; i < (L - 1) * C; i += kSelThreads) {
+    tb.best[i] = p.sp_best[(size_t)b * (L - 1) * C + i];
+    tb.blp[i] = p.sp_blp[(size_t)b * (L - 1) * C + i];
+  }
+  if (wv == 0) {
+    // row 0 over its candidates (the table kernel's arithmetic)
+    const float* v0 = p.vals + (size_t)b * LC;
+    float x[kSpC / kWave];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kSpC / kWave; ++q) {
+      const int j = lane + q * kWave;
+      x[q] = j < C ? v0[j] : -INFINITY;
+      mx = fmaxf(mx, x[q]);
+    }
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float sum = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kSpC / kWave; ++q) sum += x[q] == -INFINITY ? 0.0f : __expf(x[q] - mx);
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) sum += __shfl_xor(sum, o);
+    const float lse = mx + __logf(sum);
+    // its best (rounding can tie distinct logits: ties go to the lower token)
+    const int32_t* t0 = p.ids + (size_t)b * LC;
+    float bv = -INFINITY;
+    int bt = 0x7FFFFFFF, bj = 0;
+#pragma unroll
+    for (int q = 0; q < kSpC / kWave; ++q) {
+      const int j = lane + q * kWave;
+      if (j < C) {
+        const float v = x[q] - lse;
+        tb.lp0[j] = v;
+        if (sp_better(v, t0[j], bv, bt)) {
+          bv = v;
+          bt = t0[j];
+          bj = j;
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int ot = __shfl_xor(bt, o), oj = __shfl_xor(bj, o);
+      if (sp_better(ov, ot, bv, bt)) {
+        bv = ov;
+        bt = ot;
+        bj = oj;
+      }
+    }
+    if (lane == 0) tb.best0 = bj;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // the spine: best children all the way down, float64 left to right
+    int c = tb.best0;
+    double S = (double)tb.lp0[c];
+    sm.P0[0] = 0.0;
+    sm.sig[0] = 0.0;
+    sm.P0[1] = S;
+    sm.sig[1] = S;
+    tb.spine[0] = c;
+    for (int d = 1; d < L; ++d) {
+      S += (double)tb.blp[(d - 1) * C + c];
+      c = tb.best[(d - 1) * C + c];
+      tb.spine[d] = c;
+      sm.P0[d + 1] = S;
+      sm.sig[d + 1] = S;
+    }
+    sm.nE = 0;
+    sm.ovf = 0;
+  }
+  __syncthreads();
+
+  // ---- 1. threshold: the spine nodes' rows (root: row 0) give L*C one-
+  // deviation prefixes; their minimum is a lower bound with >= B above it
+  double tau = -INFINITY;
+  if (LC >= B) {
+    double* od = sm.u.mt.b;
+    for (int i = tid; i < LC; i += kSelThreads) {
+      const int d = i / C, j = i - d * C;
+      od[i] = sm.P0[d] + (double)R.row(d, d == 0 ? 0 : tb.spine[d - 1])[j];
+    }
+    __syncthreads();
+    tau = sel_tau_hist(sm, LC, B, [&](int i) { return od[i]; },
+                       [&](int ln) {
+                         double m = INFINITY;
+                         for (int i = ln; i < LC; i += kWave) m = od[i] < m ? od[i] : m;
+                         return m;
+                       });
+  }
+
+  // ---- 2. enumerate E = {score >= tau} by chains ----------------------------
+  int D0 = 0;
+  for (int d = 1; d <= L; ++d) D0 += sm.sig[d] >= tau ? 1 : 0;
+  for (int d = tid; d < D0; d += kSelThreads) {
+    en.eS[d] = sm.P0[d + 1];
+    en.eSc[d] = sm.sig[d + 1];
+    en.ePar[d] = (int16_t)(d - 1);
+    en.eRank[d] = (uint16_t)tb.spine[d];
+    en.eDep[d] = (uint8_t)(d + 1);
+    en.eLh[d] = 0;
+    en.eLl[d] = (uint64_t)(d + 1);
+  }
+  if (tid == 0) sm.nE = D0;
+  __syncthreads();
+  int g0 = 0, g1 = D0, root = 1;
+  for (;;) {
+    const int np = root + (g1 - g0);
+    if (np > kECap) {
+      if (tid == 0) sm.ovf = 1;
+      __syncthreads();
+      break;
+    }
+    // deviating children (not the row's best) of each parent that reach tau
+    const int ppt = np > kSelThreads ? 2 : 1;
+    int cpar[2] = {0, 0};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid * ppt + k;
+      if (k < ppt && i < np) {
+        double S = 0.0;
+        int d = 0, c = 0;
+        if (!(root && i == 0)) {
+          const int e = g0 + i - root;
+          S = en.eS[e];
+          d = en.eDep[e];
+          c = en.eRank[e];
+        }
+        if (d < L) {
+          const float* r = R.row(d, c);
+          const int bj = R.best(d, c);
+          int n = 0;
+          for (int j = 0; j < C; ++j) n += (j != bj && S + (double)r[j] >= tau) ? 1 : 0;
+          cpar[k] = n;
+        }
+      }
+    }
+    int A;
+    const int off = block_excl_scan_reg<kSelThreads>(cpar[0] + cpar[1], sm.wsum, A);
+    if (A == 0) break;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid * ppt + k;
+      if (k < ppt && i < np) en.cnt[i] = off + (k ? cpar[0] : 0);
+    }
+    __syncthreads();
+    for (int a = tid; a < A; a += kSelThreads) {
+      int lo = 0, hi = np - 1;  // parent = largest u with offset[u] <= a
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (en.cnt[mid] <= a) lo = mid;
+        else hi = mid - 1;
+      }
+      const int u = lo, kth = a - en.cnt[u];
+      double Su = 0.0;
+      int du = 0, cu = 0, pe = -1;
+      uint64_t lh = 0, ll = 0;
+      if (!(root && u == 0)) {
+        pe = g0 + u - root;
+        Su = en.eS[pe];
+        du = en.eDep[pe];
+        cu = en.eRank[pe];
+        lh = en.eLh[pe];
+        ll = en.eLl[pe] & ~63ull;
+      }
+      // the kth qualifying deviating child of u's row (candidate order)
+      const float* r = R.row(du, cu);
+      const int bj = R.best(du, cu);
+      int j = -1, seen = 0;
+      for (int q = 0; q < C && j < 0; ++q) {
+        if (q != bj && Su + (double)r[q] >= tau) {
+          if (seen == kth) j = q;
+          ++seen;
+        }
+      }
+      if (j < 0) {  // cannot happen: the same test counted it
+        sm.ovf = 1;
+        continue;
+      }
+      const int d = du + 1;
+      const double S = Su + (double)r[j];
+      lex_set_digit(lh, ll, d, (uint32_t)R.rank(du, cu, j), bpd);
+      // chain length: the anchor, then best children while they reach tau
+      int ell = 1;
+      {
+        double S2 = S;
+        int c2 = j;
+        for (int dd = d + 1; dd <= L; ++dd) {
+          S2 += (double)R.best_lp(dd - 1, c2);
+          if (S2 < tau) break;
+          c2 = R.best(dd - 1, c2);
+          ++ell;
+        }
+      }
+      const int pos = atomicAdd(&sm.nE, ell);
+      if (pos + ell > kECap) {
+        sm.ovf = 1;
+        continue;
+      }
+      en.eS[pos] = S;
+      en.eSc[pos] = S;
+      en.ePar[pos] = (int16_t)pe;
+      en.eRank[pos] = (uint16_t)j;
+      en.eDep[pos] = (uint8_t)d;
+      en.eLh[pos] = lh;
+      en.eLl[pos] = ll | (uint64_t)d;
+      double S2 = S;
+      int c2 = j;
+      for (int i = 1; i < ell; ++i) {
+        const int dd = d + i;
+        S2 += (double)R.best_lp(dd - 1, c2);
+        c2 = R.best(dd - 1, c2);
+        const int q = pos + i;
+        en.eS[q] = S2;
+        en.eSc[q] = S2;
+        en.ePar[q] = (int16_t)(q - 1);
+        en.eRank[q] = (uint16_t)c2;
+        en.eDep[q] = (uint8_t)dd;
+        en.eLh[q] = lh;
+        en.eLl[q] = ll | (uint64_t)dd;
+      }
+    }
+    __syncthreads();
+    if (sm.ovf) break;
+    g0 = g1;
+    g1 = sm.nE;
+    root = 0;
+    if (g0 == g1) break;
+  }
+
+  if (sm.ovf) {
+    __syncthreads();
+    if (tid == 0) sp_heap_fallback(p, sm, b, R);
+    __syncthreads();
+  } else {
+    sel_order_emit(p, sm, b, tau);
+  }
+  sel_mask(p, sm, b);
+}
+
+}  // namespace ddt

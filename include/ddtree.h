@@ -23,6 +23,12 @@
  *    packing) and item 2 (per-parent top-k expansion, joint path-score
  *    frontier pruning, global top-N packing).
  *    SparklingTree post, section "Step 1".
+ *  - sparkling_build: SparklingTree's conditioned best-first tree.
+ *    SparklingTree post, sections "Building SparklingTree" (top-C pre-filter
+ *    of every drafter row, low-rank first-order Markov head) and "Solving
+ *    the candidate tree construction" (the head looks back one token, so the
+ *    deltas between consecutive rows' candidates form a table computed up
+ *    front; best-first growth on the conditioned rows).
  *  - ddtree_select: stage 2 alone, from stage 1's tables. DDTree explainer,
  *    sections 3-4; SparklingTree post, section "Step 3".
  *    ddtree_build = ddtree_row_topk + ddtree_select in one call.
@@ -233,6 +239,43 @@ int treespark_expand(const void* backbone, const void* W, const void* E, const i
                      int32_t N, int32_t* tree_tokens, int32_t* parents, float* logq,
                      int32_t* depths, int32_t* num_nodes, void* workspace,
                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sparkling_build -- SparklingTree's conditioned best-first tree (SparklingTree
+ * post, "Building SparklingTree" and "Solving the candidate tree
+ * construction"). For request b with drafter rows x_1..x_L (logits [b][d][:]):
+ *  1. c_d = the top C tokens of x_d by (value desc, id asc) (the pre-filter);
+ *  2. row 1 (children of the root): lp_j = x_1[c_1j] - logsumexp over the C
+ *     candidates (depth 1 is not conditioned);
+ *     row d >= 2 for a parent holding candidate token p of depth d-1:
+ *     s_j = x_d[c_dj] + W1[p] . W2t[c_dj] (the rank-R Markov head,
+ *     W1 [V][R] extraction, W2t [V][R] projection transposed), lp_j = s_j -
+ *     logsumexp(s) over the C candidates; children order by (lp desc, id asc);
+ *  3. the B best prefixes, score = sum of lp along the path (float64 left to
+ *     right from float32 lp), ordered by (score desc, rank tuple lexicographic
+ *     asc, a prefix before its extensions) -- the order of the post's
+ *     best-first heap (pop, push the best child and the next sibling).
+ * logits [batch][L][V], dtype DDT_BF16 or DDT_F32, 16-byte aligned;
+ * W1, W2t [V][R] bf16, 16-byte aligned; token ids < V come from step 1.
+ * Outputs as ddtree_build ([batch][B] tree_tokens, parents, logq, depths
+ * (nullable); num_nodes [batch] = min(B, prefixes); mask [batch][B+1][W]
+ * (nullable), W = ceil((B+1)/64)); the tail is padded with -1, -1, -inf, 0.
+ * The Markov dot products accumulate bf16 products in float32 (MFMA); row
+ * normalisation is float32; path scores are float64.
+ * Supported: 1 <= C <= min(128, V), R a multiple of 64 up to 256,
+ * 1 <= L <= DDT_MAX_L, B <= DDT_MAX_B, L * ceil(log2 C) <= 122, V < 2^31;
+ * otherwise DDT_ENOTSUP (C > V: DDT_EINVAL).
+ * The workspace (sparkling_build_workspace_size bytes, no zero-fill needed)
+ * holds the top-C tables and the conditioned rows ([batch][L-1][C][C] float
+ * log-probs, each row's best child); 0 means unsupported sizes.
+ */
+size_t sparkling_build_workspace_size(int64_t batch, int32_t L, int64_t V, int32_t C,
+                                      int32_t R, int32_t B, int dtype);
+int sparkling_build(const void* logits, int dtype, const uint16_t* W1, const uint16_t* W2t,
+                    int64_t batch, int32_t L, int64_t V, int32_t C, int32_t R, int32_t B,
+                    int32_t* tree_tokens, int32_t* parents, float* logq, int32_t* depths,
+                    int32_t* num_nodes, uint64_t* mask, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
 
 #ifdef __cplusplus
 }

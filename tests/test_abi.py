@@ -26,13 +26,14 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b((?:ddt|ddtree)_[a-z0-9_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:ddt|ddtree|treespark|sparkling)_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_four_operations():
     names = declared_functions()
     for n in ("ddtree_build", "ddtree_select", "ddtree_mask", "ddtree_accept", "ddtree_row_topk",
-              "ddtree_compact_kv",
+              "ddtree_compact_kv", "treespark_expand", "treespark_workspace_size",
+              "sparkling_build", "sparkling_build_workspace_size",
               "ddtree_build_workspace_size", "ddtree_row_topk_workspace_size",
               "ddt_status_string", "ddt_abi_version"):
         assert n in names
@@ -152,3 +153,34 @@ def test_compact_kv_validation(L):
     assert call(k=MISALIGNED) == -1
     assert call(past=None) == -1
     assert call(layers=0) == 0            # nothing to do
+
+
+def test_sparkling_validation(L):
+    """Sizes and pointers rejected before any launch (pointers never dereferenced)."""
+    ws = L.sparkling_build_workspace_size
+    assert ws(64, 15, 151936, 128, 256, 64, 0) > 64 * 14 * 128 * 128 * 4   # conditioned rows
+    assert ws(64, 15, 151936, 129, 256, 64, 0) == 0      # C > 128
+    assert ws(64, 15, 151936, 128, 200, 64, 0) == 0      # R not a multiple of 64
+    assert ws(64, 15, 151936, 128, 320, 64, 0) == 0      # R > 256
+    assert ws(64, 18, 151936, 128, 256, 64, 0) == 0      # L * ceil(log2 C) > 122
+    assert ws(64, 15, 100, 128, 256, 64, 0) == 0         # C > V
+    assert ws(1, 1, 1024, 8, 64, 4, 0) > 0               # one row: no conditioned rows
+
+    def call(logits=FAKE, dtype=0, W1=FAKE, batch=2, Lr=15, V=1024, C=128, R=256, B=64, out=FAKE,
+             wsp=FAKE, ws_bytes=1 << 34):
+        return L.sparkling_build(logits, dtype, W1, FAKE, batch, Lr, V, C, R, B, out, out, out,
+                                 out, out, out, wsp, ws_bytes, None)
+    assert call(logits=None) == -1
+    assert call(W1=None) == -1
+    assert call(out=None) == -1
+    assert call(wsp=None) == -1
+    assert call(W1=MISALIGNED) == -1
+    assert call(dtype=3) == -1
+    assert call(C=0) == -1
+    assert call(C=2000, V=1024) == -1    # C > V
+    assert call(C=200) == -2
+    assert call(R=96) == -2
+    assert call(B=513) == -2
+    assert call(Lr=33) == -2
+    assert call(ws_bytes=64) == -3
+    assert call(batch=0) == 0            # nothing to do
