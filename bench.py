@@ -131,6 +131,58 @@ def treespark_bench(args) -> int:
     return 0
 
 
+def sparkling_bench(args) -> int:
+    """SparklingTree conditioned tree: 64 requests x 15 drafter rows over
+    V = 151936, top C = 128 per row, rank-256 Markov head, B = 64 nodes; one
+    step = one sparkling_build call (top-C rows, Markov-delta table,
+    selection + mask). Two copies of the logits rotate."""
+    import numpy as np
+    import torch
+
+    import draft_tree_construction_depth_amd as pkg
+    from draft_tree_construction_depth_amd import gen
+
+    c = gen.SPARKLING
+    batch, L, V, B, C, R = (c[x] for x in ("batch", "L", "V", "B", "C", "R"))
+    x, W1, W2t = gen.sparkling_inputs(0)
+    dev = torch.device("cuda:0")
+    as_bf16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
+        torch.bfloat16)
+    xs = [as_bf16(x), as_bf16(gen.sparkling_inputs(1)[0])]
+    W1d, W2d = as_bf16(W1), as_bf16(W2t)
+    out = pkg.sparkling_build(xs[0], W1d, W2d, B, C=C)
+    for i in range(args.warmup):
+        pkg.sparkling_build(xs[i % 2], W1d, W2d, B, C=C, out=out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for i in range(args.steps):
+        pkg.sparkling_build(xs[i % 2], W1d, W2d, B, C=C, out=out)
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = a.elapsed_time(b) / args.steps
+    # logits once; per conditioned row block: C rows of W1 and of W2t, the C x C
+    # float log-probs written; the selection's reads of visited rows are not counted
+    blocks = batch * (L - 1)
+    alg_bytes = batch * L * V * 2 + blocks * (2 * C * R * 2 + C * C * 4 + C * 5)
+    res = {
+        "metric": "SparklingTree trees/sec at batch 64, L=15, V=151936, C=128, R=256, B=64",
+        "value": round(batch / (ms / 1e3), 1), "unit": "trees/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16/f32/f64", "data": "synthetic",
+        "config": {"workload": "sparkling_batch64_L15_V151936_C128_R256_B64", "batch": batch,
+                   "L": L, "V": V, "C": C, "R": R, "B": B, "input_buffers": 2},
+        "algorithmic_gbps": round(alg_bytes / (ms / 1e3) / 1e9, 1),
+        "hbm_frac": round(alg_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 # Verifier cache of the KV-compaction workload: Qwen3-8B's attention shape
 # (36 layers, 8 KV heads, head dim 128, bf16), 1024 tokens of context.
 KV_LAYERS, KV_HEADS, KV_DH, KV_PAST = 36, 8, 128, 1024
@@ -209,6 +261,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--treespark", action="store_true",
                     help="time treespark_expand on the TreeSpark workload instead (own JSON line)")
+    ap.add_argument("--sparkling", action="store_true",
+                    help="time sparkling_build on the SparklingTree workload instead (own JSON line)")
     ap.add_argument("--kv-compact", action="store_true",
                     help="time ddtree_compact_kv after a batch-64 round instead (own JSON line)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -242,6 +296,8 @@ def main() -> int:
         return treespark_bench(args)
     if args.kv_compact:
         return kv_bench(args)
+    if args.sparkling:
+        return sparkling_bench(args)
 
     c = gen.CONFIGS[3]
     batch, L, V, B = c["batch"], c["L"], c["V"], c["B"]

@@ -330,7 +330,7 @@ int sp_check(int dtype, int64_t batch, int32_t L, int64_t V, int32_t C, int32_t 
   if (B > DDT_MAX_B || L > DDT_MAX_L || V > 0x7FFFFFFFLL || batch > 0x7FFFFFFFLL)
     return DDT_ENOTSUP;
   const int bpd = ceil_log2(C) < 1 ? 1 : ceil_log2(C);
-  if (L * bpd > 122) return DDT_ENOTSUP;
+  if (L * bpd > 122 || (int64_t)L * C > ddt::kSpMaxLC) return DDT_ENOTSUP;
   return DDT_OK;
 }
 

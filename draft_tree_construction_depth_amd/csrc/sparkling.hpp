@@ -14,11 +14,14 @@
 //
 // sp_table_kernel: per request and child row d >= 1, one workgroup forms
 //   delta[i][j] = W1[c_{d-1}[i]] . W2t[c_d[j]] for all C x C candidate pairs
-//   on MFMA (32x32x16 bf16, float32 accumulate; the C child rows of W2t are
-//   staged in LDS, each wave holds 32 parent rows of W1 in registers), then
-//   per parent row i: s_j = x_d[c_j] + delta[i][j], lp_j = s_j - logsumexp(s)
-//   and the row's best child (lp desc, token asc). Rows stay in candidate
-//   order: the selection counts, ranks and walks them without sorting.
+//   on MFMA (32x32x16 bf16, float32 accumulate; the child rows of W2t are
+//   the A operand, staged in LDS, each wave holds 32 parent rows of W1 as
+//   the B operand in registers), so that each lane ends up with half of one
+//   parent's row: s_j = x_d[c_j] + delta[i][j], its maximum, sum of
+//   exponentials and best child (lp desc, token asc) reduce in registers and
+//   one exchange between the two lanes of a parent. lp_j = s_j -
+//   logsumexp(s) goes out through an LDS tile as whole 16-byte rows.
+//   Rows stay in candidate order: the selection reads them unsorted.
 // The selection itself is sp_select_kernel, below.
 #pragma once
 
@@ -32,6 +35,10 @@ constexpr int kSpThreads = 256;
 constexpr int kSpC = 128;     // candidates per row, at most (MFMA tiles of 32)
 constexpr int kSpRMax = 256;  // Markov rank, at most (four k-steps of 64 in registers)
 constexpr int kSpKT = 64;
+constexpr int kSpPitch = kSpRMax + 8;  // bf16 row pitch of the staged W2t rows
+constexpr int kSpTile = 132;           // float row pitch of the staged log-prob tile
+// With L * ceil(log2 C) <= 122 bits of rank key and C <= 128, L * C <= 17 * 128.
+constexpr int kSpMaxLC = 17 * kSpC;
 
 struct SpTableParams {
   const uint16_t* W1;   // [V][R] bf16
@@ -45,10 +52,14 @@ struct SpTableParams {
 };
 
 struct SpTableSmem {
-  uint16_t w2[kSpC][kSpRMax + 8];  // the child candidates' W2t rows (row pitch padded)
+  union {
+    uint16_t w2[kSpC][kSpPitch];  // the child candidates' W2t rows (MFMA A operand)
+    float tile[kSpC][kSpTile];    // then the finished log-prob rows
+  } u;
   float vals[kSpC];
   int32_t tok[kSpC];
 };
+static_assert(sizeof(float) * kSpTile == sizeof(uint16_t) * kSpPitch, "tile overlays the rows");
 
 __device__ __forceinline__ bool sp_better(float a, int ta, float b, int tb) {
   return a > b || (a == b && ta < tb);
@@ -56,111 +67,140 @@ __device__ __forceinline__ bool sp_better(float a, int ta, float b, int tb) {
 
 __global__ __launch_bounds__(kSpThreads) void sp_table_kernel(SpTableParams p) {
   __shared__ SpTableSmem sm;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5;
   const int64_t b = blockIdx.x;
   const int d = blockIdx.y + 1;  // child row
   const int C = p.C, R = p.R, L = p.L;
   const int32_t* pid = p.ids + ((size_t)b * L + d - 1) * C;  // parent candidates
   const int32_t* cid = p.ids + ((size_t)b * L + d) * C;      // child candidates
+  // every load in flight before the first wait: this lane's parent row (B
+  // operand: parent 32 w + l % 32, k-chunks 8 (l / 32) of each 16), then its
+  // share of the child rows (16-byte chunks; half a wave covers one row of
+  // 256 bf16)
+  const int i = 32 * w + (l & 31);
+  const int ptok = pid[i < C ? i : 0];
+  const uint16_t* brow = p.W1 + (size_t)ptok * R + 8 * h;
+  const int nks = R / kSpKT;
+  u32x4 bq[kSpRMax / kSpKT][4];
+#pragma unroll
+  for (int ks = 0; ks < kSpRMax / kSpKT; ++ks)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      bq[ks][s] = ks < nks ? *(const u32x4*)(brow + ks * kSpKT + 16 * s) : u32x4{0u, 0u, 0u, 0u};
   const int cpr = R >> 3;  // 16-byte chunks per row
-  for (int q = tid; q < kSpC * cpr; q += kSpThreads) {
+  constexpr int kStage = kSpC * (kSpRMax / 8) / kSpThreads;
+  u32x4 st[kStage];
+#pragma unroll
+  for (int k = 0; k < kStage; ++k) {
+    const int q = tid + k * kSpThreads;
     const int j = q / cpr, ch = q - j * cpr;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (j < C) v = *(const u32x4*)(p.W2t + (size_t)cid[j] * R + 8 * ch);
-    *(u32x4*)&sm.w2[j][8 * ch] = v;
+    st[k] = u32x4{0u, 0u, 0u, 0u};
+    if (j < C) st[k] = *(const u32x4*)(p.W2t + (size_t)cid[j] * R + 8 * ch);
   }
   if (tid < kSpC) {
     sm.vals[tid] = tid < C ? p.vals[((size_t)b * L + d) * C + tid] : -INFINITY;
     sm.tok[tid] = tid < C ? cid[tid] : 0x7FFFFFFF;
   }
-  // this lane's parent row (A operand: row l % 32 of the wave's 32), all k-steps
-  const int i = 32 * w + (l & 31);
-  const int ptok = pid[i < C ? i : 0];
-  const uint16_t* arow = p.W1 + (size_t)ptok * R + 8 * (l >> 5);
-  const int nks = R / kSpKT;
-  u32x4 a[kSpRMax / kSpKT][4];
 #pragma unroll
-  for (int ks = 0; ks < kSpRMax / kSpKT; ++ks)
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      a[ks][s] = ks < nks ? *(const u32x4*)(arow + ks * kSpKT + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+  for (int k = 0; k < kStage; ++k) {
+    const int q = tid + k * kSpThreads;
+    const int j = q / cpr, ch = q - j * cpr;
+    if (j < kSpC) *(u32x4*)&sm.u.w2[j][8 * ch] = st[k];
+  }
   __syncthreads();
+  // acc[m][r] = delta of child 32 m + 8 (r / 4) + 4 (l / 32) + r % 4 for
+  // parent 32 w + l % 32
   f32x16 acc[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) acc[m][r] = 0.0f;
 #pragma unroll
   for (int ks = 0; ks < kSpRMax / kSpKT; ++ks) {
     if (ks < nks) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, a[ks][s]);
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, bq[ks][s]);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const u32x4 braw = *(const u32x4*)&sm.w2[c * 32 + (l & 31)][ks * kSpKT + 16 * s + 8 * (l >> 5)];
-          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, braw),
-                                                           acc[c], 0, 0, 0);
+        for (int m = 0; m < 4; ++m) {
+          const u32x4 araw = *(const u32x4*)&sm.u.w2[m * 32 + (l & 31)][ks * kSpKT + 16 * s + 8 * h];
+          acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, araw), bv,
+                                                           acc[m], 0, 0, 0);
         }
       }
     }
   }
-  // epilogue: acc[c][r] is parent row 8 (r / 4) + 4 (l / 32) + r % 4 of the
-  // wave's 32, child column c * 32 + l % 32; the 32 lanes of a half share a row
-  const size_t rowbase = ((size_t)b * (L - 1) + (d - 1)) * C;
+  // epilogue: this lane's 64 children of parent i, the other 64 in lane l ^ 32
+  float mx = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = 32 * w + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-    float s4[4];
-    float mx = -INFINITY;
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = c * 32 + (l & 31);
-      s4[c] = j < C ? acc[c][r] + sm.vals[j] : -INFINITY;
-      mx = fmaxf(mx, s4[c]);
+    for (int r = 0; r < 16; ++r) {
+      const int j = m * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      acc[m][r] = j < C ? acc[m][r] + sm.vals[j] : -INFINITY;
+      mx = fmaxf(mx, acc[m][r]);
     }
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  float sum = 0.0f;
 #pragma unroll
-    for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    float sum = 0.0f;
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) sum += s4[c] == -INFINITY ? 0.0f : __expf(s4[c] - mx);
+    for (int r = 0; r < 16; ++r) sum += acc[m][r] == -INFINITY ? 0.0f : __expf(acc[m][r] - mx);
+  sum += __shfl_xor(sum, 32);
+  const float lse = mx + __logf(sum);
+  float bv = -INFINITY;
+  int bt = 0x7FFFFFFF, bj = 0;
 #pragma unroll
-    for (int o = 1; o < 32; o <<= 1) sum += __shfl_xor(sum, o);
-    const float lse = mx + __logf(sum);
-    float bv = -INFINITY;
-    int bt = 0x7FFFFFFF, bj = 0;
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = c * 32 + (l & 31);
-      const float v = s4[c] - lse;
-      s4[c] = v;
+    for (int r = 0; r < 16; ++r) {
+      const int j = m * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      const float v = acc[m][r] - lse;
+      acc[m][r] = v;
       if (j < C && sp_better(v, sm.tok[j], bv, bt)) {
         bv = v;
         bt = sm.tok[j];
         bj = j;
       }
     }
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int ot = __shfl_xor(bt, o), oj = __shfl_xor(bj, o);
-      if (sp_better(ov, ot, bv, bt)) {
-        bv = ov;
-        bt = ot;
-        bj = oj;
-      }
+  {
+    const float ov = __shfl_xor(bv, 32);
+    const int ot = __shfl_xor(bt, 32), oj = __shfl_xor(bj, 32);
+    if (sp_better(ov, ot, bv, bt)) {
+      bv = ov;
+      bt = ot;
+      bj = oj;
     }
-    if (row < C) {
-      float* dst = p.lp + (rowbase + row) * C;
+  }
+  const size_t rowbase = ((size_t)b * (L - 1) + (d - 1)) * C;
+  if (h == 0 && i < C) {
+    p.best[rowbase + i] = (uint8_t)bj;
+    p.blp[rowbase + i] = bv;
+  }
+  __syncthreads();  // every wave has read its A operands: the rows become the tile
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int j = c * 32 + (l & 31);
-        if (j < C) dst[j] = s4[c];
-      }
-      if ((l & 31) == 0) {
-        p.best[rowbase + row] = (uint8_t)bj;
-        p.blp[rowbase + row] = bv;
-      }
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      float4 v4;
+      v4.x = acc[m][4 * rq + 0];
+      v4.y = acc[m][4 * rq + 1];
+      v4.z = acc[m][4 * rq + 2];
+      v4.w = acc[m][4 * rq + 3];
+      *(float4*)&sm.u.tile[i][m * 32 + 8 * rq + 4 * h] = v4;
+    }
+  __syncthreads();
+  float* dst = p.lp + rowbase * C;  // C rows of C floats, contiguous
+  if ((C & 3) == 0) {
+    const int cq = C >> 2;  // 16-byte chunks per row
+    for (int q = tid; q < C * cq; q += kSpThreads) {
+      const int r = q / cq, c4 = q - r * cq;
+      *(float4*)(dst + (size_t)r * C + 4 * c4) = *(const float4*)&sm.u.tile[r][4 * c4];
+    }
+  } else {
+    for (int q = tid; q < C * C; q += kSpThreads) {
+      const int r = q / C, c = q - r * C;
+      dst[(size_t)r * C + c] = sm.u.tile[r][c];
     }
   }
 }
@@ -176,22 +216,23 @@ __global__ __launch_bounds__(kSpThreads) void sp_table_kernel(SpTableParams p) {
 // chain (rank-0 extensions) is walked without memory waits. Entries carry
 // their candidate index in eRank (ranks live in the lexicographic keys).
 
-struct SpTabs {                        // overlays the row-value table (unused here)
-  float lp0[kSpC];                     // row 0: first drafter row over its candidates
-  int32_t spine[kMaxL];                // the spine's candidate at each depth
-  int32_t best0;                       // row 0's best candidate (lp desc, token asc)
-  uint8_t best[(kMaxL - 1) * kSpC];    // best child of (child row d >= 1, parent candidate)
-  float blp[(kMaxL - 1) * kSpC];
+struct SpTabs {                  // overlays the row-value table (unused here)
+  float lp0[kSpC];               // row 0: first drafter row over its candidates
+  int32_t spine[kMaxL];          // the spine's candidate at each depth
+  int32_t best0;                 // row 0's best candidate (lp desc, token asc)
+  int32_t tok[kSpMaxLC];         // [L][C] candidate tokens
+  uint8_t best[kSpMaxLC];        // best child of (child row d >= 1, parent candidate)
+  float blp[kSpMaxLC];
 };
 static_assert(sizeof(SpTabs) <= sizeof(float) * kMaxLK, "conditioned tables fit the row table");
-static_assert(kMaxL * kSpC <= kMergeCap, "one-deviation scores fit a merge buffer");
+static_assert(kSpMaxLC <= kMergeCap, "one-deviation scores fit a merge buffer");
 
 // Conditioned rows of request b: row(d, c) = log-probs of the children at
 // depth index d (0-based) of a node holding candidate c at depth index d-1.
 struct SpRows {
   const SpTabs* tb;
   const float* lp;     // [L-1][C][C]
-  const int32_t* tok;  // [L][C] candidate tokens
+  const int32_t* tok;  // [L][C] candidate tokens (LDS)
   int C;
   __device__ const float* row(int d, int c) const {
     return d == 0 ? tb->lp0 : lp + ((size_t)(d - 1) * C + c) * C;
@@ -314,8 +355,9 @@ __global__ __launch_bounds__(kSelThreads) void sp_select_kernel(SelectParams p) 
   SpRows R;
   R.tb = &tb;
   R.lp = p.sp_lp + (size_t)b * (L - 1) * C * C;
-  R.tok = p.ids + (size_t)b * LC;
+  R.tok = tb.tok;
   R.C = C;
+  for (int i = tid; i < LC; i += kSelThreads) tb.tok[i] = p.ids[(size_t)b * LC + i];
   for (int i = tid; i < (L - 1) * C; i += kSelThreads) {
     tb.best[i] = p.sp_best[(size_t)b * (L - 1) * C + i];
     tb.blp[i] = p.sp_blp[(size_t)b * (L - 1) * C + i];
@@ -340,7 +382,7 @@ __global__ __launch_bounds__(kSelThreads) void sp_select_kernel(SelectParams p) 
     for (int o = 1; o < kWave; o <<= 1) sum += __shfl_xor(sum, o);
     const float lse = mx + __logf(sum);
     // its best (rounding can tie distinct logits: ties go to the lower token)
-    const int32_t* t0 = p.ids + (size_t)b * LC;
+    const int32_t* t0 = p.ids + (size_t)b * LC;  // (the LDS copy is not yet visible)
     float bv = -INFINITY;
     int bt = 0x7FFFFFFF, bj = 0;
 #pragma unroll
@@ -422,128 +464,134 @@ __global__ __launch_bounds__(kSelThreads) void sp_select_kernel(SelectParams p) 
   }
   if (tid == 0) sm.nE = D0;
   __syncthreads();
+  // Generation g: the chains whose anchors deviate g times. One wave per
+  // parent: its row is read once (two floats a lane), a ballot marks the
+  // children that deviate (not the row's best) and reach tau, and each such
+  // lane appends its chain. A child's rank is 1 (the best child) plus the
+  // deviating children ordered before it: every child ordered before a
+  // qualifying one scores at least as high, so qualifies too.
   int g0 = 0, g1 = D0, root = 1;
   for (;;) {
     const int np = root + (g1 - g0);
-    if (np > kECap) {
-      if (tid == 0) sm.ovf = 1;
-      __syncthreads();
-      break;
-    }
-    // deviating children (not the row's best) of each parent that reach tau
-    const int ppt = np > kSelThreads ? 2 : 1;
-    int cpar[2] = {0, 0};
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int i = tid * ppt + k;
-      if (k < ppt && i < np) {
-        double S = 0.0;
-        int d = 0, c = 0;
-        if (!(root && i == 0)) {
-          const int e = g0 + i - root;
-          S = en.eS[e];
-          d = en.eDep[e];
-          c = en.eRank[e];
-        }
-        if (d < L) {
-          const float* r = R.row(d, c);
-          const int bj = R.best(d, c);
-          int n = 0;
-          for (int j = 0; j < C; ++j) n += (j != bj && S + (double)r[j] >= tau) ? 1 : 0;
-          cpar[k] = n;
-        }
-      }
-    }
-    int A;
-    const int off = block_excl_scan_reg<kSelThreads>(cpar[0] + cpar[1], sm.wsum, A);
-    if (A == 0) break;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int i = tid * ppt + k;
-      if (k < ppt && i < np) en.cnt[i] = off + (k ? cpar[0] : 0);
-    }
-    __syncthreads();
-    for (int a = tid; a < A; a += kSelThreads) {
-      int lo = 0, hi = np - 1;  // parent = largest u with offset[u] <= a
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (en.cnt[mid] <= a) lo = mid;
-        else hi = mid - 1;
-      }
-      const int u = lo, kth = a - en.cnt[u];
-      double Su = 0.0;
-      int du = 0, cu = 0, pe = -1;
-      uint64_t lh = 0, ll = 0;
+    auto parent = [&](int u, double& S, int& d, int& c, int& pe) {
+      S = 0.0;
+      d = 0;
+      c = 0;
+      pe = -1;
       if (!(root && u == 0)) {
         pe = g0 + u - root;
-        Su = en.eS[pe];
-        du = en.eDep[pe];
-        cu = en.eRank[pe];
+        S = en.eS[pe];
+        d = en.eDep[pe];
+        c = en.eRank[pe];
+      }
+    };
+    auto load = [&](int u, float& v0, float& v1) {
+      v0 = -INFINITY;
+      v1 = -INFINITY;
+      if (u >= np) return;
+      double S;
+      int d, c, pe;
+      parent(u, S, d, c, pe);
+      if (d < L) {
+        const float* r = R.row(d, c);
+        if (lane < C) v0 = r[lane];
+        if (lane + kWave < C) v1 = r[lane + kWave];
+      }
+    };
+    float n0, n1;
+    load(wv, n0, n1);
+    for (int u = wv; u < np; u += kSelWaves) {
+      const float v0 = n0, v1 = n1;
+      load(u + kSelWaves, n0, n1);  // the wave's next parent, in flight meanwhile
+      double S;
+      int d, c, pe;
+      parent(u, S, d, c, pe);
+      if (d >= L) continue;
+      const int bj = R.best(d, c);
+      const int j0 = lane, j1 = lane + kWave;
+      const bool q0 = j0 < C && j0 != bj && S + (double)v0 >= tau;
+      const bool q1 = j1 < C && j1 != bj && S + (double)v1 >= tau;
+      const uint64_t m0 = __ballot(q0), m1 = __ballot(q1);
+      if ((m0 | m1) == 0) continue;
+      const int32_t* tk = tb.tok + d * C;
+      const int t0 = j0 < C ? tk[j0] : 0x7FFFFFFF, t1 = j1 < C ? tk[j1] : 0x7FFFFFFF;
+      int rk0 = 1, rk1 = 1;
+      for (uint64_t m = m0; m; m &= m - 1) {
+        const int src = __builtin_ctzll(m);
+        const float v = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v0), src));
+        const int t = __builtin_amdgcn_readlane(t0, src);
+        rk0 += sp_better(v, t, v0, t0) ? 1 : 0;
+        rk1 += sp_better(v, t, v1, t1) ? 1 : 0;
+      }
+      for (uint64_t m = m1; m; m &= m - 1) {
+        const int src = __builtin_ctzll(m);
+        const float v = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v1), src));
+        const int t = __builtin_amdgcn_readlane(t1, src);
+        rk0 += sp_better(v, t, v0, t0) ? 1 : 0;
+        rk1 += sp_better(v, t, v1, t1) ? 1 : 0;
+      }
+      uint64_t lh = 0, ll = 0;
+      if (pe >= 0) {
         lh = en.eLh[pe];
         ll = en.eLl[pe] & ~63ull;
       }
-      // the kth qualifying deviating child of u's row (candidate order)
-      const float* r = R.row(du, cu);
-      const int bj = R.best(du, cu);
-      int j = -1, seen = 0;
-      for (int q = 0; q < C && j < 0; ++q) {
-        if (q != bj && Su + (double)r[q] >= tau) {
-          if (seen == kth) j = q;
-          ++seen;
+      // the anchor (child j of the parent, score S + v, rank rk) and its
+      // best-child extensions while they reach tau
+      auto emit = [&](int j, float v, int rk) {
+        const int dn = d + 1;
+        const double Sa = S + (double)v;
+        uint64_t ah = lh, al = ll;
+        lex_set_digit(ah, al, dn, (uint32_t)rk, bpd);
+        int ell = 1;
+        {
+          double S2 = Sa;
+          int c2 = j;
+          for (int dd = dn + 1; dd <= L; ++dd) {
+            S2 += (double)R.best_lp(dd - 1, c2);
+            if (S2 < tau) break;
+            c2 = R.best(dd - 1, c2);
+            ++ell;
+          }
         }
-      }
-      if (j < 0) {  // cannot happen: the same test counted it
-        sm.ovf = 1;
-        continue;
-      }
-      const int d = du + 1;
-      const double S = Su + (double)r[j];
-      lex_set_digit(lh, ll, d, (uint32_t)R.rank(du, cu, j), bpd);
-      // chain length: the anchor, then best children while they reach tau
-      int ell = 1;
-      {
-        double S2 = S;
+        const int pos = atomicAdd(&sm.nE, ell);
+        if (pos + ell > kECap) {
+          sm.ovf = 1;
+          return;
+        }
+        en.eS[pos] = Sa;
+        en.eSc[pos] = Sa;
+        en.ePar[pos] = (int16_t)pe;
+        en.eRank[pos] = (uint16_t)j;
+        en.eDep[pos] = (uint8_t)dn;
+        en.eLh[pos] = ah;
+        en.eLl[pos] = al | (uint64_t)dn;
+        double S2 = Sa;
         int c2 = j;
-        for (int dd = d + 1; dd <= L; ++dd) {
+        for (int k = 1; k < ell; ++k) {
+          const int dd = dn + k;
           S2 += (double)R.best_lp(dd - 1, c2);
-          if (S2 < tau) break;
           c2 = R.best(dd - 1, c2);
-          ++ell;
+          const int q = pos + k;
+          en.eS[q] = S2;
+          en.eSc[q] = S2;
+          en.ePar[q] = (int16_t)(q - 1);
+          en.eRank[q] = (uint16_t)c2;
+          en.eDep[q] = (uint8_t)dd;
+          en.eLh[q] = ah;
+          en.eLl[q] = al | (uint64_t)dd;
         }
-      }
-      const int pos = atomicAdd(&sm.nE, ell);
-      if (pos + ell > kECap) {
-        sm.ovf = 1;
-        continue;
-      }
-      en.eS[pos] = S;
-      en.eSc[pos] = S;
-      en.ePar[pos] = (int16_t)pe;
-      en.eRank[pos] = (uint16_t)j;
-      en.eDep[pos] = (uint8_t)d;
-      en.eLh[pos] = lh;
-      en.eLl[pos] = ll | (uint64_t)d;
-      double S2 = S;
-      int c2 = j;
-      for (int i = 1; i < ell; ++i) {
-        const int dd = d + i;
-        S2 += (double)R.best_lp(dd - 1, c2);
-        c2 = R.best(dd - 1, c2);
-        const int q = pos + i;
-        en.eS[q] = S2;
-        en.eSc[q] = S2;
-        en.ePar[q] = (int16_t)(q - 1);
-        en.eRank[q] = (uint16_t)c2;
-        en.eDep[q] = (uint8_t)dd;
-        en.eLh[q] = lh;
-        en.eLl[q] = ll | (uint64_t)dd;
-      }
+      };
+      if (q0) emit(j0, v0, rk0);
+      if (q1) emit(j1, v1, rk1);
     }
     __syncthreads();
     if (sm.ovf) break;
     g0 = g1;
     g1 = sm.nE;
     root = 0;
+    __syncthreads();  // every wave has read nE before the next generation appends
     if (g0 == g1) break;
   }
 
