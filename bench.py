@@ -183,6 +183,48 @@ def sparkling_bench(args) -> int:
     return 0
 
 
+def dspark_bench(args) -> int:
+    """DSpark's verification budget over 256 active requests with blocks of
+    16 guesses (4096 slots), cost 25 ms + 0.1 ms per verified token; one
+    step = one dspark_budget call (survival, ranking, budget, lengths)."""
+    import numpy as np
+    import torch
+
+    import draft_tree_construction_depth_amd as pkg
+    from draft_tree_construction_depth_amd import gen
+
+    c = gen.DSPARK
+    batch, P = c["batch"], c["P"]
+    conf, cost = gen.dspark_inputs(0)
+    dev = torch.device("cuda:0")
+    cd, kd = torch.from_numpy(conf).to(dev), torch.from_numpy(cost).to(dev)
+    out = pkg.dspark_budget(cd, kd)
+    for _ in range(args.warmup):
+        pkg.dspark_budget(cd, kd, out=out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(args.steps):
+        pkg.dspark_budget(cd, kd, out=out)
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = a.elapsed_time(b) / args.steps
+    res = {
+        "metric": "DSpark budget decisions/sec at 256 requests x 16 guesses",
+        "value": round(1e3 / ms, 1), "unit": "decisions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": "dspark_budget_batch256_P16", "batch": batch, "P": P,
+                   "cost": "25 ms + 0.1 ms per token"},
+        "n_keep": int(out["n_keep"].item()), "wall_s": round(wall, 3),
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 # Verifier cache of the KV-compaction workload: Qwen3-8B's attention shape
 # (36 layers, 8 KV heads, head dim 128, bf16), 1024 tokens of context.
 KV_LAYERS, KV_HEADS, KV_DH, KV_PAST = 36, 8, 128, 1024
@@ -263,6 +305,8 @@ def main() -> int:
                     help="time treespark_expand on the TreeSpark workload instead (own JSON line)")
     ap.add_argument("--sparkling", action="store_true",
                     help="time sparkling_build on the SparklingTree workload instead (own JSON line)")
+    ap.add_argument("--dspark", action="store_true",
+                    help="time dspark_budget on 256 requests x 16 guesses instead (own JSON line)")
     ap.add_argument("--kv-compact", action="store_true",
                     help="time ddtree_compact_kv after a batch-64 round instead (own JSON line)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -298,6 +342,8 @@ def main() -> int:
         return kv_bench(args)
     if args.sparkling:
         return sparkling_bench(args)
+    if args.dspark:
+        return dspark_bench(args)
 
     c = gen.CONFIGS[3]
     batch, L, V, B = c["batch"], c["L"], c["V"], c["B"]

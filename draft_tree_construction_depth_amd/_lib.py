@@ -66,6 +66,8 @@ def lib() -> C.CDLL:
         L.sparkling_build.restype = C.c_int
         L.sparkling_build.argtypes = [p, C.c_int, p, p, i64, i32, i64, i32, i32, i32, p, p, p, p,
                                       p, p, p, sz, p]
+        L.dspark_budget.restype = C.c_int
+        L.dspark_budget.argtypes = [p, i64, i32, p, i32, p, p, p, p, p, p]
         _lib = L
     return _lib
 
@@ -323,4 +325,29 @@ def sparkling_build(logits: torch.Tensor, W1: torch.Tensor, W2t: torch.Tensor, B
                                _ptr(out.get("depths")), _ptr(out["num_nodes"]),
                                _ptr(out.get("mask")), _ptr(ws), ws.numel(), _stream(dev))
     _check("sparkling_build", rc)
+    return out
+
+
+def dspark_budget(conf: torch.Tensor, cost_ms: torch.Tensor, *, out: dict | None = None) -> dict:
+    """DSpark budget: conf [batch, P] float32, cost_ms [n_cost] float32 (cuda) ->
+    keep [batch], n_keep [1], survival [batch, P], expected_tokens [1], objective [1]."""
+    _arg(conf, "conf", (torch.float32,))
+    if conf.dim() != 2:
+        raise ValueError("conf must be [batch, P]")
+    _arg(cost_ms, "cost_ms", (torch.float32,))
+    if cost_ms.dim() != 1:
+        raise ValueError("cost_ms must be 1-D")
+    batch, P = conf.shape
+    dev = conf.device
+    if out is None:
+        out = dict(keep=torch.empty((batch,), dtype=torch.int32, device=dev),
+                   n_keep=torch.empty((1,), dtype=torch.int32, device=dev),
+                   survival=torch.empty((batch, P), dtype=torch.float64, device=dev),
+                   expected_tokens=torch.empty((1,), dtype=torch.float64, device=dev),
+                   objective=torch.empty((1,), dtype=torch.float64, device=dev))
+    rc = lib().dspark_budget(_ptr(conf), batch, P, _ptr(cost_ms), cost_ms.numel(),
+                             _ptr(out["keep"]), _ptr(out.get("survival")), _ptr(out["n_keep"]),
+                             _ptr(out.get("expected_tokens")), _ptr(out.get("objective")),
+                             _stream(dev))
+    _check("dspark_budget", rc)
     return out

@@ -10,6 +10,7 @@
 #include "walk.hpp"
 #include "kv.hpp"
 #include "sparkling.hpp"
+#include "dspark.hpp"
 
 namespace {
 
@@ -673,6 +674,29 @@ int sparkling_build(const void* logits, int dtype, const uint16_t* W1, const uin
   sp.sp_blp = blp;
   hipLaunchKernelGGL(ddt::sp_select_kernel, dim3((unsigned)batch), dim3(ddt::kSelThreads), 0,
                      stream, sp);
+  return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
+}
+
+int dspark_budget(const float* conf, int64_t batch, int32_t P, const float* cost_ms,
+                  int32_t n_cost, int32_t* keep, double* survival, int32_t* n_keep,
+                  double* expected_tokens, double* objective, hipStream_t stream) {
+  if (batch < 0 || P <= 0) return DDT_EINVAL;
+  if (batch == 0) return DDT_OK;
+  if (batch * P > ddt::kDsMaxN) return DDT_ENOTSUP;
+  if (n_cost <= batch) return DDT_EINVAL;  // the step without guesses must be costed
+  if (!conf || !cost_ms || !keep || !n_keep) return DDT_EINVAL;
+  ddt::DsParams dp;
+  dp.conf = conf;
+  dp.R = (int32_t)batch;
+  dp.P = P;
+  dp.cost = cost_ms;
+  dp.n_cost = n_cost;
+  dp.keep = keep;
+  dp.survival = survival;
+  dp.n_keep = n_keep;
+  dp.expected = expected_tokens;
+  dp.objective = objective;
+  hipLaunchKernelGGL(ddt::dspark_budget_kernel, dim3(1), dim3(ddt::kDsThreads), 0, stream, dp);
   return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
 }
 

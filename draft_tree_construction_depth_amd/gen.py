@@ -247,3 +247,34 @@ def sparkling_inputs(seed: int = 0, *, batch: int | None = None, first: int = 0,
                                peak=c3["peak"], dtype=c3["dtype"]) for b in range(batch)])
     return x, sparkling_factor(seed, 1, V=V, R=R, wscale=wscale), sparkling_factor(seed, 2, V=V, R=R,
                                                                                  wscale=wscale)
+
+
+# DSpark budget workload: 256 active requests with blocks of 16 guesses (the
+# long end of the 4-16 token blocks the pages report), and the DSpark guide's
+# made-up step cost of 25 ms plus 0.1 ms per verified token.
+DSPARK = dict(batch=256, P=16, c0=25.0, c1=0.1)
+CFG_DSPARK = 7
+
+
+def dspark_inputs(seed: int = 0, *, batch: int | None = None, P: int | None = None,
+                  c0: float | None = None, c1: float | None = None):
+    """(conf [batch, P] float32, cost [batch * (P + 1) + 1] float32 ms).
+
+    conf[b][p] = clip(u_b - delta_b * p + N(0, 0.05^2), 0.01, 0.999) with a
+    per-request level u_b ~ U[0.35, 0.98] and decay delta_b ~ U[0, 0.06]:
+    confident and unsure requests side by side, each falling along its block.
+    cost[T] = c0 + c1 * T.
+    """
+    c = DSPARK
+    batch = c["batch"] if batch is None else batch
+    P = c["P"] if P is None else P
+    c0 = c["c0"] if c0 is None else c0
+    c1 = c["c1"] if c1 is None else c1
+    rng = _rng(CFG_DSPARK, seed, 0)
+    u = rng.uniform(0.35, 0.98, (batch, 1))
+    dl = rng.uniform(0.0, 0.06, (batch, 1))
+    conf = u - dl * np.arange(P)[None, :] + rng.normal(0.0, 0.05, (batch, P))
+    conf = np.clip(conf, 0.01, 0.999).astype(np.float32)
+    T = np.arange(batch * (P + 1) + 1, dtype=np.float64)
+    cost = (c0 + c1 * T).astype(np.float32)
+    return conf, cost

@@ -29,6 +29,9 @@
  *    the candidate tree construction" (the head looks back one token, so the
  *    deltas between consecutive rows' candidates form a table computed up
  *    front; best-first growth on the conditioned rows).
+ *  - dspark_budget: DSpark's survival-ranked verification budget. DSpark
+ *    explainer, section "Hardware aware prefix scheduler"; DSpark guide,
+ *    sections "Survival probability" and "Picking the budget".
  *  - ddtree_select: stage 2 alone, from stage 1's tables. DDTree explainer,
  *    sections 3-4; SparklingTree post, section "Step 3".
  *    ddtree_build = ddtree_row_topk + ddtree_select in one call.
@@ -276,6 +279,35 @@ int sparkling_build(const void* logits, int dtype, const uint16_t* W1, const uin
                     int32_t* tree_tokens, int32_t* parents, float* logq, int32_t* depths,
                     int32_t* num_nodes, uint64_t* mask, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
+
+/*
+ * dspark_budget -- DSpark's hardware-aware prefix scheduler (DSpark explainer,
+ * "Hardware aware prefix scheduler"; DSpark guide, "Survival probability",
+ * "Picking the budget"). For the R = batch active requests with block
+ * confidences conf[b][p] (the chance guess p survives if every earlier one
+ * did; clamped into [0, 1], NaN as 0):
+ *   survival[b][p] = conf[b][0] * ... * conf[b][p] (float64, left to right);
+ *   every slot ranks by survival desc, then request asc, then position asc;
+ *   keeping the first n slots costs cost_ms[R + n] (one target step over
+ *   R + n tokens: each request's last token plus its kept guesses) and is
+ *   expected to yield R + (sum of the kept survivals) tokens;
+ *   n = the count maximising expected tokens / cost over n = 0..min(R*P,
+ *   n_cost-1-R) (the smallest such n among equal maxima).
+ * conf [batch][P] float, cost_ms [n_cost] float (positive; n_cost > batch),
+ * both device memory.
+ * Outputs: keep [batch] int32 (each request keeps the first keep[b] guesses
+ * of its block), n_keep [1] int32 = n, survival [batch][P] float64
+ * (nullable), expected_tokens [1] float64 (nullable), objective [1] float64
+ * expected tokens per ms (nullable).
+ * The scan of expected tokens sums in a tree order: within about 1e-15
+ * relative of a sequential sum, so n can differ from a sequential
+ * evaluation only between counts whose objectives agree that closely.
+ * Supported: batch * P <= 4096 (DDT_ENOTSUP otherwise). One workgroup; no
+ * workspace.
+ */
+int dspark_budget(const float* conf, int64_t batch, int32_t P, const float* cost_ms,
+                  int32_t n_cost, int32_t* keep, double* survival, int32_t* n_keep,
+                  double* expected_tokens, double* objective, hipStream_t stream);
 
 #ifdef __cplusplus
 }

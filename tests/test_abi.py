@@ -26,14 +26,14 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b((?:ddt|ddtree|treespark|sparkling)_[a-z0-9_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:ddt|ddtree|treespark|sparkling|dspark)_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_four_operations():
     names = declared_functions()
     for n in ("ddtree_build", "ddtree_select", "ddtree_mask", "ddtree_accept", "ddtree_row_topk",
               "ddtree_compact_kv", "treespark_expand", "treespark_workspace_size",
-              "sparkling_build", "sparkling_build_workspace_size",
+              "sparkling_build", "sparkling_build_workspace_size", "dspark_budget",
               "ddtree_build_workspace_size", "ddtree_row_topk_workspace_size",
               "ddt_status_string", "ddt_abi_version"):
         assert n in names
@@ -184,3 +184,17 @@ def test_sparkling_validation(L):
     assert call(Lr=33) == -2
     assert call(ws_bytes=64) == -3
     assert call(batch=0) == 0            # nothing to do
+
+
+def test_dspark_validation(L):
+    def call(conf=FAKE, batch=4, P=5, cost=FAKE, n_cost=100, keep=FAKE, n_keep=FAKE):
+        return L.dspark_budget(conf, batch, P, cost, n_cost, keep, None, n_keep, None, None, None)
+    assert call(conf=None) == -1
+    assert call(cost=None) == -1
+    assert call(keep=None) == -1
+    assert call(n_keep=None) == -1
+    assert call(P=0) == -1
+    assert call(batch=-1) == -1
+    assert call(n_cost=4) == -1           # the step without guesses is not costed
+    assert call(batch=1000, P=5) == -2    # more than 4096 slots
+    assert call(batch=0) == 0
