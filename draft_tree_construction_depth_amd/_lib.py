@@ -68,6 +68,9 @@ def lib() -> C.CDLL:
                                       p, p, p, sz, p]
         L.dspark_budget.restype = C.c_int
         L.dspark_budget.argtypes = [p, i64, i32, p, i32, p, p, p, p, p, p]
+        L.sparkling_beam.restype = C.c_int
+        L.sparkling_beam.argtypes = [p, C.c_int, p, p, i64, i32, i64, i32, i32, p, p, p, p, p, p,
+                                     p, p, sz, p]
         _lib = L
     return _lib
 
@@ -350,4 +353,49 @@ def dspark_budget(conf: torch.Tensor, cost_ms: torch.Tensor, *, out: dict | None
                              _ptr(out.get("expected_tokens")), _ptr(out.get("objective")),
                              _stream(dev))
     _check("dspark_budget", rc)
+    return out
+
+
+def even_widths(B: int, L: int) -> list:
+    """The budget B spread over L depths as evenly as possible (remainder first)."""
+    q, r = divmod(B, L)
+    return [q + (1 if d < r else 0) for d in range(L)]
+
+
+def sparkling_beam(logits: torch.Tensor, W1: torch.Tensor, W2t: torch.Tensor, widths=None, *,
+                   B: int | None = None, C: int = 128, with_mask: bool = True,
+                   out: dict | None = None, ws: torch.Tensor | None = None) -> dict:
+    """Beam tree on SparklingTree's rows: per-depth widths (default: B spread evenly)."""
+    _arg(logits, "logits", _LOGITS)
+    if logits.dim() != 3:
+        raise ValueError("logits must be [batch, L, V]")
+    batch, L, V = logits.shape
+    _arg(W1, "W1", _BF16)
+    if W1.dim() != 2 or W1.shape[0] != V:
+        raise ValueError(f"W1 must be [{V}, R]")
+    R = W1.shape[1]
+    _arg(W2t, "W2t", _BF16, (V, R))
+    if widths is None:
+        if B is None:
+            raise ValueError("give widths or a budget B")
+        widths = even_widths(B, L)
+    widths = [int(w) for w in widths]
+    if len(widths) != L:
+        raise ValueError(f"widths must have {L} entries")
+    Bt = sum(widths)
+    dev = logits.device
+    dt = _dtype_code(logits)
+    if out is None:
+        out = _tree_out(batch, max(Bt, 1), dev, with_mask)
+    size = lib().sparkling_build_workspace_size(batch, L, V, C, R, max(Bt, 1), dt)
+    if ws is None:
+        ws = workspace("sparkling", size, dev, (batch, L, V, C, R, max(Bt, 1), dt))
+    import ctypes  # (the argument C shadows the module alias)
+    wa = (ctypes.c_int32 * L)(*widths)
+    rc = lib().sparkling_beam(_ptr(logits), dt, _ptr(W1), _ptr(W2t), batch, L, V, C, R,
+                              ctypes.cast(wa, ctypes.c_void_p),
+                              _ptr(out["tree_tokens"]), _ptr(out["parents"]), _ptr(out["logq"]),
+                              _ptr(out.get("depths")), _ptr(out["num_nodes"]),
+                              _ptr(out.get("mask")), _ptr(ws), ws.numel(), _stream(dev))
+    _check("sparkling_beam", rc)
     return out

@@ -11,6 +11,7 @@
 #include "kv.hpp"
 #include "sparkling.hpp"
 #include "dspark.hpp"
+#include "beam.hpp"
 
 namespace {
 
@@ -323,6 +324,37 @@ SpLayout sp_layout(int64_t batch, int32_t L, int64_t V, int32_t C, int dtype) {
   return l;
 }
 
+// SparklingTree's rows: 1. every drafter row cut to its top C (value desc,
+// id asc); 2. the conditioned child rows (Markov deltas on MFMA, log-probs,
+// best child) into the workspace
+int sp_rows(const void* logits, int dtype, const uint16_t* W1, const uint16_t* W2t, int64_t batch,
+            int32_t L, int64_t V, int32_t C, int32_t R, const S1Plan& pl, const SpLayout& lay,
+            char* ws, hipStream_t stream) {
+  float* tv = (float*)(ws + lay.vals);
+  int32_t* ti = (int32_t*)(ws + lay.ids);
+  double* tz = (double*)(ws + lay.lse);
+  hipError_t e =
+      launch_stage1(dtype, pl, logits, batch * L, V, C, lay.s1, ws, ti, tv, tz, stream);
+  if (e != hipSuccess) return DDT_EHIP;
+  if (L > 1) {
+    ddt::SpTableParams tp;
+    tp.W1 = W1;
+    tp.W2t = W2t;
+    tp.ids = ti;
+    tp.vals = tv;
+    tp.L = L;
+    tp.C = C;
+    tp.R = R;
+    tp.lp = (float*)(ws + lay.lp);
+    tp.best = (uint8_t*)(ws + lay.best);
+    tp.blp = (float*)(ws + lay.blp);
+    hipLaunchKernelGGL(ddt::sp_table_kernel, dim3((unsigned)batch, (unsigned)(L - 1)),
+                       dim3(ddt::kSpThreads), 0, stream, tp);
+    if (hipGetLastError() != hipSuccess) return DDT_EHIP;
+  }
+  return DDT_OK;
+}
+
 int sp_check(int dtype, int64_t batch, int32_t L, int64_t V, int32_t C, int32_t R, int32_t B) {
   if (!valid_dtype(dtype) || batch < 0 || L <= 0 || V <= 0 || C <= 0 || R <= 0 || B <= 0)
     return DDT_EINVAL;
@@ -632,26 +664,8 @@ int sparkling_build(const void* logits, int dtype, const uint16_t* W1, const uin
   float* lp = (float*)(ws + lay.lp);
   uint8_t* best = (uint8_t*)(ws + lay.best);
   float* blp = (float*)(ws + lay.blp);
-  // 1. every drafter row cut to its top C (value desc, id asc)
-  hipError_t e = launch_stage1(dtype, pl, logits, rows, V, C, lay.s1, ws, ti, tv, tz, stream);
-  if (e != hipSuccess) return DDT_EHIP;
-  // 2. the conditioned child rows: Markov deltas on MFMA, log-probs, best child
-  if (L > 1) {
-    ddt::SpTableParams tp;
-    tp.W1 = W1;
-    tp.W2t = W2t;
-    tp.ids = ti;
-    tp.vals = tv;
-    tp.L = L;
-    tp.C = C;
-    tp.R = R;
-    tp.lp = lp;
-    tp.best = best;
-    tp.blp = blp;
-    hipLaunchKernelGGL(ddt::sp_table_kernel, dim3((unsigned)batch, (unsigned)(L - 1)),
-                       dim3(ddt::kSpThreads), 0, stream, tp);
-    if (hipGetLastError() != hipSuccess) return DDT_EHIP;
-  }
+  if (sp_rows(logits, dtype, W1, W2t, batch, L, V, C, R, pl, lay, ws, stream) != DDT_OK)
+    return DDT_EHIP;
   // 3. best-first selection on the conditioned rows, then the mask
   ddt::SelectParams sp;
   sp.vals = tv;
@@ -697,6 +711,61 @@ int dspark_budget(const float* conf, int64_t batch, int32_t P, const float* cost
   dp.expected = expected_tokens;
   dp.objective = objective;
   hipLaunchKernelGGL(ddt::dspark_budget_kernel, dim3(1), dim3(ddt::kDsThreads), 0, stream, dp);
+  return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
+}
+
+int sparkling_beam(const void* logits, int dtype, const uint16_t* W1, const uint16_t* W2t,
+                   int64_t batch, int32_t L, int64_t V, int32_t C, int32_t R,
+                   const int32_t* widths, int32_t* tree_tokens, int32_t* parents, float* logq,
+                   int32_t* depths, int32_t* num_nodes, uint64_t* mask, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  if (!widths || L <= 0) return DDT_EINVAL;
+  if (L > DDT_MAX_L) return DDT_ENOTSUP;
+  int32_t B = 0;
+  for (int d = 0; d < L; ++d) {
+    if (widths[d] < 0) return DDT_EINVAL;
+    if (widths[d] > ddt::kBmMaxW) return DDT_ENOTSUP;
+    B += widths[d];
+  }
+  if (B <= 0) return DDT_EINVAL;
+  const int chk = sp_check(dtype, batch, L, V, C, R, B);
+  if (chk != DDT_OK) return chk;
+  if (batch == 0) return DDT_OK;
+  if (!logits || !W1 || !W2t || !tree_tokens || !parents || !logq || !num_nodes || !workspace)
+    return DDT_EINVAL;
+  if ((uintptr_t)logits % 16 != 0 || (uintptr_t)W1 % 16 != 0 || (uintptr_t)W2t % 16 != 0)
+    return DDT_EINVAL;
+  const int64_t rows = batch * L;
+  const S1Plan pl = plan_stage1(rows, V, dtype, C);
+  if (!pl.ok || rows * pl.S > 0x7FFFFFFFLL) return DDT_ENOTSUP;
+  const SpLayout lay = sp_layout(batch, L, V, C, dtype);
+  if (workspace_bytes < lay.end) return DDT_EWORKSPACE;
+  char* ws = (char*)workspace;
+  if (sp_rows(logits, dtype, W1, W2t, batch, L, V, C, R, pl, lay, ws, stream) != DDT_OK)
+    return DDT_EHIP;
+  ddt::BeamParams bp;
+  ddt::SelectParams& sp = bp.sp;
+  sp.vals = (const float*)(ws + lay.vals);
+  sp.ids = (const int32_t*)(ws + lay.ids);
+  sp.lse = (const double*)(ws + lay.lse);
+  sp.batch = batch;
+  sp.L = L;
+  sp.K = C;
+  sp.B = B;
+  sp.bpd = ceil_log2(C) < 1 ? 1 : ceil_log2(C);
+  sp.tree_tokens = tree_tokens;
+  sp.parents = parents;
+  sp.logq = logq;
+  sp.depths = depths;
+  sp.num_nodes = num_nodes;
+  sp.mask = mask;
+  sp.W = (B + 1 + 63) / 64;
+  sp.sp_lp = (const float*)(ws + lay.lp);
+  sp.sp_best = (const uint8_t*)(ws + lay.best);
+  sp.sp_blp = (const float*)(ws + lay.blp);
+  for (int d = 0; d < ddt::kMaxL; ++d) bp.widths[d] = d < L ? widths[d] : 0;
+  hipLaunchKernelGGL(ddt::beam_kernel, dim3((unsigned)batch), dim3(ddt::kSelThreads), 0, stream,
+                     bp);
   return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
 }
 

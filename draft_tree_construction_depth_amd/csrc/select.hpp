@@ -433,13 +433,14 @@ __device__ __forceinline__ void sel_order_emit(const SelectParams& p, SelectSmem
   __syncthreads();
 }
 
-// Phase 4: the bit-packed ancestor mask from the emitted parents.
-__device__ __forceinline__ void sel_mask(const SelectParams& p, SelectSmem& sm, int64_t b) {
+// Phase 4: the bit-packed ancestor mask from the emitted parents (opar[j] =
+// parent node number of node j+1, in LDS; nodes past nsel get zero rows).
+__device__ __forceinline__ void sel_mask_rows(const SelectParams& p, const int* opar, int nsel,
+                                              int64_t b) {
   const int tid = threadIdx.x;
   const int B = p.B;
-  // ---- 4. ancestor mask ------------------------------------------------------
   if (p.mask) {
-    const int nsel = sm.nsel, W = p.W;
+    const int W = p.W;
     for (int i = tid; i <= B; i += kSelThreads) {
       uint64_t m[kMaxW];
 #pragma unroll
@@ -452,7 +453,7 @@ __device__ __forceinline__ void sel_mask(const SelectParams& p, SelectSmem& sm, 
 #pragma unroll
           for (int q = 0; q < kMaxW; ++q) m[q] |= (q == wq) ? bit : 0ull;
           if (u == 0) break;
-          u = sm.opar[u - 1];
+          u = opar[u - 1];
         }
       }
       uint64_t* dst = p.mask + ((size_t)b * (B + 1) + i) * W;
@@ -461,6 +462,10 @@ __device__ __forceinline__ void sel_mask(const SelectParams& p, SelectSmem& sm, 
         if (q < W) dst[q] = m[q];
     }
   }
+}
+
+__device__ __forceinline__ void sel_mask(const SelectParams& p, SelectSmem& sm, int64_t b) {
+  sel_mask_rows(p, sm.opar, sm.nsel, b);
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {

@@ -29,6 +29,8 @@
  *    the candidate tree construction" (the head looks back one token, so the
  *    deltas between consecutive rows' candidates form a table computed up
  *    front; best-first growth on the conditioned rows).
+ *  - sparkling_beam: a fixed-branching beam tree on SparklingTree's rows.
+ *    SparklingTree post, section "Future Ideas", item 4.
  *  - dspark_budget: DSpark's survival-ranked verification budget. DSpark
  *    explainer, section "Hardware aware prefix scheduler"; DSpark guide,
  *    sections "Survival probability" and "Picking the budget".
@@ -308,6 +310,32 @@ int sparkling_build(const void* logits, int dtype, const uint16_t* W1, const uin
 int dspark_budget(const float* conf, int64_t batch, int32_t P, const float* cost_ms,
                   int32_t n_cost, int32_t* keep, double* survival, int32_t* n_keep,
                   double* expected_tokens, double* objective, hipStream_t stream);
+
+/*
+ * sparkling_beam -- a fixed-branching beam tree on SparklingTree's conditioned
+ * rows (SparklingTree post, "Future Ideas", item 4: a beam with a fixed
+ * branching budget in place of the best-first heap; evenly spread branches).
+ * Rows as sparkling_build (top C candidates per row, the rank-R Markov head,
+ * log-probs over the C candidates). widths [L] is a HOST array: depth 1 keeps
+ * the widths[0] best children of the root; depth d+1 the widths[d] best of all
+ * children of depth d's beam; best = score (sum of lp along the path,
+ * float64) desc, then rank tuple lexicographic asc (a child's rank = its
+ * position in its row by lp desc, token asc). A width above the number of
+ * candidates keeps them all; a zero width ends the tree.
+ * Nodes are emitted depth by depth, each depth in beam order: node j+1 is the
+ * j-th, parents[j] its parent's node number (0 = the root).
+ * Outputs [batch][B] with B = sum of widths (tree_tokens, parents, logq,
+ * depths nullable), num_nodes [batch], mask [batch][B+1][ceil((B+1)/64)]
+ * (nullable); the tail is padded with -1, -1, -inf, 0.
+ * Supported: each width <= 64, B <= DDT_MAX_B, and sparkling_build's limits
+ * on C, R, L and V (DDT_ENOTSUP); a negative width or B = 0: DDT_EINVAL.
+ * Workspace: sparkling_build_workspace_size(batch, L, V, C, R, B, dtype) bytes.
+ */
+int sparkling_beam(const void* logits, int dtype, const uint16_t* W1, const uint16_t* W2t,
+                   int64_t batch, int32_t L, int64_t V, int32_t C, int32_t R,
+                   const int32_t* widths, int32_t* tree_tokens, int32_t* parents, float* logq,
+                   int32_t* depths, int32_t* num_nodes, uint64_t* mask, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

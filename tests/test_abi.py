@@ -34,6 +34,7 @@ def test_header_declares_the_four_operations():
     for n in ("ddtree_build", "ddtree_select", "ddtree_mask", "ddtree_accept", "ddtree_row_topk",
               "ddtree_compact_kv", "treespark_expand", "treespark_workspace_size",
               "sparkling_build", "sparkling_build_workspace_size", "dspark_budget",
+              "sparkling_beam",
               "ddtree_build_workspace_size", "ddtree_row_topk_workspace_size",
               "ddt_status_string", "ddt_abi_version"):
         assert n in names
@@ -197,4 +198,24 @@ def test_dspark_validation(L):
     assert call(batch=-1) == -1
     assert call(n_cost=4) == -1           # the step without guesses is not costed
     assert call(batch=1000, P=5) == -2    # more than 4096 slots
+    assert call(batch=0) == 0
+
+
+def test_sparkling_beam_validation(L):
+    f = L.sparkling_beam
+
+    def call(widths=(4,) * 15, Lr=15, Cc=128, R=256, batch=2, out=FAKE, wsp=FAKE, ws_bytes=1 << 34):
+        wa = None if widths is None else (C_int32 * len(widths))(*widths)
+        return f(FAKE, 0, FAKE, FAKE, batch, Lr, 1024, Cc, R,
+                 None if wa is None else C.cast(wa, C.c_void_p), out, out, out, out, out, out,
+                 wsp, ws_bytes, None)
+    C_int32 = C.c_int32
+    assert call(widths=None) == -1
+    assert call(widths=(0,) * 15) == -1          # empty budget
+    assert call(widths=(-1,) + (4,) * 14) == -1
+    assert call(widths=(65,) + (4,) * 14) == -2  # a width above 64
+    assert call(widths=(64,) * 9, Lr=9) == -2    # B = 576 > 512
+    assert call(Cc=200) == -2
+    assert call(out=None) == -1
+    assert call(ws_bytes=64) == -3
     assert call(batch=0) == 0
