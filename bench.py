@@ -183,6 +183,52 @@ def sparkling_bench(args) -> int:
     return 0
 
 
+def beam_bench(args) -> int:
+    """Beam tree on SparklingTree's rows: the --sparkling workload with the
+    budget B = 64 spread evenly over the 15 depths; one step = one
+    sparkling_beam call (top-C rows, Markov-delta table, beam + mask)."""
+    import numpy as np
+    import torch
+
+    import draft_tree_construction_depth_amd as pkg
+    from draft_tree_construction_depth_amd import gen
+
+    c = gen.SPARKLING
+    batch, L, V, B, C, R = (c[x] for x in ("batch", "L", "V", "B", "C", "R"))
+    widths = pkg.even_widths(B, L)
+    x, W1, W2t = gen.sparkling_inputs(0)
+    dev = torch.device("cuda:0")
+    as_bf16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
+        torch.bfloat16)
+    xs = [as_bf16(x), as_bf16(gen.sparkling_inputs(1)[0])]
+    W1d, W2d = as_bf16(W1), as_bf16(W2t)
+    out = pkg.sparkling_beam(xs[0], W1d, W2d, widths, C=C)
+    for i in range(args.warmup):
+        pkg.sparkling_beam(xs[i % 2], W1d, W2d, widths, C=C, out=out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for i in range(args.steps):
+        pkg.sparkling_beam(xs[i % 2], W1d, W2d, widths, C=C, out=out)
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = a.elapsed_time(b) / args.steps
+    res = {
+        "metric": "beam trees/sec at batch 64, L=15, V=151936, C=128, R=256, B=64 spread evenly",
+        "value": round(batch / (ms / 1e3), 1), "unit": "trees/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16/f32/f64", "data": "synthetic",
+        "config": {"workload": "beam_batch64_L15_V151936_C128_R256_B64_even", "batch": batch,
+                   "L": L, "V": V, "C": C, "R": R, "widths": widths, "input_buffers": 2},
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def dspark_bench(args) -> int:
     """DSpark's verification budget over 256 active requests with blocks of
     16 guesses (4096 slots), cost 25 ms + 0.1 ms per verified token; one
@@ -307,6 +353,8 @@ def main() -> int:
                     help="time sparkling_build on the SparklingTree workload instead (own JSON line)")
     ap.add_argument("--dspark", action="store_true",
                     help="time dspark_budget on 256 requests x 16 guesses instead (own JSON line)")
+    ap.add_argument("--beam", action="store_true",
+                    help="time sparkling_beam on the SparklingTree workload instead (own JSON line)")
     ap.add_argument("--kv-compact", action="store_true",
                     help="time ddtree_compact_kv after a batch-64 round instead (own JSON line)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -344,6 +392,8 @@ def main() -> int:
         return sparkling_bench(args)
     if args.dspark:
         return dspark_bench(args)
+    if args.beam:
+        return beam_bench(args)
 
     c = gen.CONFIGS[3]
     batch, L, V, B = c["batch"], c["L"], c["V"], c["B"]

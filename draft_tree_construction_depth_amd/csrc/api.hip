@@ -764,7 +764,7 @@ int sparkling_beam(const void* logits, int dtype, const uint16_t* W1, const uint
   sp.sp_best = (const uint8_t*)(ws + lay.best);
   sp.sp_blp = (const float*)(ws + lay.blp);
   for (int d = 0; d < ddt::kMaxL; ++d) bp.widths[d] = d < L ? widths[d] : 0;
-  hipLaunchKernelGGL(ddt::beam_kernel, dim3((unsigned)batch), dim3(ddt::kSelThreads), 0, stream,
+  hipLaunchKernelGGL(ddt::beam_kernel, dim3((unsigned)batch), dim3(ddt::kBmThreads), 0, stream,
                      bp);
   return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
 }

@@ -11,9 +11,11 @@
 // (a child's rank = its position in its row by lp desc, token asc). The tree
 // is every beam node, emitted depth by depth in beam order.
 //
-// MI355X design: one 1024-thread workgroup per request, widths <= 64, so a
-// depth has at most 64 x 128 candidates. Their scores go to LDS; the w-th best
-// is found by a histogram over [min, max] (1024 bins, monotone in the score)
+// MI355X design: one 256-thread workgroup per request (a depth is a chain of
+// short block-synchronous steps: small workgroups synchronise faster),
+// widths <= 64, so a depth has at most 64 x 128 candidates. Their scores and
+// log-probs go to LDS; the w-th best is found by a histogram over [min, max]
+// (256 bins, monotone in the score)
 // and one scan; the bins above the cut are taken whole, the cut bin is
 // resolved exactly with full keys (each member's rank in its row by counting,
 // then counting among the members), or, when it holds more than kBmCut
@@ -27,9 +29,11 @@
 
 namespace ddt {
 
+constexpr int kBmThreads = 256;
+constexpr int kBmWaves = kBmThreads / kWave;
 constexpr int kBmMaxW = 64;
 constexpr int kBmMaxM = kBmMaxW * kSpC;  // candidates of one depth, at most
-constexpr int kBmBins = kSelThreads;
+constexpr int kBmBins = kBmThreads;
 constexpr int kBmCut = 512;  // cut-bin members ranked by counting, at most
 
 struct BeamParams {
@@ -39,6 +43,7 @@ struct BeamParams {
 
 struct BeamSmem {
   double cs[kBmMaxM];         // candidate scores of the current depth
+  float clp[kBmMaxM];         // their log-probs (the beam's rows, in LDS for ranking)
   float lp0[kSpC];            // row 1 over its candidates
   int32_t tok[kSpMaxLC];      // [L][C] candidate tokens
   // the beam of the previous depth (entry u: candidate c, score, rank key, node)
@@ -49,17 +54,30 @@ struct BeamSmem {
   // the selection of the current depth
   int32_t sel[kBmMaxW];       // candidate index m = u * C + j
   int32_t srank[kBmMaxW];     // child rank of each selected candidate
+  double sS[kBmMaxW];         // and its key: score, parent rank key
+  uint64_t sH[kBmMaxW], sL[kBmMaxW];
   int32_t cut[kBmCut];        // members of the cut bin
   int32_t crank[kBmCut];      // their child ranks
-  int16_t mrank[kBmMaxM];     // child ranks of the cut bin's members (tie fallback)
+  double cS[kBmCut];          // and their keys
+  uint64_t cH[kBmCut], cL[kBmCut];
   int hist[kBmBins];
-  alignas(16) int wsum[kSelWaves];
-  double rmin[kSelWaves], rmax[kSelWaves];
-  int opar[kMaxB];
+  alignas(16) int wsum[kBmWaves];
+  double rmin[kBmWaves], rmax[kBmWaves];
+  int opar[kMaxB];            // the tree, written out at the end
+  int otok[kMaxB];
+  float oq[kMaxB];
+  uint8_t odep[kMaxB];
   int nsel, ncut, kcut, kexc, nprev, nout;
   int pick;
   uint64_t taken[kBmMaxM / 64];  // cut members already extracted (fallback)
 };
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its outstanding global memory operations (which
+// __syncthreads() drains as well).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // the child rank of candidate j in row `r` of tokens `t`: entries before it
 // by (lp desc, token asc)
@@ -68,6 +86,20 @@ __device__ __forceinline__ int bm_rank(const float* r, const int32_t* t, int C, 
   const int tj = t[j];
   int n = 0;
   for (int q = 0; q < C; ++q) n += (r[q] > v || (r[q] == v && t[q] < tj)) ? 1 : 0;
+  return n;
+}
+
+// the same, one wavefront for one candidate: two compares a lane, ballots
+__device__ __forceinline__ int bm_rank_wave(const float* r, const int32_t* t, int C, int j) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const float v = r[j];
+  const int tj = t[j];
+  int n = 0;
+  for (int q0 = 0; q0 < C; q0 += kWave) {
+    const int q = q0 + lane;
+    const bool bt = q < C && (r[q] > v || (r[q] == v && t[q] < tj));
+    n += __popcll(__ballot(bt));
+  }
   return n;
 }
 
@@ -81,14 +113,14 @@ __device__ __forceinline__ bool bm_before(double sa, uint64_t ha, uint64_t la, i
   return ra < rb;
 }
 
-__global__ __launch_bounds__(kSelThreads) void beam_kernel(BeamParams bp) {
+__global__ __launch_bounds__(kBmThreads) void beam_kernel(BeamParams bp) {
   __shared__ BeamSmem sm;
   const SelectParams& p = bp.sp;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t b = blockIdx.x;
   const int L = p.L, C = p.K, B = p.B, LC = L * C, bpd = p.bpd;
   const float* lpb = p.sp_lp + (size_t)b * (L - 1) * C * C;
-  for (int i = tid; i < LC; i += kSelThreads) sm.tok[i] = p.ids[(size_t)b * LC + i];
+  for (int i = tid; i < LC; i += kBmThreads) sm.tok[i] = p.ids[(size_t)b * LC + i];
   if (wv == 0) {
     // row 1 over its candidates (as the SparklingTree selection)
     const float* v0 = p.vals + (size_t)b * LC;
@@ -135,18 +167,26 @@ __global__ __launch_bounds__(kSelThreads) void beam_kernel(BeamParams bp) {
     };
     // ---- candidate scores, their range --------------------------------------
     double mn = INFINITY, mxs = -INFINITY;
-    for (int m = tid; m < M; m += kSelThreads) {
+    for (int m = tid; m < M; m += kBmThreads) {
       const int u = m / C, j = m - u * C;
-      const double s = sm.bS[u] + (double)row(u)[j];
+      const float v = row(u)[j];
+      const double s = sm.bS[u] + (double)v;
       sm.cs[m] = s;
+      sm.clp[m] = v;
       mn = s < mn ? s : mn;
       mxs = s > mxs ? s : mxs;
     }
     int nsel = 0;  // candidates taken before the cut bin's
     if (w >= M) {
-      for (int m = tid; m < M; m += kSelThreads) sm.sel[m] = m;
+      for (int m = tid; m < M; m += kBmThreads) {
+        const int u = m / C;
+        sm.sel[m] = m;
+        sm.sS[m] = sm.cs[m];
+        sm.sH[m] = sm.bh[u];
+        sm.sL[m] = sm.bl[u];
+      }
       nsel = M;
-      __syncthreads();
+      lds_barrier();
     } else {
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
@@ -163,10 +203,10 @@ __global__ __launch_bounds__(kSelThreads) void beam_kernel(BeamParams bp) {
         sm.ncut = 0;
         sm.nsel = 0;
       }
-      __syncthreads();
+      lds_barrier();
       mn = sm.rmin[0];
       mxs = sm.rmax[0];
-      for (int q = 1; q < kSelWaves; ++q) {
+      for (int q = 1; q < kBmWaves; ++q) {
         mn = sm.rmin[q] < mn ? sm.rmin[q] : mn;
         mxs = sm.rmax[q] > mxs ? sm.rmax[q] : mxs;
       }
@@ -176,13 +216,13 @@ __global__ __launch_bounds__(kSelThreads) void beam_kernel(BeamParams bp) {
         const double t = (mxs - s) * scale;
         return t >= (double)(kBmBins - 1) ? kBmBins - 1 : (t > 0.0 ? (int)t : 0);
       };
-      for (int m = tid; m < M; m += kSelThreads) atomicAdd(&sm.hist[bin_of(sm.cs[m])], 1);
-      __syncthreads();
+      for (int m = tid; m < M; m += kBmThreads) atomicAdd(&sm.hist[bin_of(sm.cs[m])], 1);
+      lds_barrier();
       {
         const int h = sm.hist[tid];
         const int x = wave_incl_scan(h);
         if (lane == kWave - 1) sm.wsum[wv] = x;
-        __syncthreads();
+        lds_barrier();
         int pre = 0;
         for (int q = 0; q < wv; ++q) pre += sm.wsum[q];
         const int inc = pre + x, exc = inc - h;
@@ -191,60 +231,69 @@ __global__ __launch_bounds__(kSelThreads) void beam_kernel(BeamParams bp) {
           sm.kexc = exc;
         }
       }
-      __syncthreads();
+      lds_barrier();
       const int kc = sm.kcut;
       nsel = sm.kexc;  // taken whole: the bins before the cut
-      for (int m = tid; m < M; m += kSelThreads) {
-        const int bn = bin_of(sm.cs[m]);
-        if (bn < kc) sm.sel[atomicAdd(&sm.nsel, 1)] = m;
-        else if (bn == kc) {
+      for (int m = tid; m < M; m += kBmThreads) {
+        const double sc = sm.cs[m];
+        const int bn = bin_of(sc);
+        const int u = m / C;
+        if (bn < kc) {
+          const int k = atomicAdd(&sm.nsel, 1);
+          sm.sel[k] = m;
+          sm.sS[k] = sc;
+          sm.sH[k] = sm.bh[u];
+          sm.sL[k] = sm.bl[u];
+        } else if (bn == kc) {
           const int k = atomicAdd(&sm.ncut, 1);
-          if (k < kBmCut) sm.cut[k] = m;
+          if (k < kBmCut) {
+            sm.cut[k] = m;
+            sm.cS[k] = sc;
+            sm.cH[k] = sm.bh[u];
+            sm.cL[k] = sm.bl[u];
+          }
         }
       }
-      __syncthreads();
+      lds_barrier();
       const int nc = sm.ncut, need = w - nsel;
       if (nc <= kBmCut) {
         // members' child ranks, then their order by full key
-        for (int k = tid; k < nc; k += kSelThreads) {
+        for (int k = wv; k < nc; k += kBmWaves) {
           const int m = sm.cut[k], u = m / C;
-          sm.crank[k] = bm_rank(row(u), tk, C, m - u * C);
+          const int r = bm_rank_wave(sm.clp + u * C, tk, C, m - u * C);
+          if (lane == 0) sm.crank[k] = r;
         }
-        __syncthreads();
-        for (int k = tid; k < nc; k += kSelThreads) {
-          const int m = sm.cut[k], u = m / C;
-          const double s = sm.cs[m];
-          const uint64_t h = sm.bh[u], l = sm.bl[u];
+        lds_barrier();
+        for (int k = tid; k < nc; k += kBmThreads) {
+          const double s = sm.cS[k];
+          const uint64_t h = sm.cH[k], l = sm.cL[k];
           const int r = sm.crank[k];
           int pos = 0;
-          for (int q = 0; q < nc; ++q) {
-            const int mq = sm.cut[q], uq = mq / C;
-            pos += bm_before(sm.cs[mq], sm.bh[uq], sm.bl[uq], sm.crank[q], s, h, l, r) ? 1 : 0;
-          }
+          for (int q = 0; q < nc; ++q)
+            pos += bm_before(sm.cS[q], sm.cH[q], sm.cL[q], sm.crank[q], s, h, l, r) ? 1 : 0;
           if (pos < need) {
-            sm.sel[nsel + pos] = m;
-            sm.srank[nsel + pos] = r;
+            const int o = nsel + pos;
+            sm.sel[o] = sm.cut[k];
+            sm.srank[o] = r;
+            sm.sS[o] = s;
+            sm.sH[o] = h;
+            sm.sL[o] = l;
           }
         }
-        __syncthreads();
+        lds_barrier();
       } else {
         // many exact ties: take the best remaining cut-bin candidate `need`
         // times (child ranks computed once)
-        for (int q = tid; q < kBmMaxM / 64; q += kSelThreads) sm.taken[q] = 0;
-        for (int m = tid; m < M; m += kSelThreads)
-          if (bin_of(sm.cs[m]) == kc) {
-            const int u = m / C;
-            sm.mrank[m] = (int16_t)bm_rank(row(u), tk, C, m - u * C);
-          }
-        __syncthreads();
+        for (int q = tid; q < kBmMaxM / 64; q += kBmThreads) sm.taken[q] = 0;
+        lds_barrier();
         for (int t = 0; t < need; ++t) {
           double bs = -INFINITY;
           uint64_t bh = ~0ull, bl = ~0ull;
           int br = 0x7FFFFFFF, bm = -1;
-          for (int m = tid; m < M; m += kSelThreads) {
+          for (int m = tid; m < M; m += kBmThreads) {
             if (bin_of(sm.cs[m]) != kc || ((sm.taken[m >> 6] >> (m & 63)) & 1)) continue;
             const int u = m / C;
-            const int r = sm.mrank[m];
+            const int r = bm_rank(sm.clp + u * C, tk, C, m - u * C);
             if (bm < 0 || bm_before(sm.cs[m], sm.bh[u], sm.bl[u], r, bs, bh, bl, br)) {
               bs = sm.cs[m];
               bh = sm.bh[u];
@@ -270,10 +319,10 @@ __global__ __launch_bounds__(kSelThreads) void beam_kernel(BeamParams bp) {
             sm.cut[wv] = bm;
             sm.crank[wv] = br;
           }
-          __syncthreads();
+          lds_barrier();
           if (tid == 0) {
             int best = -1;
-            for (int q = 0; q < kSelWaves; ++q) {
+            for (int q = 0; q < kBmWaves; ++q) {
               const int mq = sm.cut[q];
               if (mq < 0) continue;
               if (best < 0) {
@@ -285,23 +334,27 @@ __global__ __launch_bounds__(kSelThreads) void beam_kernel(BeamParams bp) {
                             sm.bl[ub], sm.crank[best]))
                 best = q;
             }
-            const int mb = sm.cut[best];
+            const int mb = sm.cut[best], ub = mb / C;
             sm.sel[nsel + t] = mb;
             sm.srank[nsel + t] = sm.crank[best];
+            sm.sS[nsel + t] = sm.cs[mb];
+            sm.sH[nsel + t] = sm.bh[ub];
+            sm.sL[nsel + t] = sm.bl[ub];
             sm.taken[mb >> 6] |= 1ull << (mb & 63);
           }
-          __syncthreads();
+          lds_barrier();
         }
       }
       nsel = w;
     }
     // ---- the new beam: child ranks of the whole-bin entries, keys, order ----
     const int cutfrom = w >= M ? M : sm.kexc;  // entries before it need their rank
-    for (int k = tid; k < cutfrom; k += kSelThreads) {
+    for (int k = wv; k < cutfrom; k += kBmWaves) {
       const int m = sm.sel[k], u = m / C;
-      sm.srank[k] = bm_rank(row(u), tk, C, m - u * C);
+      const int r = bm_rank_wave(sm.clp + u * C, tk, C, m - u * C);
+      if (lane == 0) sm.srank[k] = r;
     }
-    __syncthreads();
+    lds_barrier();
     // entry k: candidate m, score, key = parent key + digit; its position by
     // counting; written straight into the next beam (staged in registers)
     int nb_c = 0, nb_node = 0, nb_pos = -1;
@@ -309,21 +362,17 @@ __global__ __launch_bounds__(kSelThreads) void beam_kernel(BeamParams bp) {
     uint64_t nb_h = 0, nb_l = 0;
     if (tid < nsel) {
       const int m = sm.sel[tid], u = m / C, j = m - u * C;
-      const double s = sm.cs[m];
-      uint64_t h = sm.bh[u], l = sm.bl[u];
+      const double s = sm.sS[tid];
+      uint64_t h = sm.sH[tid], l = sm.sL[tid];
       const int r = sm.srank[tid];
       int pos = 0;
-      for (int q = 0; q < nsel; ++q) {
-        const int mq = sm.sel[q], uq = mq / C;
-        pos += bm_before(sm.cs[mq], sm.bh[uq], sm.bl[uq], sm.srank[q], s, h, l, r) ? 1 : 0;
-      }
+      for (int q = 0; q < nsel; ++q)
+        pos += bm_before(sm.sS[q], sm.sH[q], sm.sL[q], sm.srank[q], s, h, l, r) ? 1 : 0;
       lex_set_digit(h, l, d + 1, (uint32_t)r, bpd);
       const int node = sm.nout + pos + 1;
-      const size_t o = (size_t)b * B + node - 1;
-      p.tree_tokens[o] = tk[j];
-      p.parents[o] = sm.bnode[u];
-      p.logq[o] = (float)s;
-      if (p.depths) p.depths[o] = d + 1;
+      sm.otok[node - 1] = tk[j];
+      sm.oq[node - 1] = (float)s;
+      sm.odep[node - 1] = (uint8_t)(d + 1);
       sm.opar[node - 1] = sm.bnode[u];
       nb_c = j;
       nb_S = s;
@@ -332,7 +381,7 @@ __global__ __launch_bounds__(kSelThreads) void beam_kernel(BeamParams bp) {
       nb_node = node;
       nb_pos = pos;
     }
-    __syncthreads();  // every read of the old beam is done
+    lds_barrier();  // every read of the old beam is done
     if (nb_pos >= 0) {
       sm.bc[nb_pos] = nb_c;
       sm.bS[nb_pos] = nb_S;
@@ -344,18 +393,19 @@ __global__ __launch_bounds__(kSelThreads) void beam_kernel(BeamParams bp) {
       sm.nprev = nsel;
       sm.nout += nsel;
     }
-    __syncthreads();
+    lds_barrier();
   }
   const int nout = sm.nout;
-  for (int j = nout + tid; j < B; j += kSelThreads) {
+  for (int j = tid; j < B; j += kBmThreads) {
     const size_t o = (size_t)b * B + j;
-    p.tree_tokens[o] = -1;
-    p.parents[o] = -1;
-    p.logq[o] = -INFINITY;
-    if (p.depths) p.depths[o] = 0;
+    const bool in = j < nout;
+    p.tree_tokens[o] = in ? sm.otok[j] : -1;
+    p.parents[o] = in ? sm.opar[j] : -1;
+    p.logq[o] = in ? sm.oq[j] : -INFINITY;
+    if (p.depths) p.depths[o] = in ? (int)sm.odep[j] : 0;
   }
   if (tid == 0) p.num_nodes[b] = nout;
-  sel_mask_rows(p, sm.opar, nout, b);
+  sel_mask_rows<kBmThreads>(p, sm.opar, nout, b);
 }
 
 }  // namespace ddt

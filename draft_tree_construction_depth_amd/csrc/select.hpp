@@ -435,13 +435,14 @@ __device__ __forceinline__ void sel_order_emit(const SelectParams& p, SelectSmem
 
 // Phase 4: the bit-packed ancestor mask from the emitted parents (opar[j] =
 // parent node number of node j+1, in LDS; nodes past nsel get zero rows).
+template <int NT = kSelThreads>
 __device__ __forceinline__ void sel_mask_rows(const SelectParams& p, const int* opar, int nsel,
                                               int64_t b) {
   const int tid = threadIdx.x;
   const int B = p.B;
   if (p.mask) {
     const int W = p.W;
-    for (int i = tid; i <= B; i += kSelThreads) {
+    for (int i = tid; i <= B; i += NT) {
       uint64_t m[kMaxW];
 #pragma unroll
       for (int q = 0; q < kMaxW; ++q) m[q] = 0;
