@@ -435,33 +435,27 @@ __device__ __forceinline__ void sel_order_emit(const SelectParams& p, SelectSmem
 
 // Phase 4: the bit-packed ancestor mask from the emitted parents (opar[j] =
 // parent node number of node j+1, in LDS; nodes past nsel get zero rows).
+// One thread per (row, 64-bit word): it walks the row's ancestor chain and
+// keeps the bits that fall in its word, so consecutive threads write
+// consecutive words.
 template <int NT = kSelThreads>
 __device__ __forceinline__ void sel_mask_rows(const SelectParams& p, const int* opar, int nsel,
                                               int64_t b) {
-  const int tid = threadIdx.x;
-  const int B = p.B;
-  if (p.mask) {
-    const int W = p.W;
-    for (int i = tid; i <= B; i += NT) {
-      uint64_t m[kMaxW];
-#pragma unroll
-      for (int q = 0; q < kMaxW; ++q) m[q] = 0;
-      if (i <= nsel) {
-        int u = i;
-        for (int step = 0; step <= kMaxL + 1; ++step) {
-          const int wq = u >> 6;
-          const uint64_t bit = 1ull << (u & 63);
-#pragma unroll
-          for (int q = 0; q < kMaxW; ++q) m[q] |= (q == wq) ? bit : 0ull;
-          if (u == 0) break;
-          u = opar[u - 1];
-        }
+  if (!p.mask) return;
+  const int B = p.B, W = p.W;
+  uint64_t* dst = p.mask + (size_t)b * (B + 1) * W;
+  for (int t = threadIdx.x; t < (B + 1) * W; t += NT) {
+    const int i = t / W, q = t - i * W;
+    uint64_t m = 0;
+    if (i <= nsel) {
+      int u = i;
+      for (int step = 0; step <= kMaxL + 1; ++step) {
+        m |= (u >> 6) == q ? 1ull << (u & 63) : 0ull;
+        if (u == 0) break;
+        u = opar[u - 1];
       }
-      uint64_t* dst = p.mask + ((size_t)b * (B + 1) + i) * W;
-#pragma unroll
-      for (int q = 0; q < kMaxW; ++q)
-        if (q < W) dst[q] = m[q];
     }
+    dst[t] = m;
   }
 }
 

@@ -29,33 +29,34 @@ struct MaskParams {
 };
 
 __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskParams p) {
-  constexpr int MW = (512 + 1 + 63) / 64;
+  __shared__ int spar[512];
   const int64_t b = blockIdx.x;
   const int B = p.B, W = p.W;
   int n = p.num_nodes[b];
   n = n < 0 ? 0 : (n > B ? B : n);
   const int32_t* par = p.parents + (size_t)b * B;
-  for (int i = threadIdx.x; i <= B; i += kMaskThreads) {
-    uint64_t m[MW];
-#pragma unroll
-    for (int q = 0; q < MW; ++q) m[q] = 0;
+  // parents in LDS, a malformed one (not an earlier node) ends its chain
+  for (int j = threadIdx.x; j < n; j += kMaskThreads) {
+    const int pu = par[j];
+    spar[j] = pu < 0 || pu > j ? -1 : pu;
+  }
+  __syncthreads();
+  // one thread per (row, 64-bit word): the row's ancestor chain, this word's bits
+  uint64_t* dst = p.mask + (size_t)b * (B + 1) * W;
+  for (int t = threadIdx.x; t < (B + 1) * W; t += kMaskThreads) {
+    const int i = t / W, q = t - i * W;
+    uint64_t m = 0;
     if (i <= n) {
       int u = i;
       for (int step = 0; step <= B; ++step) {
-        const int wq = u >> 6;
-        const uint64_t bit = 1ull << (u & 63);
-#pragma unroll
-        for (int q = 0; q < MW; ++q) m[q] |= (q == wq) ? bit : 0ull;
+        m |= (u >> 6) == q ? 1ull << (u & 63) : 0ull;
         if (u == 0) break;
-        const int pu = par[u - 1];
-        if (pu < 0 || pu >= u) break;  // malformed parent: stop the walk
+        const int pu = spar[u - 1];
+        if (pu < 0) break;
         u = pu;
       }
     }
-    uint64_t* dst = p.mask + ((size_t)b * (B + 1) + i) * W;
-#pragma unroll
-    for (int q = 0; q < MW; ++q)
-      if (q < W) dst[q] = m[q];
+    dst[t] = m;
   }
 }
 
