@@ -177,6 +177,23 @@ __global__ __launch_bounds__(kSpThreads) void sp_table_kernel(SpTableParams p) {
     p.best[rowbase + i] = (uint8_t)bj;
     p.blp[rowbase + i] = bv;
   }
+  float* dst = p.lp + rowbase * C;  // C rows of C floats, contiguous
+  if (C == kSpC) {
+    // full tiles: each lane's four consecutive children go out as one
+    // 16-byte store (the two lanes of a parent cover 32 contiguous bytes)
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        float4 v4;
+        v4.x = acc[m][4 * rq + 0];
+        v4.y = acc[m][4 * rq + 1];
+        v4.z = acc[m][4 * rq + 2];
+        v4.w = acc[m][4 * rq + 3];
+        *(float4*)(dst + (size_t)i * C + m * 32 + 8 * rq + 4 * h) = v4;
+      }
+    return;
+  }
   __syncthreads();  // every wave has read its A operands: the rows become the tile
 #pragma unroll
   for (int m = 0; m < 4; ++m)
@@ -190,7 +207,6 @@ __global__ __launch_bounds__(kSpThreads) void sp_table_kernel(SpTableParams p) {
       *(float4*)&sm.u.tile[i][m * 32 + 8 * rq + 4 * h] = v4;
     }
   __syncthreads();
-  float* dst = p.lp + rowbase * C;  // C rows of C floats, contiguous
   if ((C & 3) == 0) {
     const int cq = C >> 2;  // 16-byte chunks per row
     for (int q = tid; q < C * cq; q += kSpThreads) {
