@@ -257,16 +257,6 @@ struct SpRows {
   __device__ float best_lp(int d, int c) const {
     return d == 0 ? tb->lp0[tb->best0] : tb->blp[(d - 1) * C + c];
   }
-  // position of child j in row (d, c): entries before it by (lp desc, token asc)
-  __device__ int rank(int d, int c, int j) const {
-    const float* r = row(d, c);
-    const int32_t* t = tok + (size_t)d * C;
-    const float v = r[j];
-    const int tj = t[j];
-    int n = 0;
-    for (int q = 0; q < C; ++q) n += (r[q] > v || (r[q] == v && t[q] < tj)) ? 1 : 0;
-    return n;
-  }
 };
 
 // Serial best-first heap (the post's loop) for requests whose enumeration

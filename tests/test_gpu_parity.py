@@ -273,6 +273,22 @@ def test_mask_kernel_on_oracle_trees(cfg, seed):
                                   O.mask(o["parents"], o["num_nodes"], B))
 
 
+@pytest.mark.parametrize("B", [1, 63, 200, 512])
+def test_mask_kernel_random_trees(B):
+    """Random prefix-ordered trees (parent of node j+1 drawn from 0..j), deep
+    and wide, every row width up to nine words; node counts below B too."""
+    rng = np.random.default_rng(B)
+    batch = 6
+    par = np.full((batch, B), -1, np.int32)
+    nn = np.array([B, B, B // 2, 1, 0, max(B - 1, 0)], np.int32)
+    for b in range(batch):
+        for j in range(nn[b]):
+            par[b, j] = j if b == 1 else int(rng.integers(0, j + 1))  # b = 1: one chain
+    m = pkg.ddtree_mask(torch.from_numpy(par).to(DEV), torch.from_numpy(nn).to(DEV), B)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(m.cpu().numpy().view(np.uint64), O.mask(par, nn, B))
+
+
 def _walk_both(o, tgt, L):
     dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
     r = pkg.ddtree_accept(dv(o["tree_tokens"]), dv(o["parents"]), dv(o["num_nodes"]), dv(tgt), L)
