@@ -271,6 +271,69 @@ def dspark_bench(args) -> int:
     return 0
 
 
+def latency_bench(args) -> int:
+    """Single-request latency (batch 1, L = 15, V = 151936 bf16 with planted
+    peaks, B = 64): one round = ddtree_build (stage 1, selection, fused mask)
+    + ddtree_accept. Device time per round from events around many
+    back-to-back rounds; host-visible latency (enqueue to synchronize) per
+    round, median and spread."""
+    import numpy as np
+    import torch
+
+    import draft_tree_construction_depth_amd as pkg
+    from draft_tree_construction_depth_amd import gen
+
+    c = gen.CONFIGS[2]
+    L, V, B = c["L"], c["V"], c["B"]
+    dev = torch.device("cuda:0")
+    x = gen.make_logits(2, 0)
+    Y = gen.drafter_draws(2, 0, x, c["dtype"])
+    xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    tree = pkg.ddtree_build(xd, B)
+    torch.cuda.synchronize()
+    tgt = torch.from_numpy(gen.node_targets_from_depths(
+        Y, tree["depths"].cpu().numpy(), tree["num_nodes"].cpu().numpy(), B)).to(dev)
+    acc = pkg.ddtree_accept(tree["tree_tokens"], tree["parents"], tree["num_nodes"], tgt, L)
+
+    def rnd():
+        pkg.ddtree_build(xd, B, out=tree)
+        pkg.ddtree_accept(tree["tree_tokens"], tree["parents"], tree["num_nodes"], tgt, L, out=acc)
+
+    n = max(args.steps, 1000)
+    for _ in range(max(args.warmup, 20)):
+        rnd()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        rnd()
+    b.record()
+    torch.cuda.synchronize()
+    dev_us = a.elapsed_time(b) * 1e3 / n
+    host = []
+    for _ in range(n):
+        t0 = time.perf_counter()
+        rnd()
+        torch.cuda.synchronize()
+        host.append((time.perf_counter() - t0) * 1e6)
+    host = np.array(host)
+    res = {
+        "metric": "build+mask+accept latency at batch 1, V=151936, L=15, B=64",
+        "value": round(float(np.median(host)), 2), "unit": "us", "n_gpus": 1, "steps": n,
+        "warmup": max(args.warmup, 20), "ms_per_step": round(float(np.median(host)) / 1e3, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32/f64",
+        "data": "synthetic",
+        "config": {"workload": "batch1_L15_V151936_B64_bf16_logits", "batch": 1, "L": L, "V": V,
+                   "B": B},
+        "host_latency_us": {"p10": round(float(np.percentile(host, 10)), 2),
+                            "p50": round(float(np.median(host)), 2),
+                            "p90": round(float(np.percentile(host, 90)), 2)},
+        "device_us_per_round": round(dev_us, 2),
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 # Verifier cache of the KV-compaction workload: Qwen3-8B's attention shape
 # (36 layers, 8 KV heads, head dim 128, bf16), 1024 tokens of context.
 KV_LAYERS, KV_HEADS, KV_DH, KV_PAST = 36, 8, 128, 1024
@@ -357,6 +420,9 @@ def main() -> int:
                     help="time sparkling_beam on the SparklingTree workload instead (own JSON line)")
     ap.add_argument("--kv-compact", action="store_true",
                     help="time ddtree_compact_kv after a batch-64 round instead (own JSON line)")
+    ap.add_argument("--workload", choices=("c3", "c2", "c5"), default="c3",
+                    help="c3: batch 64, B 128 (default, the headline); c2: batch 1, B 64 latency "
+                         "of build + mask + accept; c5: batch 256, B 256 (own JSON lines)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 3 device-to-device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -394,15 +460,18 @@ def main() -> int:
         return dspark_bench(args)
     if args.beam:
         return beam_bench(args)
+    if args.workload == "c2":
+        return latency_bench(args)
+    cfg = 5 if args.workload == "c5" else 3
 
-    c = gen.CONFIGS[3]
+    c = gen.CONFIGS[cfg]
     batch, L, V, B = c["batch"], c["L"], c["V"], c["B"]
     K = min(B, V)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    x = gen.make_logits(3, 0)
-    Y = gen.drafter_draws(3, 0, x, c["dtype"])
+    x = gen.make_logits(cfg, 0)
+    Y = gen.drafter_draws(cfg, 0, x, c["dtype"])
     x_dev = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
     bufs = [x_dev] + [x_dev.clone() for _ in range(args.buffers - 1)]
 
@@ -464,10 +533,11 @@ def main() -> int:
     step_bytes = logits_bytes + batch * (B * 12 + B * 4 + 4 + (B + 1) * W * 8
                                          + (B + 1) * 4 + (L + 2) * 4)
     achieved = logits_bytes / (s1_avg_ms / 1e3) / 1e9
-    traffic = measured_traffic()
+    traffic = measured_traffic() if cfg == 3 else None
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC if cfg == 3 else
+        "draft trees/sec at batch 256, V=151936, L=15, B=256; achieved HBM GB/s vs peak",
         "value": round(trees_per_s, 1),
         "unit": "trees/s",
         "n_gpus": 1,
@@ -479,8 +549,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32/f64",
         "data": "synthetic",
-        "config": {"workload": "batch64_L15_V151936_B128_bf16_logits", "batch": batch, "L": L,
-                   "V": V, "B": B, "input_buffers": len(bufs)},
+        "config": {"workload": f"batch{batch}_L{L}_V{V}_B{B}_bf16_logits", "batch": batch,
+                   "L": L, "V": V, "B": B, "input_buffers": len(bufs)},
         "whole_step_gbps": round(step_bytes * args.steps / (total_ms / 1e3) / 1e9, 1),
         "wall_s": round(wall, 4),
         "roofline": {"bound": "hbm", "kernel": "stage1 (ddtree_row_topk)",
@@ -490,7 +560,7 @@ def main() -> int:
                      "launches_sampled": len(s1_ms),
                      "traffic": traffic},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and cfg == 3:
         cb, _ = cpu_baseline(x, Y, B, L)
         result["cpu_baseline"] = {k: (round(v, 2) if isinstance(v, float) else v)
                                   for k, v in cb.items()}

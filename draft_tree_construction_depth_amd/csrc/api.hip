@@ -151,7 +151,7 @@ hipError_t launch_stage1_dt(const S1Plan& pl, bool aligned, int64_t rows,
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 mgrid((unsigned)((rows + ddt::kMergeWaves - 1) / ddt::kMergeWaves));
+  const dim3 mgrid((unsigned)rows);
   hipLaunchKernelGGL((ddt::stage1_merge_kernel<DT>), mgrid, dim3(ddt::kWave * ddt::kMergeWaves),
                      0, st, prm);
   return hipGetLastError();

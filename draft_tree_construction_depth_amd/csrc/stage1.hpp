@@ -23,10 +23,11 @@
 // Two shapes:
 //  stage1_chunk_kernel + stage1_merge_kernel (few rows): one workgroup per
 //    chunk writes a record (survivors, threshold, normaliser partial); one
-//    wavefront per row then keeps the survivors at or above the largest
+//    workgroup per row then keeps the survivors at or above the largest
 //    chunk threshold, finds the exact K-th (value, id) key by a ballot
-//    bisection over registers, ranks the K winners by counting and writes
-//    the row's table and log-sum-exp (float64).
+//    bisection over registers (four waves' counts summed in LDS), ranks the
+//    K winners by counting and writes the row's table and log-sum-exp
+//    (float64).
 //  stage1_row_kernel (many rows): one workgroup walks all chunks of its row
 //    with double-buffered register loads (chunk i+1 in flight while chunk i
 //    is processed), raises the row threshold on a schedule of chunks, keeps
@@ -179,67 +180,6 @@ __device__ __forceinline__ float exp_collect(v4u32 (&raw)[NV], float mc, float t
     if (j == NV - 1) total = a;
   }
   return total;
-}
-
-// ---------------------------------------------------------------------------
-// Exact top-K by one wavefront from up to 64 * kMergeSlots keys held in
-// registers (0 = empty slot): ballot bisection for the K-th largest key, then
-// each winner's rank by counting. Writes the table row. `stage` is a
-// wave-private LDS area of >= K keys. Requires >= K nonzero keys.
-template <int NS>
-__device__ __forceinline__ void wave_topk_finish(uint64_t (&v)[NS], int R, int K,
-                                                 int idbits, bool bf16, uint64_t* stage,
-                                                 int32_t* out_ids, float* out_vals) {
-  const int lane = threadIdx.x & 63;
-  auto count_ge = [&](uint64_t x) -> int {
-    int c = 0;
-#pragma unroll
-    for (int r = 0; r < NS; ++r)
-      if (r < R) c += __popcll(__ballot(v[r] >= x));
-    return c;
-  };
-  uint64_t T = 0;
-  for (int bit = 63; bit >= 32; --bit) {
-    if (bf16 && bit < 48) {
-      // bf16 value keys have a constant low half: 0x0000 (>= 0) or 0xFFFF
-      T |= (T >> 63) ? 0ull : 0x0000FFFF00000000ull;
-      break;
-    }
-    const uint64_t x = T | (1ull << bit);
-    if (count_ge(x) >= K) T = x;
-  }
-  // ids are < 2^idbits: the inverted id's higher bits are all ones
-  T |= 0xFFFFFFFFull & ~((1ull << idbits) - 1ull);
-  for (int bit = idbits - 1; bit >= 0; --bit) {
-    const uint64_t x = T | (1ull << bit);
-    if (count_ge(x) >= K) T = x;
-  }
-  // the K winners (keys are unique) into the wave's staging area
-  int nw = 0;
-#pragma unroll
-  for (int r = 0; r < NS; ++r) {
-    if (r < R) {
-      const bool win = v[r] >= T && v[r] != 0;
-      const uint64_t M = __ballot(win);
-      if (win) stage[nw + lanes_below(M)] = v[r];
-      nw += __popcll(M);
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  // rank of winner i = number of larger winners
-  for (int i0 = 0; i0 < K; i0 += kWave) {
-    const int i = i0 + lane;
-    const uint64_t mine = i < K ? stage[i] : 0ull;
-    int rank = 0;
-#pragma unroll 8
-    for (int j = 0; j < K; ++j) rank += stage[j] > mine ? 1 : 0;
-    if (i < K) {
-      out_ids[rank] = (int32_t)cand_id(mine);
-      out_vals[rank] = key_value(cand_vkey(mine));
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -445,19 +385,29 @@ __global__ __launch_bounds__(kS1Threads) void stage1_chunk_kernel(Stage1Params p
 }
 
 // ---------------------------------------------------------------------------
-// Row merge: one wavefront per row.
-constexpr int kMergeWaves = 4;
+// Row merge: one workgroup per row.
+constexpr int kMergeWaves = 4;  // one workgroup of four waves per row
+constexpr int kMergeWSlots = (kMergeSlots + kMergeWaves - 1) / kMergeWaves;
 
 struct MergeSmem {
-  uint64_t stage[kMergeWaves][512];
+  uint64_t win[512];            // the row's K winners (K <= 512)
+  int cnt[2][kMergeWaves];      // per-wave counts of a bisection step, double buffered
+  int nw[kMergeWaves];
+  uint64_t hi[kMergeWaves];
 };
 
+// One workgroup per row; wave w holds record slots w, w+4, ... (slot r = 64
+// keys). Each chunk holds >= K elements at or above its threshold, so the
+// row's K-th key is at or above the largest threshold; every record holds all
+// of its chunk's elements at or above the chunk threshold (or its exact top
+// K). The K-th largest key comes from a bisection over the key bits whose
+// counts are one ballot per slot, summed over the four waves; the K winners
+// are then ranked by counting.
 template <int DT>
 __global__ __launch_bounds__(kWave* kMergeWaves) void stage1_merge_kernel(Stage1Params p) {
   __shared__ MergeSmem sm;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kMergeWaves + w;
-  if (row >= p.rows) return;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int64_t row = blockIdx.x;
   const int S = p.S, K = p.K, capp = p.capp;
 
   int ni = 0;
@@ -470,32 +420,106 @@ __global__ __launch_bounds__(kWave* kMergeWaves) void stage1_merge_kernel(Stage1
     oi = p.meta[2 * rec];
     si = p.meta[2 * rec + 1];
   }
-  // normaliser: z = ln2 * (OFF + log2(sum_s sum_s * 2^(off_s - OFF))), float64
-  const double OFF = wave_max(oi);
-  const double s = wave_sum(oi == -INFINITY ? 0.0 : si * exp2(oi - OFF));
-  if (lane == 0) p.out_lse[row] = kLn2 * (OFF + log2(s));
-
-  // Each chunk holds >= K elements at or above its threshold, so the row's
-  // K-th key is at or above the largest threshold; every record holds all of
-  // its chunk's elements at or above the chunk threshold (or its exact top K).
+  if (w == 0) {
+    // normaliser: z = ln2 * (OFF + log2(sum_s sum_s * 2^(off_s - OFF))), float64
+    const double OFF = wave_max(oi);
+    const double s = wave_sum(oi == -INFINITY ? 0.0 : si * exp2(oi - OFF));
+    if (lane == 0) p.out_lse[row] = kLn2 * (OFF + log2(s));
+  }
   const uint64_t lo = (uint64_t)wave_max(ti) << 32;
   const int span = S * capp;
   const int R = (span + kWave - 1) / kWave;  // <= kMergeSlots (checked on the host)
   const uint64_t* src = p.cands + (size_t)row * span;
-  uint64_t v[kMergeSlots];
+  // every slot's load in flight at once (clamped in-bounds reads, masked
+  // afterwards: a load under a per-lane condition would wait for the one
+  // before it)
+  uint64_t v[kMergeWSlots];
 #pragma unroll
-  for (int r = 0; r < kMergeSlots; ++r) {
-    v[r] = 0;
-    if (r < R) {
-      const int i = r * kWave + lane;
-      const int ch = i / capp;
-      const int n_ch = __shfl(ni, ch < S ? ch : 0);
-      const uint64_t k = (i < span && i - ch * capp < n_ch) ? src[i] : 0ull;
-      v[r] = k >= lo ? k : 0ull;
+  for (int q = 0; q < kMergeWSlots; ++q) {
+    const int r = w + kMergeWaves * q;
+    const int i = r * kWave + lane;
+    v[q] = r < R ? src[i < span ? i : span - 1] : 0ull;
+  }
+#pragma unroll
+  for (int q = 0; q < kMergeWSlots; ++q) {
+    const int r = w + kMergeWaves * q;
+    const int i = r * kWave + lane;
+    const int ch = i / capp;
+    const int n_ch = __shfl(ni, ch < S ? ch : 0);
+    v[q] = (r < R && i < span && i - ch * capp < n_ch && v[q] >= lo) ? v[q] : 0ull;
+  }
+  int par = 0;
+  auto count_ge = [&](uint64_t x) -> int {
+    int c = 0;
+#pragma unroll
+    for (int q = 0; q < kMergeWSlots; ++q)
+      if (w + kMergeWaves * q < R) c += __popcll(__ballot(v[q] >= x));
+    if (lane == 0) sm.cnt[par][w] = c;
+    __syncthreads();
+    int t = 0;
+#pragma unroll
+    for (int i = 0; i < kMergeWaves; ++i) t += sm.cnt[par][i];
+    par ^= 1;
+    return t;
+  };
+  // every candidate lies in [lo, hi]: the bits above the highest one where
+  // lo and hi differ are common to all of them, so the bisection starts there
+  uint64_t hi = 0;
+#pragma unroll
+  for (int q = 0; q < kMergeWSlots; ++q) hi = v[q] > hi ? v[q] : hi;
+  hi = wave_max(hi);
+  if (lane == 0) sm.hi[w] = hi;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kMergeWaves; ++i) hi = sm.hi[i] > hi ? sm.hi[i] : hi;
+  const int top = (lo ^ hi) == 0 ? 31 : 63 - __clzll(lo ^ hi);
+  uint64_t T = top >= 63 ? 0ull : lo & ~((2ull << top) - 1ull);
+  for (int bit = top < 63 ? top : 63; bit >= 32; --bit) {
+    if (DT == 0 && bit < 48) break;
+    const uint64_t x = T | (1ull << bit);
+    if (count_ge(x) >= K) T = x;
+  }
+  // bf16 value keys have a constant low half: 0x0000 (>= 0) or 0xFFFF
+  if (DT == 0) T = (T & 0xFFFF000000000000ull) | ((T >> 63) ? 0ull : 0x0000FFFF00000000ull);
+  // ids are < 2^idbits: the inverted id's higher bits are all ones. If
+  // exactly K keys reach the K-th value, no id bisection is needed.
+  T |= 0xFFFFFFFFull & ~((1ull << p.idbits) - 1ull);
+  if (count_ge(T) > K) {
+    for (int bit = p.idbits - 1; bit >= 0; --bit) {
+      const uint64_t x = T | (1ull << bit);
+      if (count_ge(x) >= K) T = x;
     }
   }
-  wave_topk_finish(v, R, K, p.idbits, DT == 0, sm.stage[w], p.out_ids + row * K,
-                   p.out_vals + row * K);
+  // the K winners (keys are unique) into LDS, waves in order
+  int nw = 0;
+#pragma unroll
+  for (int q = 0; q < kMergeWSlots; ++q)
+    if (w + kMergeWaves * q < R) nw += __popcll(__ballot(v[q] >= T && v[q] != 0));
+  if (lane == 0) sm.nw[w] = nw;
+  __syncthreads();
+  int pos = 0;
+  for (int i = 0; i < w; ++i) pos += sm.nw[i];
+#pragma unroll
+  for (int q = 0; q < kMergeWSlots; ++q) {
+    if (w + kMergeWaves * q < R) {
+      const bool win = v[q] >= T && v[q] != 0;
+      const uint64_t M = __ballot(win);
+      if (win) sm.win[pos + lanes_below(M)] = v[q];
+      pos += __popcll(M);
+    }
+  }
+  __syncthreads();
+  // rank of winner i = number of larger winners
+  int32_t* oid = p.out_ids + row * K;
+  float* oval = p.out_vals + row * K;
+  for (int i = tid; i < K; i += kWave * kMergeWaves) {
+    const uint64_t mine = sm.win[i];
+    int rank = 0;
+#pragma unroll 8
+    for (int j = 0; j < K; ++j) rank += sm.win[j] > mine ? 1 : 0;
+    oid[rank] = (int32_t)cand_id(mine);
+    oval[rank] = key_value(cand_vkey(mine));
+  }
 }
 
 // ---------------------------------------------------------------------------
