@@ -77,6 +77,22 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
+// Sum of the first w of NW per-wave totals in LDS (16-byte aligned, NW a
+// multiple of 4), read four at a time; total gets the sum of all NW.
+template <int NW>
+__device__ __forceinline__ int waves_before(const int* wsum, int w, int& total) {
+  static_assert(NW % 4 == 0, "int4 reads of the wave totals");
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; i += 4) {
+    const int4 t = *(const int4*)&wsum[i];
+    pre += (i < w ? t.x : 0) + (i + 1 < w ? t.y : 0) + (i + 2 < w ? t.z : 0) + (i + 3 < w ? t.w : 0);
+    tot += t.x + t.y + t.z + t.w;
+  }
+  total = tot;
+  return pre;
+}
+
 // Exclusive scan of one int per thread over the block (every thread calls
 // it); total gets the block sum. wsum: NT/64 ints of LDS, 16-byte aligned.
 // One barrier; a later call reusing wsum needs a barrier in between.
@@ -88,15 +104,7 @@ __device__ __forceinline__ int block_excl_scan_reg(int x, int* wsum, int& total)
   const int inc = wave_incl_scan(x);
   if (lane == kWave - 1) wsum[w] = inc;
   __syncthreads();
-  int pre = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < NW; i += 4) {
-    const int4 t = *(const int4*)&wsum[i];
-    pre += (i < w ? t.x : 0) + (i + 1 < w ? t.y : 0) + (i + 2 < w ? t.z : 0) + (i + 3 < w ? t.w : 0);
-    tot += t.x + t.y + t.z + t.w;
-  }
-  total = tot;
-  return pre + inc - x;
+  return waves_before<NW>(wsum, w, total) + inc - x;
 }
 
 // In-place exclusive scan of a[0..n) (LDS) by NT threads; returns the total.

@@ -47,6 +47,7 @@ namespace ddt {
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kECap = 2048;
+constexpr int kSelRetries = 3;  // threshold raises after an enumeration overflow
 constexpr int kMaxLK = 8192;
 constexpr int kMaxL = 32;
 constexpr int kMaxB = 512;
@@ -83,8 +84,8 @@ struct SelEnum {
   int16_t ePar[kECap];
   uint16_t eRank[kECap];
   uint8_t eDep[kECap];
-  int cnt[kECap + 1];  // enumeration: child counts; then: output rank of each entry
-  uint16_t ord[kECap];  // entries at or above the second threshold
+  int cnt[kECap + 1];  // output rank of each entry
+  uint32_t own[kECap];  // enumeration: a generation's new anchor -> (parent << 16) | rank
 };
 
 struct SelHeap {
@@ -241,9 +242,12 @@ __device__ void heap_fallback(const SelectParams& p, SelectSmem& sm, int64_t b) 
 // valid lower bound.
 // onedev(i) gives the i-th of the LK scores; lane_bound(lane) a per-lane
 // value whose minimum over wave 0 is a lower bound with >= B scores at or
-// above it.
+// above it. mem (memcap doubles of LDS, not read by onedev) holds the cut
+// bin's members.
 template <class OD, class LB>
-__device__ double sel_tau_hist(SelectSmem& sm, int LK, int B, OD onedev, LB lane_bound) {
+__device__ double sel_tau_hist(SelectSmem& sm, int LK, int B, OD onedev, LB lane_bound,
+                               double* mem = nullptr, int memcap = kMergeCap) {
+  if (mem == nullptr) mem = sm.u.mt.a;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   sm.hist[tid] = 0;
   if (w == 0) {
@@ -275,26 +279,24 @@ __device__ double sel_tau_hist(SelectSmem& sm, int LK, int B, OD onedev, LB lane
   const int x = wave_incl_scan(h);
   if (lane == kWave - 1) sm.wsum[w] = x;
   __syncthreads();
-  int pre = 0;
-  for (int i = 0; i < w; ++i) pre += sm.wsum[i];
-  const int inc = pre + x, exc = inc - h;
+  int tot;
+  const int inc = waves_before<kSelWaves>(sm.wsum, w, tot) + x, exc = inc - h;
   if (inc >= B && exc < B) {
     sm.kcut = tid;
     sm.kexc = exc;
   }
   __syncthreads();
   const int kb = sm.kcut, t = B - 1 - sm.kexc;  // the B-th is member t of bin kb
-  double* mem = sm.u.mt.a;
   for (int i = tid; i < LK; i += kSelThreads) {
     const double sc = onedev(i);
     if (sc >= mn && bin_of(sc) == kb) {
       const int k = atomicAdd(&sm.n2, 1);
-      if (k < kMergeCap) mem[k] = sc;
+      if (k < memcap) mem[k] = sc;
     }
   }
   __syncthreads();
   const int m = sm.n2;
-  if (m > kMergeCap) return mn;
+  if (m > memcap) return mn;
   for (int k = tid; k < m; k += kSelThreads) {
     const double v = mem[k];
     int gt = 0, ge = 0;
@@ -329,6 +331,14 @@ __device__ __forceinline__ void sel_order_emit(const SelectParams& p, SelectSmem
   // before it (score, then the 128-bit lexicographic rank key).
   const int nE = sm.nE;
   static_assert(kECap <= 2 * kSelThreads, "two entries per thread at most");
+  // token ids of this thread's entries, loaded now so that the ordering's
+  // barriers cover the global-load latency
+  int etok[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = tid + k * kSelThreads;
+    etok[k] = i < nE ? p.ids[(size_t)b * LK + (size_t)(en.eDep[i] - 1) * K + en.eRank[i]] : -1;
+  }
   const double top = sm.sig[1];  // the best prefix: depth 1, rank 0
   const double span = top - tau;
   const double scale = span > 0.0 ? (double)kSelThreads / span : 0.0;
@@ -352,19 +362,17 @@ __device__ __forceinline__ void sel_order_emit(const SelectParams& p, SelectSmem
     const int lane = tid & 63, w = tid >> 6;
     if (lane == kWave - 1) sm.wsum[w] = x;
     __syncthreads();
-    int pre = 0;
-    for (int q = 0; q < w; ++q) pre += sm.wsum[q];
-    const int inc = pre + x, exc = inc - h;
+    int tot;
+    const int inc = waves_before<kSelWaves>(sm.wsum, w, tot) + x, exc = inc - h;
     // the first bin reaching B is the cut (the last bin when nE <= B)
     if (nE > B ? (inc >= B && exc < B) : tid == kSelThreads - 1) {
       sm.kcut = tid;
-      sm.n2 = inc;
     }
     sm.hexc[tid] = exc;
     sm.hist[tid] = 0;  // now the bins' fill counters (only this thread read it)
   }
   __syncthreads();
-  const int kcut = sm.kcut, n2 = sm.n2;
+  const int kcut = sm.kcut;
   // E2 in bin order, with compact copies of the order keys: scores in eS,
   // rank keys in the (dead) table of row values
   double* s2 = en.eS;
@@ -379,7 +387,6 @@ __device__ __forceinline__ void sel_order_emit(const SelectParams& p, SelectSmem
     if (i < nE && ebin[k] <= kcut) {
       const int q = sm.hexc[ebin[k]] + atomicAdd(&sm.hist[ebin[k]], 1);
       epos[k] = q;
-      en.ord[q] = (uint16_t)i;
       s2[q] = en.eSc[i];
       h2[q] = en.eLh[i];
       l2[q] = en.eLl[i];
@@ -405,18 +412,22 @@ __device__ __forceinline__ void sel_order_emit(const SelectParams& p, SelectSmem
   }
   __syncthreads();
   const int nsel = nE < B ? nE : B;
-  for (int k = tid; k < n2; k += kSelThreads) {
-    const int i = en.ord[k];
-    const int j = en.cnt[i];
-    if (j < nsel) {
-      const size_t o = (size_t)b * B + j;
-      const int d = en.eDep[i], r = en.eRank[i], pe = en.ePar[i];
-      const int par = pe < 0 ? 0 : en.cnt[pe] + 1;
-      p.tree_tokens[o] = p.ids[(size_t)b * LK + (size_t)(d - 1) * K + r];
-      p.parents[o] = par;
-      p.logq[o] = (float)en.eSc[i];
-      if (p.depths) p.depths[o] = d;
-      sm.opar[j] = par;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = tid + k * kSelThreads;
+    if (epos[k] >= 0) {
+      const int j = en.cnt[i];
+      if (j < nsel) {
+        // a parent of an output node is an earlier output node
+        const size_t o = (size_t)b * B + j;
+        const int pe = en.ePar[i];
+        const int par = pe < 0 ? 0 : en.cnt[pe] + 1;
+        p.tree_tokens[o] = etok[k];
+        p.parents[o] = par;
+        p.logq[o] = (float)en.eSc[i];
+        if (p.depths) p.depths[o] = en.eDep[i];
+        sm.opar[j] = par;
+      }
     }
   }
   for (int j = nsel + tid; j < B; j += kSelThreads) {
@@ -509,157 +520,178 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   }
 
   // ---- 2. enumerate E = {score >= tau} by chains ----------------------------
-  int D0 = 0;
-  for (int d = 1; d <= L; ++d) D0 += sm.sig[d] >= tau ? 1 : 0;
-  if (D0 > kECap) D0 = kECap;  // cannot happen (L <= 32)
-  for (int d = tid; d < D0; d += kSelThreads) {
-    en.eS[d] = sm.P0[d + 1];
-    en.eSc[d] = sm.sig[d + 1];
-    en.ePar[d] = (int16_t)(d - 1);
-    en.eRank[d] = 0;
-    en.eDep[d] = (uint8_t)(d + 1);
-    en.eLh[d] = 0;
-    en.eLl[d] = (uint64_t)(d + 1);
-  }
-  if (tid == 0) sm.nE = D0;
-  __syncthreads();
-  int g0 = 0, g1 = D0, root = 1;
-  for (;;) {
-    const int np = root + (g1 - g0);
-    if (np > kECap) {  // parents must fit the count array
-      if (tid == 0) sm.ovf = 1;
+  // If E outgrows its capacity, every entry found so far is a valid prefix
+  // scoring >= tau: the B-th best of them is a valid, usually much tighter,
+  // threshold, and the enumeration restarts from it (kSelRetries times at
+  // most, then the heap).
+  for (int attempt = 0;; ++attempt) {
+    // spine prefixes reaching tau (the spine's scores do not increase): one
+    // ballot over L <= 32 lanes
+    const int D0 = __popcll(__ballot((tid & 63) < L && sm.sig[(tid & 63) + 1] >= tau));
+    for (int d = tid; d < D0; d += kSelThreads) {
+      en.eS[d] = sm.P0[d + 1];
+      en.eSc[d] = sm.sig[d + 1];
+      en.ePar[d] = (int16_t)(d - 1);
+      en.eRank[d] = 0;
+      en.eDep[d] = (uint8_t)(d + 1);
+      en.eLh[d] = 0;
+      en.eLl[d] = (uint64_t)(d + 1);
+    }
+    if (tid == 0) sm.nE = D0;
+    __syncthreads();
+    int g0 = 0, g1 = D0, root = 1;
+    for (;;) {
+      const int np = root + (g1 - g0);
+      if (np > kECap) {  // parents must fit the count array
+        if (tid == 0) sm.ovf = 1;
+        __syncthreads();
+        break;
+      }
+      // deviating children (rank >= 1) of each parent that reach tau, counted
+      // by binary search in the sorted row; parents per thread: 1, or 2 when
+      // np > kSelThreads (consecutive, so the offsets follow parent order)
+      const int ppt = np > kSelThreads ? 2 : 1;
+      int cpar[2] = {0, 0};
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int i = tid * ppt + k;
+        if (k < ppt && i < np) {
+          double S = 0.0;
+          int d = 0;
+          if (!(root && i == 0)) {
+            const int e = g0 + i - root;
+            S = en.eS[e];
+            d = en.eDep[e];
+          }
+          if (d < L) {
+            const float* row = sm.v + d * K;
+            const double Zd = sm.Z[d];
+            int lo = 1, hi = K;  // first failing rank lies in [lo, hi]
+            while (lo < hi) {
+              const int mid = (lo + hi) >> 1;
+              if ((S + (double)row[mid]) - Zd >= tau) lo = mid + 1;
+              else hi = mid;
+            }
+            cpar[k] = lo - 1;
+          }
+        }
+      }
+      int A;
+      const int off = block_excl_scan_reg<kSelThreads>(cpar[0] + cpar[1], sm.wsum, A);
+      if (A == 0) break;
+      if (A > kECap) {  // more new anchors than entries fit
+        if (tid == 0) sm.ovf = 1;
+        __syncthreads();
+        break;
+      }
+      // each parent labels its new anchors' slots with (parent, rank)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int i = tid * ppt + k;
+        if (k < ppt && i < np) {
+          const int o = off + (k ? cpar[0] : 0);
+          for (int c = 0; c < cpar[k]; ++c) en.own[o + c] = ((uint32_t)i << 16) | (uint32_t)(c + 1);
+        }
+      }
       __syncthreads();
-      break;
-    }
-    // deviating children (rank >= 1) of each parent that reach tau, counted
-    // by binary search in the sorted row; parents per thread: 1, or 2 when
-    // np > kSelThreads (consecutive, so the offsets follow parent order)
-    const int ppt = np > kSelThreads ? 2 : 1;
-    int cpar[2] = {0, 0};
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int i = tid * ppt + k;
-      if (k < ppt && i < np) {
-        double S = 0.0;
-        int d = 0;
-        if (!(root && i == 0)) {
-          const int e = g0 + i - root;
-          S = en.eS[e];
-          d = en.eDep[e];
+      for (int a = tid; a < A; a += kSelThreads) {
+        const uint32_t ow = en.own[a];
+        const int u = (int)(ow >> 16);
+        const int r = (int)(ow & 0xFFFFu);
+        double Su = 0.0, scu = 0.0;
+        int du = 0, pe = -1;
+        uint64_t lh = 0, ll = 0;
+        if (!(root && u == 0)) {
+          pe = g0 + u - root;
+          Su = en.eS[pe];
+          scu = en.eSc[pe];
+          du = en.eDep[pe];
+          lh = en.eLh[pe];
+          ll = en.eLl[pe] & ~63ull;
         }
-        if (d < L) {
-          const float* row = sm.v + d * K;
-          const double Zd = sm.Z[d];
-          int lo = 1, hi = K;  // first failing rank lies in [lo, hi]
-          while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if ((S + (double)row[mid]) - Zd >= tau) lo = mid + 1;
-            else hi = mid;
+        const int d = du + 1;
+        const double S = Su + (double)sm.v[(d - 1) * K + r];
+        const double raw = S - sm.Z[d - 1];
+        const double sc = raw > scu ? scu : raw;
+        lex_set_digit(lh, ll, d, (uint32_t)r, bpd);
+        // chain length: the anchor, then rank-0 extensions while they reach
+        // tau (the next depth's spine values are read one step ahead)
+        int ell = 1;
+        {
+          double S2 = S, sc2 = sc;
+          float vn = sm.v[(d < L ? d : L - 1) * K];
+          double zn = sm.Z[d < L ? d : L - 1];
+          for (int dd = d + 1; dd <= L; ++dd) {
+            const double v0 = (double)vn, Zm = zn;
+            const int nx = dd < L ? dd : L - 1;
+            vn = sm.v[nx * K];
+            zn = sm.Z[nx];
+            S2 += v0;
+            const double raw2 = S2 - Zm;
+            sc2 = raw2 > sc2 ? sc2 : raw2;
+            if (sc2 < tau) break;
+            ++ell;
           }
-          cpar[k] = lo - 1;
         }
-      }
-    }
-    int A;
-    const int off = block_excl_scan_reg<kSelThreads>(cpar[0] + cpar[1], sm.wsum, A);
-    if (A == 0) break;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int i = tid * ppt + k;
-      if (k < ppt && i < np) en.cnt[i] = off + (k ? cpar[0] : 0);
-    }
-    __syncthreads();
-    for (int a = tid; a < A; a += kSelThreads) {
-      // parent = largest u with offset[u] <= a
-      int lo = 0, hi = np - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (en.cnt[mid] <= a) lo = mid;
-        else hi = mid - 1;
-      }
-      const int u = lo;
-      const int r = a - en.cnt[u] + 1;
-      double Su = 0.0, scu = 0.0;
-      int du = 0, pe = -1;
-      uint64_t lh = 0, ll = 0;
-      if (!(root && u == 0)) {
-        pe = g0 + u - root;
-        Su = en.eS[pe];
-        scu = en.eSc[pe];
-        du = en.eDep[pe];
-        lh = en.eLh[pe];
-        ll = en.eLl[pe] & ~63ull;
-      }
-      const int d = du + 1;
-      const double S = Su + (double)sm.v[(d - 1) * K + r];
-      const double raw = S - sm.Z[d - 1];
-      const double sc = raw > scu ? scu : raw;
-      lex_set_digit(lh, ll, d, (uint32_t)r, bpd);
-      // chain length: the anchor, then rank-0 extensions while they reach
-      // tau (the spine values are read at addresses common to all threads)
-      // chain length: the anchor, then rank-0 extensions while they reach
-      // tau (the next depth's spine values are read one step ahead)
-      int ell = 1;
-      {
-        double S2 = S, sc2 = sc;
-        float vn = sm.v[(d < L ? d : L - 1) * K];
-        double zn = sm.Z[d < L ? d : L - 1];
-        for (int dd = d + 1; dd <= L; ++dd) {
-          const double v0 = (double)vn, Zm = zn;
-          const int nx = dd < L ? dd : L - 1;
-          vn = sm.v[nx * K];
-          zn = sm.Z[nx];
-          S2 += v0;
-          const double raw2 = S2 - Zm;
-          sc2 = raw2 > sc2 ? sc2 : raw2;
-          if (sc2 < tau) break;
-          ++ell;
+        const int pos = atomicAdd(&sm.nE, ell);
+        if (pos + ell > kECap) {
+          // slots of this chain below the capacity stay unwritten: mark them
+          for (int q = pos; q < kECap; ++q) en.eSc[q] = -INFINITY;
+          sm.ovf = 1;
+          continue;
         }
-      }
-      const int pos = atomicAdd(&sm.nE, ell);
-      if (pos + ell > kECap) {
-        sm.ovf = 1;
-        continue;
-      }
-      en.eS[pos] = S;
-      en.eSc[pos] = sc;
-      en.ePar[pos] = (int16_t)pe;
-      en.eRank[pos] = (uint16_t)r;
-      en.eDep[pos] = (uint8_t)d;
-      en.eLh[pos] = lh;
-      en.eLl[pos] = ll | (uint64_t)d;
-      {
-        double S2 = S, sc2 = sc;
-        float vn = sm.v[(d < L ? d : L - 1) * K];
-        double zn = sm.Z[d < L ? d : L - 1];
-        for (int i = 1; i < ell; ++i) {
-          const int dd = d + i;
-          const double v0 = (double)vn, Zm = zn;
-          const int nx = dd < L ? dd : L - 1;
-          vn = sm.v[nx * K];
-          zn = sm.Z[nx];
-          S2 += v0;
-          const double raw2 = S2 - Zm;
-          sc2 = raw2 > sc2 ? sc2 : raw2;
-          {
-            const int q = pos + i;
-            en.eS[q] = S2;
-            en.eSc[q] = sc2;
-            en.ePar[q] = (int16_t)(q - 1);
-            en.eRank[q] = 0;
-            en.eDep[q] = (uint8_t)dd;
-            en.eLh[q] = lh;
-            en.eLl[q] = ll | (uint64_t)dd;
+        en.eS[pos] = S;
+        en.eSc[pos] = sc;
+        en.ePar[pos] = (int16_t)pe;
+        en.eRank[pos] = (uint16_t)r;
+        en.eDep[pos] = (uint8_t)d;
+        en.eLh[pos] = lh;
+        en.eLl[pos] = ll | (uint64_t)d;
+        {
+          double S2 = S, sc2 = sc;
+          float vn = sm.v[(d < L ? d : L - 1) * K];
+          double zn = sm.Z[d < L ? d : L - 1];
+          for (int i = 1; i < ell; ++i) {
+            const int dd = d + i;
+            const double v0 = (double)vn, Zm = zn;
+            const int nx = dd < L ? dd : L - 1;
+            vn = sm.v[nx * K];
+            zn = sm.Z[nx];
+            S2 += v0;
+            const double raw2 = S2 - Zm;
+            sc2 = raw2 > sc2 ? sc2 : raw2;
+            {
+              const int q = pos + i;
+              en.eS[q] = S2;
+              en.eSc[q] = sc2;
+              en.ePar[q] = (int16_t)(q - 1);
+              en.eRank[q] = 0;
+              en.eDep[q] = (uint8_t)dd;
+              en.eLh[q] = lh;
+              en.eLl[q] = ll | (uint64_t)dd;
+            }
           }
         }
       }
+      __syncthreads();
+      if (sm.ovf) break;
+      g0 = g1;
+      g1 = sm.nE;
+      root = 0;
+      if (g0 == g1) break;
     }
+    if (!sm.ovf) break;
+    // overflow: entries [0, n) are prefixes scoring >= tau, except slots
+    // marked -inf
+    const int n = sm.nE < kECap ? sm.nE : kECap;
+    if (attempt == kSelRetries || n < B) break;
+    const double t1 = sel_tau_hist(
+        sm, n, B, [&](int i) { return en.eSc[i]; }, [&](int) { return tau; },
+        reinterpret_cast<double*>(en.eLh), kECap);
+    if (!(t1 > tau)) break;
+    tau = t1;
+    if (tid == 0) sm.ovf = 0;
     __syncthreads();
-    if (sm.ovf) break;
-    g0 = g1;
-    g1 = sm.nE;
-    root = 0;
-    if (g0 == g1) break;
   }
 
   if (sm.ovf) {

@@ -177,6 +177,22 @@ def test_build_c5_full_batch_sampled():
     _check_counts(compare_batch(g, o, 256, idx=idx), "c5 seed 0 (32 of 256 requests)")
 
 
+def test_build_c5_enumeration_overflow():
+    # Request 15 of the batch-256 workload, seed 1, has 2436 prefixes at or
+    # above its one-deviation threshold, more than the enumeration holds: the
+    # threshold is raised to the B-th best entry found and the enumeration
+    # restarts. Its neighbours take the ordinary path in the same launch.
+    x = _inputs(5, 1, batch=3, first=14)
+    g = _gpu_build(x, BF16, 256)
+    o = O.build(x, BF16, 256, threads=THREADS)
+    _check_counts(compare_batch(g, o, 256), "c5 seed 1 requests 14-16")
+    om = O.mask(o["parents"], o["num_nodes"], 256)
+    for b in range(3):
+        if classify({k: v[b:b + 1] for k, v in g.items()}, {k: v[b:b + 1] for k, v in o.items()},
+                    0, 256) == "exact":
+            np.testing.assert_array_equal(g["mask"][b], om[b])
+
+
 @pytest.mark.parametrize("seed", range(1, 4))
 def test_build_c3_small_batches(seed):
     # A few requests of the batch-64 workload (smaller launch shape).
