@@ -457,148 +457,164 @@ __global__ __launch_bounds__(kSelThreads) void sp_select_kernel(SelectParams p) 
   }
 
   // ---- 2. enumerate E = {score >= tau} by chains ----------------------------
-  int D0 = 0;
-  for (int d = 1; d <= L; ++d) D0 += sm.sig[d] >= tau ? 1 : 0;
-  for (int d = tid; d < D0; d += kSelThreads) {
-    en.eS[d] = sm.P0[d + 1];
-    en.eSc[d] = sm.sig[d + 1];
-    en.ePar[d] = (int16_t)(d - 1);
-    en.eRank[d] = (uint16_t)tb.spine[d];
-    en.eDep[d] = (uint8_t)(d + 1);
-    en.eLh[d] = 0;
-    en.eLl[d] = (uint64_t)(d + 1);
-  }
-  if (tid == 0) sm.nE = D0;
-  __syncthreads();
-  // Generation g: the chains whose anchors deviate g times. One wave per
-  // parent: its row is read once (two floats a lane), a ballot marks the
-  // children that deviate (not the row's best) and reach tau, and each such
-  // lane appends its chain. A child's rank is 1 (the best child) plus the
-  // deviating children ordered before it: every child ordered before a
-  // qualifying one scores at least as high, so qualifies too.
-  int g0 = 0, g1 = D0, root = 1;
-  for (;;) {
-    const int np = root + (g1 - g0);
-    auto parent = [&](int u, double& S, int& d, int& c, int& pe) {
-      S = 0.0;
-      d = 0;
-      c = 0;
-      pe = -1;
-      if (!(root && u == 0)) {
-        pe = g0 + u - root;
-        S = en.eS[pe];
-        d = en.eDep[pe];
-        c = en.eRank[pe];
-      }
-    };
-    auto load = [&](int u, float& v0, float& v1) {
-      v0 = -INFINITY;
-      v1 = -INFINITY;
-      if (u >= np) return;
-      double S;
-      int d, c, pe;
-      parent(u, S, d, c, pe);
-      if (d < L) {
-        const float* r = R.row(d, c);
-        if (lane < C) v0 = r[lane];
-        if (lane + kWave < C) v1 = r[lane + kWave];
-      }
-    };
-    float n0, n1;
-    load(wv, n0, n1);
-    for (int u = wv; u < np; u += kSelWaves) {
-      const float v0 = n0, v1 = n1;
-      load(u + kSelWaves, n0, n1);  // the wave's next parent, in flight meanwhile
-      double S;
-      int d, c, pe;
-      parent(u, S, d, c, pe);
-      if (d >= L) continue;
-      const int bj = R.best(d, c);
-      const int j0 = lane, j1 = lane + kWave;
-      const bool q0 = j0 < C && j0 != bj && S + (double)v0 >= tau;
-      const bool q1 = j1 < C && j1 != bj && S + (double)v1 >= tau;
-      const uint64_t m0 = __ballot(q0), m1 = __ballot(q1);
-      if ((m0 | m1) == 0) continue;
-      const int32_t* tk = tb.tok + d * C;
-      const int t0 = j0 < C ? tk[j0] : 0x7FFFFFFF, t1 = j1 < C ? tk[j1] : 0x7FFFFFFF;
-      int rk0 = 1, rk1 = 1;
-      for (uint64_t m = m0; m; m &= m - 1) {
-        const int src = __builtin_ctzll(m);
-        const float v = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v0), src));
-        const int t = __builtin_amdgcn_readlane(t0, src);
-        rk0 += sp_better(v, t, v0, t0) ? 1 : 0;
-        rk1 += sp_better(v, t, v1, t1) ? 1 : 0;
-      }
-      for (uint64_t m = m1; m; m &= m - 1) {
-        const int src = __builtin_ctzll(m);
-        const float v = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v1), src));
-        const int t = __builtin_amdgcn_readlane(t1, src);
-        rk0 += sp_better(v, t, v0, t0) ? 1 : 0;
-        rk1 += sp_better(v, t, v1, t1) ? 1 : 0;
-      }
-      uint64_t lh = 0, ll = 0;
-      if (pe >= 0) {
-        lh = en.eLh[pe];
-        ll = en.eLl[pe] & ~63ull;
-      }
-      // the anchor (child j of the parent, score S + v, rank rk) and its
-      // best-child extensions while they reach tau
-      auto emit = [&](int j, float v, int rk) {
-        const int dn = d + 1;
-        const double Sa = S + (double)v;
-        uint64_t ah = lh, al = ll;
-        lex_set_digit(ah, al, dn, (uint32_t)rk, bpd);
-        int ell = 1;
-        {
-          double S2 = Sa;
-          int c2 = j;
-          for (int dd = dn + 1; dd <= L; ++dd) {
-            S2 += (double)R.best_lp(dd - 1, c2);
-            if (S2 < tau) break;
-            c2 = R.best(dd - 1, c2);
-            ++ell;
-          }
-        }
-        const int pos = atomicAdd(&sm.nE, ell);
-        if (pos + ell > kECap) {
-          sm.ovf = 1;
-          return;
-        }
-        en.eS[pos] = Sa;
-        en.eSc[pos] = Sa;
-        en.ePar[pos] = (int16_t)pe;
-        en.eRank[pos] = (uint16_t)j;
-        en.eDep[pos] = (uint8_t)dn;
-        en.eLh[pos] = ah;
-        en.eLl[pos] = al | (uint64_t)dn;
-        double S2 = Sa;
-        int c2 = j;
-        for (int k = 1; k < ell; ++k) {
-          const int dd = dn + k;
-          S2 += (double)R.best_lp(dd - 1, c2);
-          c2 = R.best(dd - 1, c2);
-          const int q = pos + k;
-          en.eS[q] = S2;
-          en.eSc[q] = S2;
-          en.ePar[q] = (int16_t)(q - 1);
-          en.eRank[q] = (uint16_t)c2;
-          en.eDep[q] = (uint8_t)dd;
-          en.eLh[q] = ah;
-          en.eLl[q] = al | (uint64_t)dd;
+  // On overflow the B-th best entry found so far becomes the threshold and
+  // the enumeration restarts (as in select_kernel), then the heap.
+  for (int attempt = 0;; ++attempt) {
+    // spine prefixes reaching tau (the spine's scores do not increase)
+    const int D0 = __popcll(__ballot(lane < L && sm.sig[lane + 1] >= tau));
+    for (int d = tid; d < D0; d += kSelThreads) {
+      en.eS[d] = sm.P0[d + 1];
+      en.eSc[d] = sm.sig[d + 1];
+      en.ePar[d] = (int16_t)(d - 1);
+      en.eRank[d] = (uint16_t)tb.spine[d];
+      en.eDep[d] = (uint8_t)(d + 1);
+      en.eLh[d] = 0;
+      en.eLl[d] = (uint64_t)(d + 1);
+    }
+    if (tid == 0) sm.nE = D0;
+    __syncthreads();
+    // Generation g: the chains whose anchors deviate g times. One wave per
+    // parent: its row is read once (two floats a lane), a ballot marks the
+    // children that deviate (not the row's best) and reach tau, and each such
+    // lane appends its chain. A child's rank is 1 (the best child) plus the
+    // deviating children ordered before it: every child ordered before a
+    // qualifying one scores at least as high, so qualifies too.
+    int g0 = 0, g1 = D0, root = 1;
+    for (;;) {
+      const int np = root + (g1 - g0);
+      auto parent = [&](int u, double& S, int& d, int& c, int& pe) {
+        S = 0.0;
+        d = 0;
+        c = 0;
+        pe = -1;
+        if (!(root && u == 0)) {
+          pe = g0 + u - root;
+          S = en.eS[pe];
+          d = en.eDep[pe];
+          c = en.eRank[pe];
         }
       };
-      if (q0) emit(j0, v0, rk0);
-      if (q1) emit(j1, v1, rk1);
+      auto load = [&](int u, float& v0, float& v1) {
+        v0 = -INFINITY;
+        v1 = -INFINITY;
+        if (u >= np) return;
+        double S;
+        int d, c, pe;
+        parent(u, S, d, c, pe);
+        if (d < L) {
+          const float* r = R.row(d, c);
+          if (lane < C) v0 = r[lane];
+          if (lane + kWave < C) v1 = r[lane + kWave];
+        }
+      };
+      float n0, n1;
+      load(wv, n0, n1);
+      for (int u = wv; u < np; u += kSelWaves) {
+        const float v0 = n0, v1 = n1;
+        load(u + kSelWaves, n0, n1);  // the wave's next parent, in flight meanwhile
+        double S;
+        int d, c, pe;
+        parent(u, S, d, c, pe);
+        if (d >= L) continue;
+        const int bj = R.best(d, c);
+        const int j0 = lane, j1 = lane + kWave;
+        const bool q0 = j0 < C && j0 != bj && S + (double)v0 >= tau;
+        const bool q1 = j1 < C && j1 != bj && S + (double)v1 >= tau;
+        const uint64_t m0 = __ballot(q0), m1 = __ballot(q1);
+        if ((m0 | m1) == 0) continue;
+        const int32_t* tk = tb.tok + d * C;
+        const int t0 = j0 < C ? tk[j0] : 0x7FFFFFFF, t1 = j1 < C ? tk[j1] : 0x7FFFFFFF;
+        int rk0 = 1, rk1 = 1;
+        for (uint64_t m = m0; m; m &= m - 1) {
+          const int src = __builtin_ctzll(m);
+          const float v = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v0), src));
+          const int t = __builtin_amdgcn_readlane(t0, src);
+          rk0 += sp_better(v, t, v0, t0) ? 1 : 0;
+          rk1 += sp_better(v, t, v1, t1) ? 1 : 0;
+        }
+        for (uint64_t m = m1; m; m &= m - 1) {
+          const int src = __builtin_ctzll(m);
+          const float v = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v1), src));
+          const int t = __builtin_amdgcn_readlane(t1, src);
+          rk0 += sp_better(v, t, v0, t0) ? 1 : 0;
+          rk1 += sp_better(v, t, v1, t1) ? 1 : 0;
+        }
+        uint64_t lh = 0, ll = 0;
+        if (pe >= 0) {
+          lh = en.eLh[pe];
+          ll = en.eLl[pe] & ~63ull;
+        }
+        // the anchor (child j of the parent, score S + v, rank rk) and its
+        // best-child extensions while they reach tau
+        auto emit = [&](int j, float v, int rk) {
+          const int dn = d + 1;
+          const double Sa = S + (double)v;
+          uint64_t ah = lh, al = ll;
+          lex_set_digit(ah, al, dn, (uint32_t)rk, bpd);
+          int ell = 1;
+          {
+            double S2 = Sa;
+            int c2 = j;
+            for (int dd = dn + 1; dd <= L; ++dd) {
+              S2 += (double)R.best_lp(dd - 1, c2);
+              if (S2 < tau) break;
+              c2 = R.best(dd - 1, c2);
+              ++ell;
+            }
+          }
+          const int pos = atomicAdd(&sm.nE, ell);
+          if (pos + ell > kECap) {
+            // slots of this chain below the capacity stay unwritten: mark them
+            for (int q = pos; q < kECap; ++q) en.eSc[q] = -INFINITY;
+            sm.ovf = 1;
+            return;
+          }
+          en.eS[pos] = Sa;
+          en.eSc[pos] = Sa;
+          en.ePar[pos] = (int16_t)pe;
+          en.eRank[pos] = (uint16_t)j;
+          en.eDep[pos] = (uint8_t)dn;
+          en.eLh[pos] = ah;
+          en.eLl[pos] = al | (uint64_t)dn;
+          double S2 = Sa;
+          int c2 = j;
+          for (int k = 1; k < ell; ++k) {
+            const int dd = dn + k;
+            S2 += (double)R.best_lp(dd - 1, c2);
+            c2 = R.best(dd - 1, c2);
+            const int q = pos + k;
+            en.eS[q] = S2;
+            en.eSc[q] = S2;
+            en.ePar[q] = (int16_t)(q - 1);
+            en.eRank[q] = (uint16_t)c2;
+            en.eDep[q] = (uint8_t)dd;
+            en.eLh[q] = ah;
+            en.eLl[q] = al | (uint64_t)dd;
+          }
+        };
+        if (q0) emit(j0, v0, rk0);
+        if (q1) emit(j1, v1, rk1);
+      }
+      __syncthreads();
+      if (sm.ovf) break;
+      g0 = g1;
+      g1 = sm.nE;
+      root = 0;
+      __syncthreads();  // every wave has read nE before the next generation appends
+      if (g0 == g1) break;
     }
+    if (!sm.ovf) break;
+    const int n = sm.nE < kECap ? sm.nE : kECap;
+    if (attempt == kSelRetries || n < B) break;
+    const double t1 = sel_tau_hist(
+        sm, n, B, [&](int i) { return en.eSc[i]; }, [&](int) { return tau; },
+        reinterpret_cast<double*>(en.eLh), kECap);
+    if (!(t1 > tau)) break;
+    tau = t1;
+    if (tid == 0) sm.ovf = 0;
     __syncthreads();
-    if (sm.ovf) break;
-    g0 = g1;
-    g1 = sm.nE;
-    root = 0;
-    __syncthreads();  // every wave has read nE before the next generation appends
-    if (g0 == g1) break;
   }
 
   if (sm.ovf) {
