@@ -36,31 +36,62 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Wave-wide reductions (every lane of the wave active; every lane gets the
+// result). Inside each row of 16 lanes by DPP moves (quad_perm [1,0,3,2],
+// quad_perm [2,3,0,1], row_ror:4, row_ror:8: no LDS round trips), then the
+// four row results combined from readlanes.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp_move(T v) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit lanes");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, dpp_u32<CTRL>(__builtin_bit_cast(uint32_t, v)));
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = dpp_u32<CTRL>((uint32_t)u), hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ T lane_value(T v, int lane) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(
+        T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  }
+}
+
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  v = op(v, dpp_move<0xB1>(v));
+  v = op(v, dpp_move<0x4E>(v));
+  v = op(v, dpp_move<0x124>(v));
+  v = op(v, dpp_move<0x128>(v));
+  return op(op(lane_value(v, 0), lane_value(v, 16)), op(lane_value(v, 32), lane_value(v, 48)));
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    T w = __shfl_xor(v, o);
-    v = v > w ? v : w;
-  }
-  return v;
+  return wave_reduce(v, [](T a, T b) { return a > b ? a : b; });
 }
 
 template <typename T>
 __device__ __forceinline__ T wave_min(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    T w = __shfl_xor(v, o);
-    v = v < w ? v : w;
-  }
-  return v;
+  return wave_reduce(v, [](T a, T b) { return a < b ? a : b; });
 }
 
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return wave_reduce(v, [](T a, T b) { return a + b; });
 }
 
 // Inclusive scan of one int per lane over the 64 lanes, by DPP: shifts by
