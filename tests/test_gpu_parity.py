@@ -373,3 +373,40 @@ def test_chain_closed_form_through_gpu(a, g, printed):
     tokens = 1.0 + float(np.exp(t["logq"][0].astype(np.float64)).sum())
     assert tokens == pytest.approx((1 - a ** (g + 1)) / (1 - a), abs=1e-5)
     assert round(tokens, 2 if printed != 3.4 else 1) == pytest.approx(printed)
+
+
+def test_build_accept_graph_replays_match_eager():
+    # build + accept captured once as a HIP graph; between replays new logits
+    # and targets are copied into the captured inputs and the host
+    # synchronises; every replay must equal the eager calls on the same input.
+    B, L = 64, 15
+    xs = [gen.make_logits(2, s) for s in range(3)]
+    d = to_device(xs[0], BF16)
+    tree = pkg.ddtree_build(d, B)
+    tgt = torch.zeros((1, B + 1), dtype=torch.int32, device=DEV)
+    acc = pkg.ddtree_accept(tree["tree_tokens"], tree["parents"], tree["num_nodes"], tgt, L)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pkg.ddtree_build(d, B, out=tree)
+        pkg.ddtree_accept(tree["tree_tokens"], tree["parents"], tree["num_nodes"], tgt, L, out=acc)
+    torch.cuda.synchronize()
+    accepted = 0
+    for rep in range(6):
+        s = rep % 3
+        d.copy_(to_device(xs[s], BF16))
+        et = to_host(pkg.ddtree_build(d, B))
+        Y = gen.drafter_draws(2, s, xs[s], BF16)
+        tgt.copy_(torch.from_numpy(gen.node_targets_from_depths(Y, et["depths"], et["num_nodes"], B)))
+        ea = to_host(pkg.ddtree_accept(torch.from_numpy(et["tree_tokens"]).to(DEV),
+                                       torch.from_numpy(et["parents"]).to(DEV),
+                                       torch.from_numpy(et["num_nodes"]).to(DEV), tgt, L))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = to_host({**tree, **acc})
+        for k, v in {**et, **ea}.items():
+            np.testing.assert_array_equal(got[k], v, err_msg=f"replay {rep}: {k}")
+        accepted += int(got["accept_len"][0])
+    _say("graph replays: accepted nodes over six rounds", accepted)
