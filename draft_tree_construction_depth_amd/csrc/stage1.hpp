@@ -389,9 +389,18 @@ __global__ __launch_bounds__(kS1Threads) void stage1_chunk_kernel(Stage1Params p
 constexpr int kMergeWaves = 4;  // one workgroup of four waves per row
 constexpr int kMergeWSlots = (kMergeSlots + kMergeWaves - 1) / kMergeWaves;
 
+// Value-code bins of the bf16 merge (codes between the largest chunk
+// threshold and the row maximum).
+constexpr int kMergeBins = 1024;
+
 struct MergeSmem {
-  uint64_t win[512];            // the row's K winners (K <= 512)
-  int cnt[2][kMergeWaves];      // per-wave counts of a bisection step, double buffered
+  union {
+    uint64_t win[512];                     // the row's K winners (K <= 512)
+    uint64_t sorted[kMergeSlots * kWave];  // bf16: candidates in code order
+  };
+  int hist[kMergeBins];  // bf16: candidates per code, then those in higher codes
+  int scan[kMergeWaves];
+  int cnt[2][kMergeWaves];  // per-wave counts of a bisection step, double buffered
   int nw[kMergeWaves];
   uint64_t hi[kMergeWaves];
 };
@@ -472,6 +481,43 @@ __global__ __launch_bounds__(kWave* kMergeWaves) void stage1_merge_kernel(Stage1
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kMergeWaves; ++i) hi = sm.hi[i] > hi ? sm.hi[i] : hi;
+  int32_t* oid = p.out_ids + row * K;
+  float* oval = p.out_vals + row * K;
+  // bf16 rows: every candidate's rank from a histogram over its value code
+  // (candidates in higher codes, by an exclusive scan) plus the larger keys
+  // of its own code (equal values, ordered by id); no bisection
+  const int lo_code = (int)(lo >> 48), hi_code = (int)(hi >> 48);
+  const int nbins = hi_code - lo_code + 1;
+  if (DT == 0 && lo != 0 && nbins <= kMergeBins) {
+    for (int i = tid; i < nbins; i += kWave * kMergeWaves) sm.hist[i] = 0;
+    __syncthreads();
+    int bin[kMergeWSlots], slot[kMergeWSlots];
+#pragma unroll
+    for (int q = 0; q < kMergeWSlots; ++q) {
+      bin[q] = hi_code - (int)(v[q] >> 48);
+      slot[q] = v[q] != 0 ? atomicAdd(&sm.hist[bin[q]], 1) : 0;
+    }
+    __syncthreads();
+    const int total = block_excl_scan<kWave * kMergeWaves>(sm.hist, nbins, sm.scan);  // + barrier
+#pragma unroll
+    for (int q = 0; q < kMergeWSlots; ++q)
+      if (v[q] != 0 && sm.hist[bin[q]] < K) sm.sorted[sm.hist[bin[q]] + slot[q]] = v[q];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kMergeWSlots; ++q) {
+      if (v[q] == 0) continue;
+      const int b0 = sm.hist[bin[q]];
+      if (b0 >= K) continue;
+      const int b1 = bin[q] + 1 < nbins ? sm.hist[bin[q] + 1] : total;
+      int rank = b0;
+      for (int j = b0; j < b1; ++j) rank += sm.sorted[j] > v[q] ? 1 : 0;
+      if (rank < K) {
+        oid[rank] = (int32_t)cand_id(v[q]);
+        oval[rank] = key_value(cand_vkey(v[q]));
+      }
+    }
+    return;
+  }
   const int top = (lo ^ hi) == 0 ? 31 : 63 - __clzll(lo ^ hi);
   uint64_t T = top >= 63 ? 0ull : lo & ~((2ull << top) - 1ull);
   for (int bit = top < 63 ? top : 63; bit >= 32; --bit) {
@@ -510,8 +556,6 @@ __global__ __launch_bounds__(kWave* kMergeWaves) void stage1_merge_kernel(Stage1
   }
   __syncthreads();
   // rank of winner i = number of larger winners
-  int32_t* oid = p.out_ids + row * K;
-  float* oval = p.out_vals + row * K;
   for (int i = tid; i < K; i += kWave * kMergeWaves) {
     const uint64_t mine = sm.win[i];
     int rank = 0;
