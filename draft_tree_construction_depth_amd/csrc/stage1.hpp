@@ -394,11 +394,14 @@ constexpr int kMergeWSlots = (kMergeSlots + kMergeWaves - 1) / kMergeWaves;
 constexpr int kMergeBins = 1024;
 
 struct MergeSmem {
-  union {
+  union alignas(16) {
     uint64_t win[512];                     // the row's K winners (K <= 512)
     uint64_t sorted[kMergeSlots * kWave];  // bf16: candidates in code order
   };
   int hist[kMergeBins];  // bf16: candidates per code, then those in higher codes
+  uint64_t wins[512];    // bf16: the K winners by rank
+  uint32_t range[kMergeSlots * kWave];  // bf16: each placed candidate's code range
+  int nrel;
   int scan[kMergeWaves];
   int cnt[2][kMergeWaves];  // per-wave counts of a bisection step, double buffered
   int nw[kMergeWaves];
@@ -499,9 +502,10 @@ __global__ __launch_bounds__(kWave* kMergeWaves) void stage1_merge_kernel(Stage1
     }
     __syncthreads();
     const int total = block_excl_scan<kWave * kMergeWaves>(sm.hist, nbins, sm.scan);  // + barrier
-#pragma unroll
-    for (int q = 0; q < kMergeWSlots; ++q)
-      if (v[q] != 0 && sm.hist[bin[q]] < K) sm.sorted[sm.hist[bin[q]] + slot[q]] = v[q];
+    // candidates of the codes that start below rank K, in code order, each
+    // with its code's range [b0, b1) (packed b0 << 16 | b1); they fill
+    // positions [0, nrel)
+    if (tid == 0) sm.nrel = 0;
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < kMergeWSlots; ++q) {
@@ -509,12 +513,40 @@ __global__ __launch_bounds__(kWave* kMergeWaves) void stage1_merge_kernel(Stage1
       const int b0 = sm.hist[bin[q]];
       if (b0 >= K) continue;
       const int b1 = bin[q] + 1 < nbins ? sm.hist[bin[q] + 1] : total;
-      int rank = b0;
-      for (int j = b0; j < b1; ++j) rank += sm.sorted[j] > v[q] ? 1 : 0;
-      if (rank < K) {
-        oid[rank] = (int32_t)cand_id(v[q]);
-        oval[rank] = key_value(cand_vkey(v[q]));
+      sm.sorted[b0 + slot[q]] = v[q];
+      sm.range[b0 + slot[q]] = ((uint32_t)b0 << 16) | (uint32_t)b1;
+      if (b0 + slot[q] == b1 - 1) atomicMax(&sm.nrel, b1);
+    }
+    __syncthreads();
+    // one candidate per thread: its rank is its code's start plus the larger
+    // keys of its code (16-byte LDS reads, eight keys a batch)
+    const int nrel = sm.nrel;
+    const u64x2* s2 = (const u64x2*)&sm.sorted[0];
+    for (int t = tid; t < nrel; t += kWave * kMergeWaves) {
+      const uint64_t me = sm.sorted[t];
+      const uint32_t rg = sm.range[t];
+      const int b0 = (int)(rg >> 16), b1 = (int)(rg & 0xFFFFu);
+      int rank = b0, j = b0;
+      if ((j & 1) && j < b1) rank += sm.sorted[j++] > me ? 1 : 0;
+      for (; j + 8 <= b1; j += 8) {
+        const u64x2 a0 = s2[j >> 1], a1 = s2[(j >> 1) + 1], a2 = s2[(j >> 1) + 2],
+                    a3 = s2[(j >> 1) + 3];
+        rank += (a0.x > me) + (a0.y > me) + (a1.x > me) + (a1.y > me) + (a2.x > me) + (a2.y > me) +
+                (a3.x > me) + (a3.y > me);
       }
+      for (; j + 2 <= b1; j += 2) {
+        const u64x2 a0 = s2[j >> 1];
+        rank += (a0.x > me) + (a0.y > me);
+      }
+      if (j < b1) rank += sm.sorted[j] > me ? 1 : 0;
+      if (rank < K) sm.wins[rank] = me;
+    }
+    __syncthreads();
+    // the K winners in order, written by consecutive threads
+    for (int i = tid; i < K; i += kWave * kMergeWaves) {
+      const uint64_t k = sm.wins[i];
+      oid[i] = (int32_t)cand_id(k);
+      oval[i] = key_value(cand_vkey(k));
     }
     return;
   }
