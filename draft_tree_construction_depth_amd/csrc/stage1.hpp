@@ -24,10 +24,11 @@
 //  stage1_chunk_kernel + stage1_merge_kernel (few rows): one workgroup per
 //    chunk writes a record (survivors, threshold, normaliser partial); one
 //    workgroup per row then keeps the survivors at or above the largest
-//    chunk threshold, finds the exact K-th (value, id) key by a ballot
-//    bisection over registers (four waves' counts summed in LDS), ranks the
-//    K winners by counting and writes the row's table and log-sum-exp
-//    (float64).
+//    chunk threshold and ranks them: bf16 rows by a histogram over their
+//    value codes (one scan; equal values ordered by id), otherwise through
+//    the exact K-th (value, id) key from a ballot bisection over registers
+//    (four waves' counts summed in LDS) and counting; then writes the row's
+//    table and log-sum-exp (float64).
 //  stage1_row_kernel (many rows): one workgroup walks all chunks of its row
 //    with double-buffered register loads (chunk i+1 in flight while chunk i
 //    is processed), raises the row threshold on a schedule of chunks, keeps
@@ -399,7 +400,7 @@ struct MergeSmem {
     uint64_t sorted[kMergeSlots * kWave];  // bf16: candidates in code order
   };
   int hist[kMergeBins];  // bf16: candidates per code, then those in higher codes
-  uint64_t wins[512];    // bf16: the K winners by rank
+  uint64_t ranked[512];  // bf16: the K winners by rank
   uint32_t range[kMergeSlots * kWave];  // bf16: each placed candidate's code range
   int nrel;
   int scan[kMergeWaves];
@@ -539,12 +540,12 @@ __global__ __launch_bounds__(kWave* kMergeWaves) void stage1_merge_kernel(Stage1
         rank += (a0.x > me) + (a0.y > me);
       }
       if (j < b1) rank += sm.sorted[j] > me ? 1 : 0;
-      if (rank < K) sm.wins[rank] = me;
+      if (rank < K) sm.ranked[rank] = me;
     }
     __syncthreads();
     // the K winners in order, written by consecutive threads
     for (int i = tid; i < K; i += kWave * kMergeWaves) {
-      const uint64_t k = sm.wins[i];
+      const uint64_t k = sm.ranked[i];
       oid[i] = (int32_t)cand_id(k);
       oval[i] = key_value(cand_vkey(k));
     }
