@@ -65,6 +65,8 @@ ROW_CASES = [
     (6, 3000, 1, BF16, "gauss"),
     (1, 7, 7, F32, "ints"),             # K == V
     (40, 151936, 128, BF16, "gauss"),
+    (5, 30000, 64, BF16, "spike"),
+    (3, 151936, 128, BF16, "straddle"),
     # >= 512 rows of 16-byte multiples: one workgroup per row
     (512, 8192, 128, BF16, "gauss"),
     (520, 6000, 64, BF16, "straddle"),
@@ -93,6 +95,11 @@ def _rows(rows, V, dt, kind, seed=0):
     elif kind == "ints":
         x = rng.integers(-3, 4, (rows, V)).astype(np.float32)
         x[:, :5] = -0.0
+    elif kind == "spike":
+        # one value 3e4 per row: the candidates' value codes span far more
+        # than the merge's histogram holds (its bisection path)
+        x = rng.standard_normal((rows, V)).astype(np.float32)
+        x[np.arange(rows), rng.integers(0, V, rows)] = 3e4
     else:
         x = np.full((rows, V), 1.25, np.float32)
     return gen.f32_to_bf16_bits(x) if dt == BF16 else x
