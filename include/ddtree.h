@@ -102,7 +102,10 @@ size_t ddtree_row_topk_workspace_size(int64_t rows, int64_t V, int32_t K, int dt
  *
  * logits       [batch][L][V] drafter logits, bf16 (DDT_BF16) or float32
  *              (DDT_F32), 16-byte aligned (DDT_EINVAL otherwise). Row d of a
- *              request is draft position d+1. Finite values only.
+ *              request is draft position d+1. Finite values of magnitude
+ *              below 2^22 only (the normaliser's exponent arguments are
+ *              float32; beyond that its offset can fall short by one
+ *              float32 unit of x * log2(e), and the result is undefined).
  * B            node budget, 1 <= B <= DDT_MAX_B. K = min(B, V) tokens per
  *              row are ranked; 1 <= L <= DDT_MAX_L; L*K <= DDT_MAX_LK; and
  *              L * ceil(log2 K) <= 122.
