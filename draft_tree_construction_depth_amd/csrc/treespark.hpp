@@ -59,7 +59,9 @@ struct TsGemmParams {
   int32_t* pid;            // [nvt][Mtot][kTsKMax]
 };
 
-struct TsGemmSmem {
+// 16-byte aligned so that the fragment reads and the staging stores are
+// single 16-byte LDS instructions.
+struct alignas(16) TsGemmSmem {
   union {
     uint16_t g[2][kTsBM][kTsKT + kTsGPad];  // parents' embedding rows, double buffered
     struct {
@@ -212,16 +214,23 @@ __global__ __launch_bounds__(kTsThreads) void ts_gemm_kernel(TsGemmParams p) {
     const int kn = ks + 2 < nks ? ks + 2 : nks - 1;  // always issue, so wait counts stay static
     load_w(wl, kn);
     load_g(gl, kn);
+    // every B fragment of the step read before the first MFMA, so that the
+    // LDS latency is paid once per step, not once per MFMA
+    u32x4 braw[4][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (c < nct)
+          braw[s][c] = *(const u32x4*)&sm.g[buf][c * 32 + (l & 31)][16 * s + 8 * (l >> 5)];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const bf16x8 a = __builtin_bit_cast(bf16x8, wu[s]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        if (c < nct) {
-          const u32x4 braw = *(const u32x4*)&sm.g[buf][c * 32 + (l & 31)][16 * s + 8 * (l >> 5)];
-          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, braw),
-                                                           acc[c], 0, 0, 0);
-        }
+        if (c < nct)
+          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              a, __builtin_bit_cast(bf16x8, braw[s][c]), acc[c], 0, 0, 0);
       }
     }
     if (ks + 1 < nks) store_g(gs, buf ^ 1);
