@@ -51,7 +51,9 @@ struct SpTableParams {
   float* blp;           // [batch][L-1][C]: its log-prob
 };
 
-struct SpTableSmem {
+// 16-byte aligned so that the fragment reads and the row stores are single
+// 16-byte LDS instructions.
+struct alignas(16) SpTableSmem {
   union {
     uint16_t w2[kSpC][kSpPitch];  // the child candidates' W2t rows (MFMA A operand)
     float tile[kSpC][kSpTile];    // then the finished log-prob rows
@@ -118,15 +120,20 @@ __global__ __launch_bounds__(kSpThreads) void sp_table_kernel(SpTableParams p) {
 #pragma unroll
   for (int ks = 0; ks < kSpRMax / kSpKT; ++ks) {
     if (ks < nks) {
+      // the step's A fragments read before its MFMAs
+      u32x4 araw[4][4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          araw[s][m] = *(const u32x4*)&sm.u.w2[m * 32 + (l & 31)][ks * kSpKT + 16 * s + 8 * h];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const bf16x8 bv = __builtin_bit_cast(bf16x8, bq[ks][s]);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const u32x4 araw = *(const u32x4*)&sm.u.w2[m * 32 + (l & 31)][ks * kSpKT + 16 * s + 8 * h];
-          acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, araw), bv,
-                                                           acc[m], 0, 0, 0);
-        }
+        for (int m = 0; m < 4; ++m)
+          acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, araw[s][m]),
+                                                           bv, acc[m], 0, 0, 0);
       }
     }
   }
