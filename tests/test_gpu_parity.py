@@ -76,6 +76,7 @@ ROW_CASES = [
     (512, 4096, 128, F32, "gauss"),
     (512, 151936, 256, BF16, "straddle"),
     (512, 151936, 256, BF16, "trend"),
+    (512, 40000, 128, BF16, "zeros"),
 ]
 
 
@@ -95,6 +96,14 @@ def _rows(rows, V, dt, kind, seed=0):
     elif kind == "ints":
         x = rng.integers(-3, 4, (rows, V)).astype(np.float32)
         x[:, :5] = -0.0
+    elif kind == "zeros":
+        # mostly -1 with about 1% each of -0 and +0 and 40 ones per row, so
+        # the K-th value is zero: the threshold is exactly +0 while zeros
+        # (many of them -0 beside nonzero neighbours) are still being kept
+        u = rng.random((rows, V))
+        x = np.where(u < 0.01, -0.0, np.where(u < 0.02, 0.0, -1.0)).astype(np.float32)
+        for i in range(rows):
+            x[i, rng.choice(V, 40, replace=False)] = 1.0
     elif kind == "spike":
         # one value 3e4 per row: the candidates' value codes span far more
         # than the merge's histogram holds (its bisection path)
