@@ -231,6 +231,10 @@ EDGE = [
     ("unaligned_V", 15, 10001, 128, BF16, "gauss"),
     ("L32_K8", 32, 8, 8, F32, "gauss"),
     ("B512_L13", 13, 5000, 512, BF16, "gauss"),
+    # rank-tuple keys of 120 bits (L * ceil(log2 K) close to the 122-bit
+    # bound) on full-depth trees whose deviations reach depth 8 and 16
+    ("L30_K16_key120_chain", 30, 16, 48, F32, "chain"),
+    ("L20_K64_key120_chain", 20, 3000, 64, BF16, "chain"),
 ]
 
 
@@ -243,9 +247,16 @@ def _edge_logits(L, V, dt, kind, batch, seed):
     elif kind == "ints":
         x = rng.integers(-2, 3, (batch, L, V)).astype(np.float32)
     else:
-        x = np.full((batch, L, V), -900.0, np.float32)
+        # one dominant token per row; "chain" makes the runner-up on even rows
+        # so unlikely that the tree's spine runs to depth L. Its background
+        # sits at -30, not -900: against -900 every other term of an odd row
+        # underflows in float64, the oracle's log-probability of the dominant
+        # token is exactly 0, and a prefix ties exactly with its extension,
+        # a tie that the kernels' float32 normaliser (within 2e-6) does not
+        # reproduce bit for bit
+        x = np.full((batch, L, V), -30.0 if kind == "chain" else -900.0, np.float32)
         x[:, :, 3] = rng.uniform(-5, 5, (batch, L)).astype(np.float32)
-        x[:, ::2, 7] = x[:, ::2, 3] - 0.5
+        x[:, ::2, 7] = x[:, ::2, 3] - (5.0 if kind == "chain" else 0.5)
     return gen.f32_to_bf16_bits(x) if dt == BF16 else x
 
 
