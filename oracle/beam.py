@@ -26,6 +26,11 @@ Readings of what the post leaves open (plainest consistent ones):
     ends the tree;
   * the tree is emitted depth by depth, each depth in beam order, so a
     parent precedes its children; node j+1 is the j-th emitted node.
+
+Near-tie variants: each depth's cut (its w-th and (w+1)-th candidates) is
+recorded with its gap; a variant keeps the (w+1)-th in place of the w-th at
+the given depths and continues with the same arithmetic. The parity check
+compares a device tree with the variants of cuts closer than 1e-5.
 """
 
 from __future__ import annotations
@@ -41,8 +46,9 @@ def even_widths(B: int, L: int) -> list[int]:
     return [q + (1 if d < r else 0) for d in range(L)]
 
 
-def build_request(x: np.ndarray, W1: np.ndarray, W2t: np.ndarray, widths, C: int, diag=None):
-    rows = S.Rows(x, W1, W2t, C)
+def build_request(x: np.ndarray, W1: np.ndarray, W2t: np.ndarray, widths, C: int, diag=None,
+                  flips=(), rows=None):
+    rows = S.Rows(x, W1, W2t, C) if rows is None else rows
     L = rows.L
     beam = [((), None, 0.0, 0)]  # (rank tuple, token, score, node number)
     tokens, parents, logq, depths = [], [], [], []
@@ -56,8 +62,10 @@ def build_request(x: np.ndarray, W1: np.ndarray, W2t: np.ndarray, widths, C: int
                 cands.append((sc + float(cl[r]), ranks + (r,), int(ct[r]), node))
         cands.sort(key=lambda c: (-c[0], c[1]))
         if w < len(cands) and w > 0:
-            cut_gaps.append(cands[w - 1][0] - cands[w][0])
-        kept = cands[:w]
+            cut_gaps.append((d, cands[w - 1][0] - cands[w][0]))
+            kept = cands[:w - 1] + [cands[w]] if d in flips else cands[:w]
+        else:
+            kept = cands[:w]
         beam = []
         for sc, ranks, tok, par in kept:
             tokens.append(tok)
@@ -68,7 +76,9 @@ def build_request(x: np.ndarray, W1: np.ndarray, W2t: np.ndarray, widths, C: int
         if not beam:
             break
     if diag is not None:
-        diag["cut_gaps"] = cut_gaps
+        diag["cut_gaps"] = [g for _, g in cut_gaps]
+        diag["cuts"] = cut_gaps
+        diag["rows"] = rows
     return tokens, parents, logq, depths
 
 
@@ -93,3 +103,26 @@ def build(logits_bits: np.ndarray, W1_bits: np.ndarray, W2t_bits: np.ndarray, wi
         out["depths"].append(np.array(dep + [0] * pad, np.int32))
         out["num_nodes"].append(n)
     return {k: np.asarray(v) for k, v in out.items()}
+
+
+def near_tie_variants(x_bits: np.ndarray, W1_bits: np.ndarray, W2t_bits: np.ndarray, widths,
+                      C: int, diag: dict, excuse: float = 1e-5, max_flips: int = 2):
+    """The request's beam trees with one or two near-tie cuts (gap < excuse)
+    taken the other way: a list of (label, tree dict). diag is the request's
+    diagnostics from build (its conditioned rows are reused)."""
+    near = [d for d, g in diag["cuts"] if g < excuse]
+    sets = [(d,) for d in near]
+    if max_flips >= 2:
+        sets += [(a, c) for i, a in enumerate(near) for c in near[i + 1:]]
+    B = int(sum(widths))
+    out = []
+    for s in sets:
+        t, p, q, dep = build_request(None, None, None, widths, C, flips=s, rows=diag["rows"])
+        n = len(t)
+        pad = B - n
+        out.append(("cut@" + ",".join(str(d + 1) for d in s),
+                    dict(tree_tokens=np.array(t + [-1] * pad, np.int32),
+                         parents=np.array(p + [-1] * pad, np.int32),
+                         logq=np.array(q + [-np.inf] * pad, np.float64),
+                         depths=np.array(dep + [0] * pad, np.int32), num_nodes=n)))
+    return out

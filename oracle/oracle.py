@@ -16,19 +16,31 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "ddtree_oracle.c")
-LIB = os.path.join(HERE, "libddtree_oracle.so")
+# DDT_ORACLE_LIB selects another build of the same source (the sanitizer
+# build of the CPU checks, see build_oracle(sanitize=True)).
+LIB = os.environ.get("DDT_ORACLE_LIB") or os.path.join(HERE, "libddtree_oracle.so")
 
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
 
 
-def build_oracle() -> str:
-    """Compile the oracle with gcc -O2 (no fast-math). Returns the library path."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", LIB + ".tmp", SRC, "-lm",
+def build_oracle(sanitize: bool = False, out: str | None = None) -> str:
+    """Compile the oracle with gcc -O2 (no fast-math). Returns the library path.
+
+    sanitize=True builds it with AddressSanitizer and UndefinedBehaviorSanitizer
+    (host code, gcc; every finding aborts) for the CPU checks that run the pins
+    under them; such a library is loaded by a process that preloads libasan.
+    """
+    out = out or LIB
+    flags = ["-O2"]
+    if sanitize:
+        flags = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                 "-fno-sanitize-recover=all"]
+    cmd = ["gcc", *flags, "-std=c11", "-fPIC", "-shared", "-o", out + ".tmp", SRC, "-lm",
            "-lpthread"]
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 _lib = None

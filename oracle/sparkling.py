@@ -111,6 +111,7 @@ def build_request(x: np.ndarray, W1: np.ndarray, W2t: np.ndarray, B: int, C: int
     if diag is not None:
         diag["pops"] = pops
         diag["next_score"] = -heap[0][0] if heap else -np.inf
+        diag["rows"] = R
     return (np.array(tokens + [-1] * pad, np.int32), np.array(parents + [-1] * pad, np.int32),
             np.array(logq + [-np.inf] * pad, np.float64), np.array(depths + [0] * pad, np.int32), n)
 

@@ -1,3 +1,4 @@
+import json
 import os
 import sys
 
@@ -19,3 +20,19 @@ def _oracle_built():
     if not os.path.exists(O.LIB):
         O.build_oracle()
     yield
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """Write the parity class counts of the run to $DDT_PARITY_JSON, if set."""
+    path = os.environ.get("DDT_PARITY_JSON")
+    if not path:
+        return
+    try:
+        from parity_util import RECORD
+    except ImportError:
+        return
+    if not RECORD:
+        return
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump({"exit_status": int(exitstatus), "counts": RECORD}, f, indent=1, sort_keys=True)

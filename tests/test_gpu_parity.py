@@ -20,7 +20,7 @@ import torch
 import draft_tree_construction_depth_amd as pkg
 from draft_tree_construction_depth_amd import gen
 from oracle import oracle as O
-from parity_util import classify, compare_batch, to_device, to_host
+from parity_util import classify, compare_batch, record, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -145,12 +145,36 @@ def test_row_topk_full_batch64_tables():
 
 
 # ----------------------------------------------------------------------------
-# stage 2 (+3): whole build against the oracle
+# stage 2 (+3): whole build against the oracle; stage 4 on the device's trees
 # ----------------------------------------------------------------------------
 
 def _check_counts(res, label):
+    record(label, res["counts"])
     _say(label, res["counts"])
     assert not res["fails"], f"{label}: {res['fails'][:5]}"
+
+
+def _check_mask_of_own_parents(g, B):
+    # the mask is a function of the parents: every request, excused or not
+    np.testing.assert_array_equal(g["mask"], O.mask(g["parents"], g["num_nodes"], B))
+
+
+def _walk_gpu_tree(g, tgt, L):
+    """ddtree_accept on the device's own trees against the oracle's walk of
+    the same trees and targets (bit-exact)."""
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    r = pkg.ddtree_accept(dv(g["tree_tokens"]), dv(g["parents"]), dv(g["num_nodes"]), dv(tgt), L)
+    torch.cuda.synchronize()
+    ga = [r[k].cpu().numpy() for k in ("accepted_nodes", "accept_len", "next_token")]
+    oa = O.accept(g["tree_tokens"], g["parents"], g["num_nodes"], tgt, L)
+    for a, b in zip(ga, oa):
+        np.testing.assert_array_equal(a, b)
+    return ga
+
+
+def _drafter_targets(cfg, seed, x, g, B, first=0):
+    Y = gen.drafter_draws(cfg, seed, x, gen.CONFIGS[cfg]["dtype"], first=first)
+    return gen.node_targets_from_depths(Y, g["depths"], g["num_nodes"], B)
 
 
 @pytest.mark.parametrize("seed", range(5))
@@ -159,38 +183,45 @@ def test_build_c1(seed):
     g = _gpu_build(x, F32, 32)
     o = _oracle(1, seed)
     res = compare_batch(g, o, 32)
-    _check_counts(res, f"c1 seed {seed}")
+    _check_counts(res, "batch-1 V=1024 f32 B=32")
     assert res["counts"].get("exact", 0) == 1
     np.testing.assert_array_equal(g["mask"], O.mask(o["parents"], o["num_nodes"], 32))
 
 
 @pytest.mark.parametrize("seed", range(5))
-def test_build_c2(seed):
+def test_build_and_walk_c2(seed):
     x = _inputs(2, seed)
     g = _gpu_build(x, BF16, 64)
     o = _oracle(2, seed)
-    _check_counts(compare_batch(g, o, 64), f"c2 seed {seed}")
+    _check_counts(compare_batch(g, o, 64), "batch-1 V=151936 bf16 B=64")
+    _check_mask_of_own_parents(g, 64)
+    _, alen, _ = _walk_gpu_tree(g, _drafter_targets(2, seed, x, g, 64), 15)
+    _say("c2 seed", seed, "accept_len", int(alen[0]))
 
 
-def test_build_c3_full_batch():
-    x = _inputs(3, 0)
+@pytest.mark.parametrize("seed", range(3))
+def test_build_and_walk_c3_full_batch(seed):
+    x = _inputs(3, seed)
     g = _gpu_build(x, BF16, 128)
-    o = _oracle(3, 0)
-    res = compare_batch(g, o, 128)
-    _check_counts(res, "c3 seed 0 (64 requests)")
-    exact = [b for b in range(64) if classify({k: v[b:b + 1] for k, v in g.items()},
-                                              {k: v[b:b + 1] for k, v in o.items()}, 0, 128) == "exact"]
-    om = O.mask(o["parents"][exact], o["num_nodes"][exact], 128)
-    np.testing.assert_array_equal(g["mask"][exact], om)
+    o = _oracle(3, seed)
+    _check_counts(compare_batch(g, o, 128), "batch-64 V=151936 bf16 B=128")
+    _check_mask_of_own_parents(g, 128)
+    _, alen, _ = _walk_gpu_tree(g, _drafter_targets(3, seed, x, g, 128), 15)
+    _say("c3 seed", seed, "mean accept_len", float(alen.mean()))
 
 
-def test_build_c5_full_batch_sampled():
-    # The GPU builds all 256 trees; the oracle checks a 32-request sample.
-    x = _inputs(5, 0)
+@pytest.mark.parametrize("seed", range(2))
+def test_build_and_walk_c5_full_batch(seed):
+    # All 256 trees of the batch-256 workload in its own launch shape; the
+    # walk (B = 256: four register slots per lane) on every tree.
+    x = gen.make_logits(5, seed)
+    _say("c5 seed", seed, "inputs ready")
     g = _gpu_build(x, BF16, 256)
-    idx = np.arange(0, 256, 8)
-    o = O.build(np.ascontiguousarray(x[idx]), BF16, 256, threads=THREADS)
-    _check_counts(compare_batch(g, o, 256, idx=idx), "c5 seed 0 (32 of 256 requests)")
+    o = O.build(x, BF16, 256, threads=THREADS)
+    _check_counts(compare_batch(g, o, 256), "batch-256 V=151936 bf16 B=256")
+    _check_mask_of_own_parents(g, 256)
+    _, alen, _ = _walk_gpu_tree(g, _drafter_targets(5, seed, x, g, 256), 15)
+    _say("c5 seed", seed, "mean accept_len", float(alen.mean()))
 
 
 def test_build_c5_enumeration_overflow():
@@ -201,12 +232,8 @@ def test_build_c5_enumeration_overflow():
     x = _inputs(5, 1, batch=3, first=14)
     g = _gpu_build(x, BF16, 256)
     o = O.build(x, BF16, 256, threads=THREADS)
-    _check_counts(compare_batch(g, o, 256), "c5 seed 1 requests 14-16")
-    om = O.mask(o["parents"], o["num_nodes"], 256)
-    for b in range(3):
-        if classify({k: v[b:b + 1] for k, v in g.items()}, {k: v[b:b + 1] for k, v in o.items()},
-                    0, 256) == "exact":
-            np.testing.assert_array_equal(g["mask"][b], om[b])
+    _check_counts(compare_batch(g, o, 256), "batch-256 requests 14-16 (enumeration overflow)")
+    _check_mask_of_own_parents(g, 256)
 
 
 @pytest.mark.parametrize("seed", range(1, 4))
@@ -215,7 +242,7 @@ def test_build_c3_small_batches(seed):
     x = _inputs(3, seed, batch=3)
     g = _gpu_build(x, BF16, 128)
     o = _oracle(3, seed, batch=3)
-    _check_counts(compare_batch(g, o, 128), f"c3 seed {seed} batch 3")
+    _check_counts(compare_batch(g, o, 128), "batch-64 workload, 3-request launches")
 
 
 EDGE = [
@@ -235,6 +262,12 @@ EDGE = [
     # bound) on full-depth trees whose deviations reach depth 8 and 16
     ("L30_K16_key120_chain", 30, 16, 48, F32, "chain"),
     ("L20_K64_key120_chain", 20, 3000, 64, BF16, "chain"),
+    # the same chains against a -900 background: every other term of an odd
+    # row underflows in the oracle's float64 normaliser, the dominant token's
+    # log-probability is exactly 0 there and a prefix ties exactly with its
+    # extension (a cross-depth tie the float32 normaliser need not reproduce)
+    ("L30_K16_key120_chain_minus900", 30, 16, 48, F32, "chain900"),
+    ("L20_K64_key120_chain_minus900", 20, 3000, 64, BF16, "chain900"),
 ]
 
 
@@ -247,16 +280,13 @@ def _edge_logits(L, V, dt, kind, batch, seed):
     elif kind == "ints":
         x = rng.integers(-2, 3, (batch, L, V)).astype(np.float32)
     else:
-        # one dominant token per row; "chain" makes the runner-up on even rows
-        # so unlikely that the tree's spine runs to depth L. Its background
-        # sits at -30, not -900: against -900 every other term of an odd row
-        # underflows in float64, the oracle's log-probability of the dominant
-        # token is exactly 0, and a prefix ties exactly with its extension,
-        # a tie that the kernels' float32 normaliser (within 2e-6) does not
-        # reproduce bit for bit
+        # one dominant token per row; the chains make the runner-up on even
+        # rows so unlikely that the tree's spine runs to depth L; "chain"
+        # keeps the background at -30, "chain900" and "onehot" at -900
+        chain = kind.startswith("chain")
         x = np.full((batch, L, V), -30.0 if kind == "chain" else -900.0, np.float32)
         x[:, :, 3] = rng.uniform(-5, 5, (batch, L)).astype(np.float32)
-        x[:, ::2, 7] = x[:, ::2, 3] - (5.0 if kind == "chain" else 0.5)
+        x[:, ::2, 7] = x[:, ::2, 3] - (5.0 if chain else 0.5)
     return gen.f32_to_bf16_bits(x) if dt == BF16 else x
 
 
@@ -264,15 +294,11 @@ def _edge_logits(L, V, dt, kind, batch, seed):
 def test_build_edge_cases(case):
     name, L, V, B, dt, kind = case
     _say("edge", name)
-    x = _edge_logits(L, V, dt, kind, 3, seed=len(name))
+    x = _edge_logits(L, V, dt, kind, 3, seed=len(name) if kind != "chain900" else len(name) - 9)
     g = _gpu_build(x, dt, B)
     o = O.build(x, dt, B)
-    _check_counts(compare_batch(g, o, B), name)
-    om = O.mask(o["parents"], o["num_nodes"], B)
-    for b in range(3):
-        if classify({k: v[b:b + 1] for k, v in g.items()}, {k: v[b:b + 1] for k, v in o.items()},
-                    0, B) == "exact":
-            np.testing.assert_array_equal(g["mask"][b], om[b])
+    _check_counts(compare_batch(g, o, B), f"edge {name}")
+    _check_mask_of_own_parents(g, B)
 
 
 def test_build_is_deterministic_and_reuses_workspace():
@@ -350,13 +376,15 @@ def test_walk_c1_fresh_argmax_targets():
         _walk_both(o, tgt, 15)
 
 
-def test_walk_c3_drafter_targets_full_batch():
-    x = _inputs(3, 0)
-    o = _oracle(3, 0)
-    Y = gen.drafter_draws(3, 0, x, BF16)
-    tgt = gen.node_targets_from_depths(Y, o["depths"], o["num_nodes"], 128)
+@pytest.mark.parametrize("cfg,seed", [(2, 1), (3, 0)])
+def test_walk_drafter_targets_on_oracle_trees(cfg, seed):
+    x = _inputs(cfg, seed)
+    o = _oracle(cfg, seed)
+    B = gen.CONFIGS[cfg]["B"]
+    Y = gen.drafter_draws(cfg, seed, x, BF16)
+    tgt = gen.node_targets_from_depths(Y, o["depths"], o["num_nodes"], B)
     _, alen, _ = _walk_both(o, tgt, 15)
-    _say("c3 accept_len mean", float(alen.mean()))
+    _say(f"workload {cfg} accept_len mean", float(alen.mean()))
 
 
 def test_prop1_monte_carlo_through_gpu_walk():
@@ -437,3 +465,28 @@ def test_build_accept_graph_replays_match_eager():
             np.testing.assert_array_equal(got[k], v, err_msg=f"replay {rep}: {k}")
         accepted += int(got["accept_len"][0])
     _say("graph replays: accepted nodes over six rounds", accepted)
+
+
+def test_two_streams_same_shape_have_separate_workspaces():
+    # Few-row builds (the chunk + merge path, which keeps per-chunk records
+    # in the workspace) of one shape enqueued on two streams at once: the
+    # binding gives each stream its own workspace, so neither call reads the
+    # other's records. Both must equal the same builds run alone.
+    xs = [_inputs(2, s) for s in (0, 1)]
+    ds = [to_device(x, BF16) for x in xs]
+    alone = [to_host(pkg.ddtree_build(d, 64)) for d in ds]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    for rep in range(3):
+        outs = [None, None]
+        torch.cuda.synchronize()
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                outs[i] = pkg.ddtree_build(ds[i], 64)
+        torch.cuda.synchronize()
+        for i in range(2):
+            got = to_host(outs[i])
+            for k, v in alone[i].items():
+                np.testing.assert_array_equal(got[k], v, err_msg=f"rep {rep} stream {i}: {k}")
+    ws_keys = [k for k in pkg._lib._workspaces if k[0] == "build" and k[3][0] == 1]
+    assert len({k[2] for k in ws_keys}) >= 2

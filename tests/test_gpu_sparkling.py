@@ -4,14 +4,12 @@ construction").
 
 The top-C pre-filter is exact on both sides (bf16 / f32 logits, ties by
 id). Conditioned log-probs are float32 on the device (MFMA dot products,
-float32 log-sum-exp), float64 in the oracle, so trees must match exactly
-except in two counted classes:
-  E1  the node sets differ and the oracle's B-th and (B+1)-th prefix scores
-      differ by less than 1e-5;
-  E2  the node sets agree and only prefixes whose oracle scores differ by
-      less than 1e-5 appear in a different order.
-logq of every common prefix within 1e-4. Exact ties (flat rows, zero head)
-are decided by token ids and rank tuples on both sides: bit-exact trees.
+float32 log-sum-exp), float64 in the oracle, so trees are compared by the
+excuse classes of oracle/parity.py (E1 at the budget boundary, E2 order
+swaps of prefixes < 1e-5 apart), with every device node re-scored on the
+oracle's conditioned rows; logq within 1e-4. Exact ties (flat rows, zero
+head) are decided by token ids and rank tuples on both sides: bit-exact
+trees.
 """
 
 import numpy as np
@@ -22,10 +20,10 @@ import draft_tree_construction_depth_amd as pkg
 from draft_tree_construction_depth_amd import gen
 from oracle import oracle as O
 from oracle import sparkling as S
+from parity_util import RowsScorer, classify_tree, record
 
 pytestmark = pytest.mark.gpu
 
-EXCUSE = 1e-5
 LOGQ_TOL = 1e-4
 
 
@@ -45,55 +43,17 @@ def _run_gpu(x, W1, W2t, B, C, f32=False):
     return g
 
 
-def _paths(tok, par, n):
-    P = {0: ()}
-    for j in range(n):
-        P[j + 1] = P[int(par[j])] + (int(tok[j]),)
-    return [P[j + 1] for j in range(n)]
-
-
-def _classify(g, gb, o, i, diag, B):
-    """GPU request gb against oracle entry i: 'exact', 'E1', 'E2' or 'F:...'."""
-    ng, no = int(g["num_nodes"][gb]), int(o["num_nodes"][i])
-    if ng != no:
-        return f"F:count {ng} vs {no}"
-    gt, gp, gq, gd = g["tree_tokens"][gb], g["parents"][gb], g["logq"][gb], g["depths"][gb]
-    if not (np.all(gt[no:] == -1) and np.all(gp[no:] == -1) and np.all(gd[no:] == 0)
-            and np.isneginf(gq[no:]).all()):
-        return "F:padding"
-    same = (np.array_equal(gt, o["tree_tokens"][i]) and np.array_equal(gp, o["parents"][i])
-            and np.array_equal(gd, o["depths"][i]))
-    if same:
-        d = np.abs(gq[:no].astype(np.float64) - o["logq"][i][:no])
-        return "exact" if no == 0 or d.max() <= LOGQ_TOL else f"F:logq {d.max():.3g}"
-    pg = _paths(gt, gp, ng)
-    po = _paths(o["tree_tokens"][i], o["parents"][i], no)
-    so = {p: float(s) for p, s in zip(po, o["logq"][i][:no])}
-    lg = {p: float(v) for p, v in zip(pg, gq[:ng])}
-    for p in set(pg) & set(po):
-        if abs(lg[p] - so[p]) > LOGQ_TOL:
-            return f"F:logq {p}"
-    for j in range(ng):  # depths consistent with the paths
-        if int(gd[j]) != len(pg[j]):
-            return "F:depth"
-    if set(pg) != set(po):
-        gap = float(o["logq"][i][B - 1] - diag["next_score"]) if no == B else np.inf
-        return "E1" if gap < EXCUSE else f"F:set gap={gap:.3g} diff={len(set(pg) ^ set(po))}"
-    pos = {p: k for k, p in enumerate(pg)}
-    for a in range(no):
-        for c in range(a + 1, no):
-            pa, pc = po[a], po[c]
-            if pos[pa] > pos[pc] and abs(so[pa] - so[pc]) >= EXCUSE:
-                return f"F:order {pa} {pc}"
-    return "E2"
-
-
-def _compare(g, o, diags, rows, B):
+def _compare(g, o, diags, rows, B, label):
     counts = {}
     for i, gb in enumerate(rows):
-        c = _classify(g, gb, o, i, diags[i], B)
+        gi = {k: g[k][gb] for k in ("tree_tokens", "parents", "logq", "depths", "num_nodes")}
+        oi = {k: o[k][i] for k in ("tree_tokens", "parents", "depths", "num_nodes")}
+        oi["score64"] = o["logq"][i]
+        c = classify_tree(gi, oi, RowsScorer(diags[i]["rows"]), B, diags[i]["next_score"],
+                          depth_strict=False)
         assert not c.startswith("F"), f"request {gb}: {c}"
         counts[c] = counts.get(c, 0) + 1
+    record(label, counts)
     return counts
 
 
@@ -121,9 +81,8 @@ def test_sparkling_small(seed, batch, L, V, C, R, B, ws):
     diags = []
     o = S.build(x, W1, W2t, B, C, diags=diags)
     g = _run_gpu(x, W1, W2t, B, C)
-    st = _compare(g, o, diags, list(range(batch)), B)
+    st = _compare(g, o, diags, list(range(batch)), B, f"sparkling L={L} C={C} R={R} B={B}")
     print(f"sparkling seed={seed} batch={batch} L={L} V={V} C={C} R={R} B={B}: {st}")
-    assert st.get("exact", 0) >= batch - 1
     _check_mask(g, B)
 
 
@@ -163,23 +122,22 @@ def test_sparkling_budget_beyond_all_prefixes():
     o = S.build(x, W1, W2t, 50, 4, diags=diags)
     g = _run_gpu(x, W1, W2t, 50, 4)
     assert (g["num_nodes"] == 4 + 16).all()
-    _compare(g, o, diags, [0, 1], 50)
+    _compare(g, o, diags, [0, 1], 50, "sparkling budget beyond all prefixes")
     _check_mask(g, 50)
 
 
 def test_sparkling_post_shape_sampled():
     """The batch-64 workload (15 rows of V = 151936, C = 128, R = 256, B = 64)
-    in one launch; the oracle checks three requests, every request is checked
+    in one launch; the oracle checks eight requests, every request is checked
     for structure."""
     c = gen.SPARKLING
     x, W1, W2t = gen.sparkling_inputs(0)
     g = _run_gpu(x, W1, W2t, c["B"], c["C"])
-    rows = [0, 31, 63]
+    rows = list(range(0, 64, 8))
     diags = []
     o = S.build(x, W1, W2t, c["B"], c["C"], requests=rows, diags=diags)
-    st = _compare(g, o, diags, rows, c["B"])
+    st = _compare(g, o, diags, rows, c["B"], "sparkling batch-64 workload (8 of 64 requests)")
     print(f"sparkling batch-64 workload, requests {rows}: {st}")
-    assert st.get("exact", 0) >= 2
     assert (g["num_nodes"] == c["B"]).all()
     for b in range(c["batch"]):
         par, dep, lq = g["parents"][b], g["depths"][b], g["logq"][b]

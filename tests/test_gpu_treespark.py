@@ -1,7 +1,9 @@
 """GPU parity of treespark_expand against the float64 oracle (TreeSpark
-README, items 1-2). Trees must match exactly except where the oracle's
-top-k, frontier or packing boundary is closer than 1e-5 (z is accumulated in
-float32 on the device); logq within 1e-4."""
+README, items 1-2). A tree must equal the oracle's (order swaps of nodes
+< 1e-5 apart counted as E2) or one of the oracle's trees with one or two
+boundaries -- a parent's k-th/(k+1)-th child, a frontier cut, the packing
+cut -- closer than 1e-5 taken the other way (E1, z is accumulated in float32
+on the device); logq within 1e-4 of the matching tree."""
 
 import numpy as np
 import pytest
@@ -11,11 +13,9 @@ import draft_tree_construction_depth_amd as pkg
 from draft_tree_construction_depth_amd import gen
 from oracle import oracle as O
 from oracle import treespark as T
+from parity_util import classify_variants, record
 
 pytestmark = pytest.mark.gpu
-
-EXCUSE = 1e-5
-
 
 def _dev_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
@@ -28,24 +28,20 @@ def _run_gpu(bb, W, E, anc, k, F, N):
     return {key: v.cpu().numpy() for key, v in out.items()}
 
 
-def _classify(o, g, diags, rows):
-    """rows: GPU batch indices matching the oracle's entries in order."""
-    stats = dict(exact=0, excused=0)
+def _classify(o, g, diags, rows, label, bb, W, E, anc, k, F, N, W64=None):
+    """rows: GPU batch indices matching the oracle's entries in order. A tree
+    that differs from the oracle's must equal one of its near-tie variants."""
+    stats = {}
     for i, b in enumerate(rows):
-        n = int(o["num_nodes"][i])
-        same = (int(g["num_nodes"][b]) == n
-                and np.array_equal(g["tree_tokens"][b], o["tree_tokens"][i])
-                and np.array_equal(g["parents"][b], o["parents"][i])
-                and np.array_equal(g["depths"][b], o["depths"][i]))
-        if same:
-            np.testing.assert_allclose(g["logq"][b][:n], o["logq"][i][:n], rtol=0, atol=1e-4)
-            assert np.isneginf(g["logq"][b][n:]).all()
-            stats["exact"] += 1
-        else:
-            d = diags[i]
-            gaps = list(d["topk_gaps"]) + list(d["frontier_gaps"]) + [d["pack_gap"]]
-            assert min(gaps) < EXCUSE, f"request {b}: trees differ with every oracle gap >= {EXCUSE}"
-            stats["excused"] += 1
+        gi = {key: g[key][b] for key in ("tree_tokens", "parents", "logq", "depths", "num_nodes")}
+        ref = {key: o[key][i] for key in ("tree_tokens", "parents", "logq", "depths", "num_nodes")}
+        c = classify_variants(gi, [(None, ref)])
+        if c.startswith("F"):
+            c = classify_variants(gi, T.near_tie_variants(bb, W, E, int(anc[b]), b, diags[i], k=k,
+                                                          F=F, N=N, W64=W64))
+        assert not c.startswith("F"), f"request {b}: {c}"
+        stats[c] = stats.get(c, 0) + 1
+    record(label, {key.split(":")[0]: v for key, v in stats.items()})
     return stats
 
 
@@ -68,24 +64,26 @@ def test_treespark_small(seed, batch, D, V, H, k, F, N, ws):
     diags = []
     o = T.expand(bb, W, E, anc, k=k, F=F, N=N, diags=diags)
     g = _run_gpu(bb, W, E, anc, k, F, N)
-    st = _classify(o, g, diags, list(range(batch)))
+    st = _classify(o, g, diags, list(range(batch)), f"treespark D={D} V={V} H={H} k={k} F={F} N={N}",
+                   bb, W, E, anc, k, F, N)
     print(f"treespark seed={seed} batch={batch} D={D} V={V} H={H} k={k} F={F} N={N}: {st}")
-    assert st["exact"] >= batch - 1
 
 
 def test_treespark_readme_shape_sampled():
     """The README's shape: 32 requests, 7 depths, V = 151936, H = 2560, k = 4,
-    F = 4, N = 32; the oracle checks two requests of the full launch."""
+    F = 4, N = 32; the oracle checks eight requests of the full launch."""
     c = gen.TREESPARK
     bb, W, E, anc = gen.treespark_inputs(0)
     g = _run_gpu(bb, W, E, anc, c["k"], c["F"], c["N"])
-    rows = [0, 17]
+    rows = list(range(0, 32, 4))
     diags = []
-    o = T.expand(bb, W, E, anc, k=c["k"], F=c["F"], N=c["N"], requests=rows, diags=diags)
+    W64 = T.bf16_to_f64(W)
+    o = T.expand(bb, W, E, anc, k=c["k"], F=c["F"], N=c["N"], requests=rows, diags=diags, W64=W64)
     for dg in diags:
         assert dg["candidates"] == 100
     assert (g["num_nodes"] == 32).all()
-    st = _classify(o, g, diags, rows)
+    st = _classify(o, g, diags, rows, "treespark README shape (8 of 32 requests)", bb, W, E, anc,
+                   c["k"], c["F"], c["N"], W64=W64)
     print(f"treespark README shape, requests {rows}: {st}")
     # structure of every request of the launch
     for b in range(c["batch"]):
