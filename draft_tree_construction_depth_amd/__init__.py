@@ -16,10 +16,10 @@ include/ddtree.h); this package only binds it:
 """
 
 from ._lib import (DDT_BF16, DDT_F32, DDTreeError, ddtree_accept, ddtree_build, ddtree_compact_kv,
-                   ddtree_mask, ddtree_row_topk, ddtree_select, dspark_budget, even_widths,
-                   lib, sparkling_beam, sparkling_build, status_string, treespark_expand)
+                   ddtree_mask, ddtree_row_topk, ddtree_select, dspark_budget, lib,
+                   sparkling_beam, sparkling_build, status_string, treespark_expand)
 
 __all__ = ["DDT_BF16", "DDT_F32", "DDTreeError", "ddtree_accept", "ddtree_build",
            "ddtree_compact_kv", "ddtree_mask", "ddtree_row_topk", "ddtree_select", "dspark_budget",
-           "even_widths", "lib", "sparkling_beam", "sparkling_build", "status_string",
+           "lib", "sparkling_beam", "sparkling_build", "status_string",
            "treespark_expand"]

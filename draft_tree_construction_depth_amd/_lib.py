@@ -69,8 +69,8 @@ def lib() -> C.CDLL:
         L.dspark_budget.restype = C.c_int
         L.dspark_budget.argtypes = [p, i64, i32, p, i32, p, p, p, p, p, p]
         L.sparkling_beam.restype = C.c_int
-        L.sparkling_beam.argtypes = [p, C.c_int, p, p, i64, i32, i64, i32, i32, p, p, p, p, p, p,
-                                     p, p, sz, p]
+        L.sparkling_beam.argtypes = [p, C.c_int, p, p, i64, i32, i64, i32, i32, p, i32, p, p, p,
+                                     p, p, p, p, sz, p]
         _lib = L
     return _lib
 
@@ -124,15 +124,16 @@ _workspaces: dict = {}
 
 
 def workspace(kind: str, size: int, device, key) -> torch.Tensor:
-    """Zero-filled workspace cached per (kind, device, shape key).
+    """Scratch buffer cached per (kind, device, stream, shape key).
 
-    The library leaves a workspace zero-filled for the next call of the same
-    shape, so one buffer per shape is reused across calls on one stream.
+    The library ignores a workspace's contents on entry, so one buffer per
+    shape is reused across calls; calls on different streams may overlap and
+    so get buffers of their own.
     """
-    k = (kind, str(device), key)
+    k = (kind, str(device), torch.cuda.current_stream(device).cuda_stream, key)
     ws = _workspaces.get(k)
     if ws is None or ws.numel() < size:
-        ws = torch.zeros(max(size, 1), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(size, 1), dtype=torch.uint8, device=device)
         _workspaces[k] = ws
     return ws
 
@@ -356,16 +357,11 @@ def dspark_budget(conf: torch.Tensor, cost_ms: torch.Tensor, *, out: dict | None
     return out
 
 
-def even_widths(B: int, L: int) -> list:
-    """The budget B spread over L depths as evenly as possible (remainder first)."""
-    q, r = divmod(B, L)
-    return [q + (1 if d < r else 0) for d in range(L)]
-
-
 def sparkling_beam(logits: torch.Tensor, W1: torch.Tensor, W2t: torch.Tensor, widths=None, *,
                    B: int | None = None, C: int = 128, with_mask: bool = True,
                    out: dict | None = None, ws: torch.Tensor | None = None) -> dict:
-    """Beam tree on SparklingTree's rows: per-depth widths (default: B spread evenly)."""
+    """Beam tree on SparklingTree's rows: per-depth widths, or (widths None) the
+    budget B spread evenly by the library."""
     _arg(logits, "logits", _LOGITS)
     if logits.dim() != 3:
         raise ValueError("logits must be [batch, L, V]")
@@ -375,14 +371,17 @@ def sparkling_beam(logits: torch.Tensor, W1: torch.Tensor, W2t: torch.Tensor, wi
         raise ValueError(f"W1 must be [{V}, R]")
     R = W1.shape[1]
     _arg(W2t, "W2t", _BF16, (V, R))
+    import ctypes  # (the argument C shadows the module alias)
     if widths is None:
         if B is None:
             raise ValueError("give widths or a budget B")
-        widths = even_widths(B, L)
-    widths = [int(w) for w in widths]
-    if len(widths) != L:
-        raise ValueError(f"widths must have {L} entries")
-    Bt = sum(widths)
+        Bt, wa = int(B), None
+    else:
+        widths = [int(w) for w in widths]
+        if len(widths) != L:
+            raise ValueError(f"widths must have {L} entries")
+        Bt = sum(widths)
+        wa = ctypes.cast((ctypes.c_int32 * L)(*widths), ctypes.c_void_p)
     dev = logits.device
     dt = _dtype_code(logits)
     if out is None:
@@ -390,10 +389,8 @@ def sparkling_beam(logits: torch.Tensor, W1: torch.Tensor, W2t: torch.Tensor, wi
     size = lib().sparkling_build_workspace_size(batch, L, V, C, R, max(Bt, 1), dt)
     if ws is None:
         ws = workspace("sparkling", size, dev, (batch, L, V, C, R, max(Bt, 1), dt))
-    import ctypes  # (the argument C shadows the module alias)
-    wa = (ctypes.c_int32 * L)(*widths)
-    rc = lib().sparkling_beam(_ptr(logits), dt, _ptr(W1), _ptr(W2t), batch, L, V, C, R,
-                              ctypes.cast(wa, ctypes.c_void_p),
+    rc = lib().sparkling_beam(_ptr(logits), dt, _ptr(W1), _ptr(W2t), batch, L, V, C, R, wa,
+                              0 if widths is not None else Bt,
                               _ptr(out["tree_tokens"]), _ptr(out["parents"]), _ptr(out["logq"]),
                               _ptr(out.get("depths")), _ptr(out["num_nodes"]),
                               _ptr(out.get("mask")), _ptr(ws), ws.numel(), _stream(dev))

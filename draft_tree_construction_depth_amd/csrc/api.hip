@@ -574,6 +574,7 @@ int treespark_expand(const void* backbone, const void* W, const void* E, const i
 
   hipLaunchKernelGGL(ddt::ts_init_kernel, dim3((unsigned)((batch + 255) / 256)), dim3(256), 0,
                      stream, st, anchor, batch);
+  if (hipGetLastError() != hipSuccess) return DDT_EHIP;
   for (int d = 0; d < D; ++d) {
     const int Fd = sh.Fd[d];
     const int64_t M = batch * Fd;
@@ -599,6 +600,7 @@ int treespark_expand(const void* backbone, const void* W, const void* E, const i
       hipLaunchKernelGGL(ddt::ts_gemm_kernel<4>, ggrid, dim3(ddt::kTsThreads), 0, stream, gp);
     else
       hipLaunchKernelGGL(ddt::ts_gemm_kernel<8>, ggrid, dim3(ddt::kTsThreads), 0, stream, gp);
+    if (hipGetLastError() != hipSuccess) return DDT_EHIP;
     ddt::TsMergeParams mp;
     mp.st = st;
     mp.pmax = pmax;
@@ -619,6 +621,7 @@ int treespark_expand(const void* backbone, const void* W, const void* E, const i
     else
       hipLaunchKernelGGL(ddt::ts_merge_kernel<8>, dim3((unsigned)batch),
                          dim3(ddt::kTsMergeThreads), 0, stream, mp);
+    if (hipGetLastError() != hipSuccess) return DDT_EHIP;
   }
   ddt::TsPackParams pp;
   pp.st = st;
@@ -716,18 +719,23 @@ int dspark_budget(const float* conf, int64_t batch, int32_t P, const float* cost
 
 int sparkling_beam(const void* logits, int dtype, const uint16_t* W1, const uint16_t* W2t,
                    int64_t batch, int32_t L, int64_t V, int32_t C, int32_t R,
-                   const int32_t* widths, int32_t* tree_tokens, int32_t* parents, float* logq,
-                   int32_t* depths, int32_t* num_nodes, uint64_t* mask, void* workspace,
-                   size_t workspace_bytes, hipStream_t stream) {
-  if (!widths || L <= 0) return DDT_EINVAL;
+                   const int32_t* widths, int32_t budget, int32_t* tree_tokens,
+                   int32_t* parents, float* logq, int32_t* depths, int32_t* num_nodes,
+                   uint64_t* mask, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (L <= 0 || budget < 0) return DDT_EINVAL;
   if (L > DDT_MAX_L) return DDT_ENOTSUP;
+  // the schedule: the caller's widths, or the budget spread evenly over the
+  // depths with the remainder on the first ones ("evenly spread branches")
+  int32_t w[DDT_MAX_L];
+  if (!widths && budget > DDT_MAX_B) return DDT_ENOTSUP;
+  for (int d = 0; d < L; ++d) w[d] = widths ? widths[d] : budget / L + (d < budget % L ? 1 : 0);
   int32_t B = 0;
   for (int d = 0; d < L; ++d) {
-    if (widths[d] < 0) return DDT_EINVAL;
-    if (widths[d] > ddt::kBmMaxW) return DDT_ENOTSUP;
-    B += widths[d];
+    if (w[d] < 0) return DDT_EINVAL;
+    if (w[d] > ddt::kBmMaxW) return DDT_ENOTSUP;
+    B += w[d];
   }
-  if (B <= 0) return DDT_EINVAL;
+  if (B <= 0 || (widths && budget != 0 && budget != B)) return DDT_EINVAL;
   const int chk = sp_check(dtype, batch, L, V, C, R, B);
   if (chk != DDT_OK) return chk;
   if (batch == 0) return DDT_OK;
@@ -763,7 +771,7 @@ int sparkling_beam(const void* logits, int dtype, const uint16_t* W1, const uint
   sp.sp_lp = (const float*)(ws + lay.lp);
   sp.sp_best = (const uint8_t*)(ws + lay.best);
   sp.sp_blp = (const float*)(ws + lay.blp);
-  for (int d = 0; d < ddt::kMaxL; ++d) bp.widths[d] = d < L ? widths[d] : 0;
+  for (int d = 0; d < ddt::kMaxL; ++d) bp.widths[d] = d < L ? w[d] : 0;
   hipLaunchKernelGGL(ddt::beam_kernel, dim3((unsigned)batch), dim3(ddt::kBmThreads), 0, stream,
                      bp);
   return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;

@@ -88,11 +88,12 @@ const char* ddt_status_string(int status);
 
 /*
  * Workspace. ddtree_build and ddtree_row_topk need a device scratch buffer of
- * at least the size the matching *_workspace_size() returns. The buffer must
- * be zero-filled before its first use and again whenever it is reused with a
- * different shape (batch, L, V, B, dtype) or passed to the other call; every
- * call that completes leaves it ready for the next call of the same shape.
- * A workspace must not be used by two calls that can run concurrently.
+ * at least the size the matching *_workspace_size() returns. Its contents on
+ * entry are ignored: every record a launch reads was written earlier in the
+ * same call, so an abandoned or failed call leaves nothing behind that a
+ * later call depends on. A workspace must not be used by two calls that can
+ * run concurrently (two streams, or two host threads on one stream without
+ * ordering): they would overwrite each other's records.
  */
 size_t ddtree_build_workspace_size(int64_t batch, int32_t L, int64_t V, int32_t B, int dtype);
 size_t ddtree_row_topk_workspace_size(int64_t rows, int64_t V, int32_t K, int dtype);
@@ -319,7 +320,10 @@ int dspark_budget(const float* conf, int64_t batch, int32_t P, const float* cost
  * rows (SparklingTree post, "Future Ideas", item 4: a beam with a fixed
  * branching budget in place of the best-first heap; evenly spread branches).
  * Rows as sparkling_build (top C candidates per row, the rank-R Markov head,
- * log-probs over the C candidates). widths [L] is a HOST array: depth 1 keeps
+ * log-probs over the C candidates). widths [L] is a HOST array, or NULL for
+ * the evenly spread schedule of `budget` nodes: floor(budget / L) per depth,
+ * one more on the first budget mod L depths. With widths given, budget must
+ * be 0 or their sum (DDT_EINVAL otherwise). Depth 1 keeps
  * the widths[0] best children of the root; depth d+1 the widths[d] best of all
  * children of depth d's beam; best = score (sum of lp along the path,
  * float64) desc, then rank tuple lexicographic asc (a child's rank = its
@@ -336,7 +340,8 @@ int dspark_budget(const float* conf, int64_t batch, int32_t P, const float* cost
  */
 int sparkling_beam(const void* logits, int dtype, const uint16_t* W1, const uint16_t* W2t,
                    int64_t batch, int32_t L, int64_t V, int32_t C, int32_t R,
-                   const int32_t* widths, int32_t* tree_tokens, int32_t* parents, float* logq,
+                   const int32_t* widths, int32_t budget, int32_t* tree_tokens,
+                   int32_t* parents, float* logq,
                    int32_t* depths, int32_t* num_nodes, uint64_t* mask, void* workspace,
                    size_t workspace_bytes, hipStream_t stream);
 

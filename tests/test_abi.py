@@ -204,13 +204,14 @@ def test_dspark_validation(L):
 def test_sparkling_beam_validation(L):
     f = L.sparkling_beam
 
-    def call(widths=(4,) * 15, Lr=15, Cc=128, R=256, batch=2, out=FAKE, wsp=FAKE, ws_bytes=1 << 34):
+    def call(widths=(4,) * 15, budget=0, Lr=15, Cc=128, R=256, batch=2, out=FAKE, wsp=FAKE,
+             ws_bytes=1 << 34):
         wa = None if widths is None else (C_int32 * len(widths))(*widths)
         return f(FAKE, 0, FAKE, FAKE, batch, Lr, 1024, Cc, R,
-                 None if wa is None else C.cast(wa, C.c_void_p), out, out, out, out, out, out,
-                 wsp, ws_bytes, None)
+                 None if wa is None else C.cast(wa, C.c_void_p), budget, out, out, out, out, out,
+                 out, wsp, ws_bytes, None)
     C_int32 = C.c_int32
-    assert call(widths=None) == -1
+    assert call(widths=None) == -1                # no widths and no budget
     assert call(widths=(0,) * 15) == -1          # empty budget
     assert call(widths=(-1,) + (4,) * 14) == -1
     assert call(widths=(65,) + (4,) * 14) == -2  # a width above 64
@@ -219,3 +220,23 @@ def test_sparkling_beam_validation(L):
     assert call(out=None) == -1
     assert call(ws_bytes=64) == -3
     assert call(batch=0) == 0
+    # widths given with a budget: the budget must be their sum
+    assert call(budget=61) == -1
+    assert call(budget=60, batch=0) == 0
+    assert call(budget=-1) == -1
+
+
+def test_sparkling_beam_even_schedule_on_the_host(L):
+    """widths == NULL: the library spreads the budget over the depths (the
+    remainder on the first ones), validated on the host before any launch."""
+    f = L.sparkling_beam
+
+    def call(budget, Lr=15, ws_bytes=1 << 34, batch=2):
+        return f(FAKE, 0, FAKE, FAKE, batch, Lr, 1024, 128, 256, None, budget, FAKE, FAKE, FAKE,
+                 FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+    assert call(0) == -1                 # nothing to spread
+    assert call(64, batch=0) == 0        # 5 on four depths, 4 on eleven: valid
+    assert call(64, ws_bytes=64) == -3   # checked against the workspace of B = 64
+    assert call(15 * 65) == -2           # above DDT_MAX_B
+    assert call(3 * 65, Lr=3) == -2      # 65 per depth: above the 64 a depth holds
+    assert call(512, Lr=8, batch=0) == 0  # exactly 64 per depth

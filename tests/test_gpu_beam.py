@@ -3,12 +3,13 @@ post, "Future Ideas", item 4).
 
 Device log-probs are float32 (as sparkling_build), the oracle's float64, so
 trees must match exactly except in two counted classes:
-  E1  some depth's cut (the w-th and (w+1)-th candidates of the oracle)
-      is closer than 1e-5: the beams may differ from that depth on;
-  E2  every depth holds the same prefixes and only prefixes whose oracle
-      scores are < 1e-5 apart appear in a different order.
-logq of common prefixes within 1e-4; flat rows with a zero head (exact
-ties everywhere, including the tie-extraction path) bit-exact."""
+  E1  the device tree is the oracle's tree with one or two depth cuts whose
+      w-th and (w+1)-th candidates are closer than 1e-5 taken the other way
+      (oracle/beam.py near_tie_variants), expanded on from there;
+  E2  the same prefixes, and only prefixes whose oracle scores are < 1e-5
+      apart appear in a different order.
+logq within 1e-4 of the matching oracle tree; flat rows with a zero head
+(exact ties everywhere, including the tie-extraction path) bit-exact."""
 
 import numpy as np
 import pytest
@@ -18,10 +19,10 @@ import draft_tree_construction_depth_amd as pkg
 from draft_tree_construction_depth_amd import gen
 from oracle import beam as BM
 from oracle import oracle as O
+from parity_util import classify_variants, record
 
 pytestmark = pytest.mark.gpu
 
-EXCUSE = 1e-5
 LOGQ_TOL = 1e-4
 
 
@@ -37,49 +38,18 @@ def _run(x, W1, W2t, widths, C):
     return g
 
 
-def _paths(tok, par, n):
-    P = {0: ()}
-    for j in range(n):
-        P[j + 1] = P[int(par[j])] + (int(tok[j]),)
-    return [P[j + 1] for j in range(n)]
-
-
-def _classify(g, gb, o, i, diag, B):
-    ng, no = int(g["num_nodes"][gb]), int(o["num_nodes"][i])
-    gt, gp, gq, gd = g["tree_tokens"][gb], g["parents"][gb], g["logq"][gb], g["depths"][gb]
-    if ng == no and not (np.all(gt[no:] == -1) and np.all(gp[no:] == -1)
-                         and np.isneginf(gq[no:]).all() and np.all(gd[no:] == 0)):
-        return "F:padding"
-    if (ng == no and np.array_equal(gt, o["tree_tokens"][i]) and np.array_equal(gp, o["parents"][i])
-            and np.array_equal(gd, o["depths"][i])):
-        d = np.abs(gq[:no].astype(np.float64) - o["logq"][i][:no])
-        return "exact" if no == 0 or d.max() <= LOGQ_TOL else f"F:logq {d.max():.3g}"
-    if diag["cut_gaps"] and min(diag["cut_gaps"]) < EXCUSE:
-        return "E1"
-    if ng != no:
-        return f"F:count {ng} vs {no}"
-    pg = _paths(gt, gp, ng)
-    po = _paths(o["tree_tokens"][i], o["parents"][i], no)
-    if set(pg) != set(po) or not np.array_equal(gd, o["depths"][i]):
-        return "F:set"
-    so = {p: float(s) for p, s in zip(po, o["logq"][i][:no])}
-    for p, v in zip(pg, gq[:ng]):
-        if abs(float(v) - so[p]) > LOGQ_TOL:
-            return f"F:logq {p}"
-    pos = {p: k for k, p in enumerate(pg)}
-    for a in range(no):
-        for c in range(a + 1, no):
-            if pos[po[a]] > pos[po[c]] and abs(so[po[a]] - so[po[c]]) >= EXCUSE:
-                return f"F:order {po[a]} {po[c]}"
-    return "E2"
-
-
-def _compare(g, o, diags, rows, B):
+def _compare(g, o, diags, rows, B, label, x, W1, W2t, widths, C):
     counts = {}
     for i, gb in enumerate(rows):
-        c = _classify(g, gb, o, i, diags[i], B)
+        gi = {k: g[k][gb] for k in ("tree_tokens", "parents", "logq", "depths", "num_nodes")}
+        ref = {k: o[k][i] for k in ("tree_tokens", "parents", "logq", "depths", "num_nodes")}
+        c = classify_variants(gi, [(None, ref)])
+        if c.startswith("F"):
+            c = classify_variants(gi, BM.near_tie_variants(x, W1, W2t, widths, C, diags[i]))
         assert not c.startswith("F"), f"request {gb}: {c}"
-        counts[c] = counts.get(c, 0) + 1
+        key = c.split(":")[0]
+        counts[key] = counts.get(key, 0) + 1
+    record(label, counts)
     return counts
 
 
@@ -89,7 +59,7 @@ CASES = [
     (1, 3, 8, 3000, 64, 128, [8, 8, 8, 8, 8, 8, 8, 8], 0.2),
     (2, 3, 6, 3001, 40, 64, [1, 2, 4, 8, 16, 32], 0.3),    # back-loaded, unaligned rows
     (3, 2, 6, 2000, 16, 64, [32, 16, 8, 4, 2, 1], 0.3),    # front-loaded; depth 1 keeps all 16
-    (4, 2, 15, 5000, 128, 256, pkg.even_widths(64, 15), 0.177),
+    (4, 2, 15, 5000, 128, 256, BM.even_widths(64, 15), 0.177),
     (5, 2, 4, 500, 50, 64, [64, 64, 64, 64], 0.3),         # widest beams
     (6, 2, 5, 800, 8, 64, [3, 0, 5, 5, 5], 0.3),           # a zero width ends the tree
     (7, 70, 3, 700, 8, 64, [2, 3, 4], 0.5),                # many requests
@@ -104,9 +74,9 @@ def test_beam_small(seed, batch, L, V, C, R, widths, ws):
     o = BM.build(x, W1, W2t, widths, C, diags=diags)
     g = _run(x, W1, W2t, widths, C)
     B = sum(widths)
-    st = _compare(g, o, diags, list(range(batch)), B)
+    st = _compare(g, o, diags, list(range(batch)), B, f"beam L={L} C={C} widths={widths}",
+                  x, W1, W2t, widths, C)
     print(f"beam seed={seed} batch={batch} L={L} C={C} widths={widths}: {st}")
-    assert st.get("exact", 0) >= batch - 1
     np.testing.assert_array_equal(g["mask"], O.mask(g["parents"], g["num_nodes"], B))
 
 
@@ -128,18 +98,33 @@ def test_beam_flat_rows_exact(C, widths):
 
 def test_beam_post_shape_sampled():
     """The batch-64 workload (15 rows of V = 151936, C = 128, R = 256) with
-    B = 64 spread evenly, in one launch; three requests against the oracle."""
+    B = 64 spread evenly, in one launch; eight requests against the oracle."""
     c = gen.SPARKLING
     x, W1, W2t = gen.sparkling_inputs(0)
-    widths = pkg.even_widths(c["B"], c["L"])
+    widths = BM.even_widths(c["B"], c["L"])
     g = _run(x, W1, W2t, widths, c["C"])
-    rows = [0, 31, 63]
+    rows = list(range(0, 64, 8))
     diags = []
     o = BM.build(x, W1, W2t, widths, c["C"], requests=rows, diags=diags)
-    st = _compare(g, o, diags, rows, c["B"])
+    xs = x[rows]
+    st = _compare(g, o, diags, rows, c["B"], "beam batch-64 workload (8 of 64 requests)",
+                  xs, W1, W2t, widths, c["C"])
     print(f"beam batch-64 workload, requests {rows}: {st}")
-    assert st.get("exact", 0) >= 2
     assert (g["num_nodes"] == c["B"]).all()
     for b in range(c["batch"]):
         dep = g["depths"][b]
         assert [int((dep == d + 1).sum()) for d in range(c["L"])] == widths
+
+
+def test_beam_default_schedule_is_the_even_split():
+    """widths None: the library spreads the budget itself; the same trees as
+    the explicit even schedule."""
+    x, W1, W2t = gen.sparkling_inputs(12, batch=3, L=7, V=3000, R=64, wscale=0.3)
+    a = pkg.sparkling_beam(_dev_bf16(x), _dev_bf16(W1), _dev_bf16(W2t), B=30, C=32)
+    b = pkg.sparkling_beam(_dev_bf16(x), _dev_bf16(W1), _dev_bf16(W2t), BM.even_widths(30, 7),
+                           C=32)
+    torch.cuda.synchronize()
+    for k in a:
+        np.testing.assert_array_equal(a[k].cpu().numpy(), b[k].cpu().numpy(), err_msg=k)
+    dep = a["depths"].cpu().numpy()
+    assert [int((dep[0] == d + 1).sum()) for d in range(7)] == BM.even_widths(30, 7)
