@@ -25,7 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "draft trees/sec at batch 64, V=151936, L=15, B=128; achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0
-SAMPLE_EVERY = 8  # timed steps per stage-1 event sample
+KERNEL_SAMPLES = 100  # event-timed launches of stage 1 and of the read probe
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_stage1_batch64.json")
 STAGE1_SOURCES = ["draft_tree_construction_depth_amd/csrc/stage1.hpp",
                   "draft_tree_construction_depth_amd/csrc/common.hpp"]
@@ -52,27 +52,86 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(x, Y, B, L):
-    """The oracle as it stands, timed on this host over the same batch."""
-    import numpy as np
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+def cpu_baseline(x, Y, B, L, sample_1core: int = 8):
+    """The oracle as it stands, timed on this host: the whole batch at the
+    host's CPU share (threads over requests), and a sample of requests on one
+    core. Returns (report, oracle trees of the whole batch with tables)."""
     from draft_tree_construction_depth_amd import gen
     from oracle import oracle as O
     if not os.path.exists(O.LIB):
         O.build_oracle()
-    threads = max(1, min(len(os.sched_getaffinity(0)), 16))
-    t0 = time.perf_counter()
-    o = O.build(x, gen.DTYPE_BF16, B, threads=threads, tables=False)
-    O.mask(o["parents"], o["num_nodes"], B)
-    t1 = time.perf_counter()
-    tgt = gen.node_targets_from_depths(Y, o["depths"], o["num_nodes"], B)
-    t2 = time.perf_counter()
-    O.accept(o["tree_tokens"], o["parents"], o["num_nodes"], tgt, L)
-    t3 = time.perf_counter()
-    secs = (t1 - t0) + (t3 - t2)
+    visible = len(os.sched_getaffinity(0))
+    # the host's CPU share for one GPU is 16 threads, whatever more it shows
+    threads = max(1, min(visible, 16))
+
+    def run(xs, T):
+        t0 = time.perf_counter()
+        o = O.build(xs, gen.DTYPE_BF16, B, threads=T, tables=True)
+        O.mask(o["parents"], o["num_nodes"], B)
+        t1 = time.perf_counter()
+        tgt = gen.node_targets_from_depths(Y[:xs.shape[0]], o["depths"], o["num_nodes"], B)
+        t2 = time.perf_counter()
+        O.accept(o["tree_tokens"], o["parents"], o["num_nodes"], tgt, L)
+        t3 = time.perf_counter()
+        return (t1 - t0) + (t3 - t2), o
+
+    secs, o = run(x, threads)
+    n1 = min(sample_1core, x.shape[0])
+    secs1, _ = run(x[:n1], 1)
     n = x.shape[0]
-    return {"value": n / secs, "unit": "trees/s", "cores": threads, "kind": "oracle",
-            "sample": f"all {n} requests of one batch (build + mask + accept), {secs:.2f} s"}, o
+    rep = {"value": n / secs, "unit": "trees/s", "cores": threads, "kind": "oracle",
+           "sample": f"all {n} requests of one batch (build + mask + accept), {secs:.2f} s",
+           "value_1core": n1 / secs1,
+           "sample_1core": f"the first {n1} requests on one thread, {secs1:.2f} s",
+           "host_cpus_visible": visible, "cpu_model": cpu_model()}
+    return rep, o
+
+
+def parity_of_run(g: dict, o: dict, tgt, B: int, L: int) -> dict:
+    """The benchmark's own trees against the oracle's: tree classes (oracle/
+    parity.py), masks (of the device's parents) and walks (on the device's
+    trees, same targets) bit for bit."""
+    import numpy as np
+
+    from oracle import oracle as O
+    from oracle.parity import ddtree_batch_counts
+    res = ddtree_batch_counts(g, o, B)
+    counts = {k: res["counts"].get(k, 0) for k in ("exact", "E1", "E2", "F")}
+    m_ok = np.array_equal(g["mask"], O.mask(g["parents"], g["num_nodes"], B))
+    oa = O.accept(g["tree_tokens"], g["parents"], g["num_nodes"], tgt, L)
+    w_ok = all(np.array_equal(a, b) for a, b in zip(
+        (g["accepted_nodes"], g["accept_len"], g["next_token"]), oa))
+    return {**counts, "masks_bit_exact": bool(m_ok), "walks_bit_exact": bool(w_ok),
+            "requests": int(len(o["num_nodes"]))}
+
+
+def read_ceiling(pkg, torch, bufs, rows, row_bytes, n):
+    """Event-timed launches of the read probe over the same rotated buffers:
+    GB/s of stage 1's load path with nothing computed."""
+    sink = torch.empty((rows, 4), dtype=torch.int32, device=bufs[0].device)
+    for i in range(3):
+        pkg.ddtree_read_probe(bufs[i % len(bufs)], rows, row_bytes, sink)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        pkg.ddtree_read_probe(bufs[i % len(bufs)], rows, row_bytes, sink)
+        b.record()
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in evs) / n * 1e3
+    return rows * row_bytes / (us * 1e-6) / 1e9, us
 
 
 def treespark_bench(args) -> int:
@@ -429,6 +488,29 @@ def kv_bench(args) -> int:
     return 0
 
 
+def read_probe_bench(args) -> int:
+    """Stage 1's load path alone over the batch-64 workload's rotated buffers
+    (960 rows of 303,872 bytes): the read ceiling stage 1 is measured against."""
+    import numpy as np
+    import torch
+
+    import draft_tree_construction_depth_amd as pkg
+    from draft_tree_construction_depth_amd import gen
+
+    c = gen.CONFIGS[3]
+    rows, V = c["batch"] * c["L"], c["V"]
+    dev = torch.device("cuda:0")
+    x = gen.make_logits(3, 0)
+    x_dev = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    bufs = [x_dev] + [x_dev.clone() for _ in range(args.buffers - 1)]
+    gbps, us = read_ceiling(pkg, torch, bufs, rows, V * 2, max(args.steps, 1))
+    print(json.dumps({"probe": "read ceiling (ddtree_read_probe)", "rows": rows,
+                      "row_bytes": V * 2, "launches_timed": max(args.steps, 1),
+                      "avg_launch_us": round(us, 2), "gbps": round(gbps, 1),
+                      "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4)}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -449,6 +531,8 @@ def main() -> int:
     ap.add_argument("--workload", choices=("c3", "c2", "c5"), default="c3",
                     help="c3: batch 64, B 128 (default, the headline); c2: batch 1, B 64 latency "
                          "of build + mask + accept; c5: batch 256, B 256 (own JSON lines)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="only time the read probe over the batch-64 buffers (own JSON line)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 3 device-to-device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -488,6 +572,8 @@ def main() -> int:
         return beam_bench(args)
     if args.workload == "c2":
         return latency_bench(args)
+    if args.read_probe:
+        return read_probe_bench(args)
     cfg = 5 if args.workload == "c5" else 3
 
     c = gen.CONFIGS[cfg]
@@ -512,7 +598,8 @@ def main() -> int:
     ws = torch.zeros(ws_size, dtype=torch.uint8, device=dev)
 
     # One untimed round gives the tree shape; the per-node target tokens (the
-    # target model's argmax at each node, a stand-in) follow from it.
+    # target model's argmax at each node, a stand-in) follow from it. Its
+    # trees, masks and walks are checked against the oracle after timing.
     pkg.ddtree_row_topk(bufs[0], K, out=tables, ws=ws)
     tree = pkg.ddtree_select(tv, ti, tz, B)
     torch.cuda.synchronize()
@@ -520,37 +607,44 @@ def main() -> int:
                                        tree["num_nodes"].cpu().numpy(), B)
     tgt_dev = torch.from_numpy(tgt).to(dev)
     acc = pkg.ddtree_accept(tree["tree_tokens"], tree["parents"], tree["num_nodes"], tgt_dev, L)
+    torch.cuda.synchronize()
+    first = {k: v.cpu().numpy() for k, v in {**tree, **acc}.items()}
+    first["mask"] = first["mask"].view(np.uint64)
 
-    def step(i, ev=None):
-        if ev is not None:
-            ev[0].record()
+    def step(i):
         pkg.ddtree_row_topk(bufs[i % len(bufs)], K, out=tables, ws=ws)
-        if ev is not None:
-            ev[1].record()
         pkg.ddtree_select(tv, ti, tz, B, out=tree)
         pkg.ddtree_accept(tree["tree_tokens"], tree["parents"], tree["num_nodes"], tgt_dev, L,
                           out=acc)
 
     for i in range(args.warmup):
         step(i)
-    # Stage-1 launch durations: events around stage 1 on every SAMPLE_EVERY-th
-    # timed step (an event pair costs the stream about 6 us per step).
-    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for i in range(0, args.steps, SAMPLE_EVERY)}
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        step(args.warmup + i, evs.get(i))
+        step(args.warmup + i)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
-    s1_ms = [a.elapsed_time(b) for a, b in evs.values()]
-    s1_avg_ms = float(np.mean(s1_ms))
     trees_per_s = batch * args.steps / (total_ms / 1e3)
+
+    # Stage 1 alone, after the timed loop: KERNEL_SAMPLES launches over the
+    # rotated buffers, each between its own pair of events on the launch
+    # stream (the library launches on torch's current stream).
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(KERNEL_SAMPLES)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        pkg.ddtree_row_topk(bufs[i % len(bufs)], K, out=tables, ws=ws)
+        b.record()
+    torch.cuda.synchronize()
+    s1_us = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+    s1_avg_us = float(s1_us.mean())
+    ceiling_gbps, probe_us = read_ceiling(pkg, torch, bufs, rows, V * 2, KERNEL_SAMPLES)
 
     logits_bytes = batch * L * V * 2
     # Algorithmic bytes of the whole step (logits once, tree outputs, mask,
@@ -558,7 +652,7 @@ def main() -> int:
     W = (B + 1 + 63) // 64
     step_bytes = logits_bytes + batch * (B * 12 + B * 4 + 4 + (B + 1) * W * 8
                                          + (B + 1) * 4 + (L + 2) * 4)
-    achieved = logits_bytes / (s1_avg_ms / 1e3) / 1e9
+    achieved = logits_bytes / (s1_avg_us * 1e-6) / 1e9
     traffic = measured_traffic() if cfg == 3 else None
 
     result = {
@@ -582,14 +676,19 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": "stage1 (ddtree_row_topk)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "avg_launch_us": round(s1_avg_ms * 1e3, 2),
-                     "launches_sampled": len(s1_ms),
+                     "avg_launch_us": round(s1_avg_us, 2),
+                     "median_launch_us": round(float(np.median(s1_us)), 2),
+                     "launches_timed": len(s1_us),
+                     "read_ceiling_gbps": round(ceiling_gbps, 1),
+                     "read_ceiling_launch_us": round(probe_us, 2),
+                     "frac_of_read_ceiling": round(achieved / ceiling_gbps, 4),
                      "traffic": traffic},
     }
-    if not args.no_cpu_baseline and cfg == 3:
-        cb, _ = cpu_baseline(x, Y, B, L)
+    if not args.no_cpu_baseline:
+        cb, o = cpu_baseline(x, Y, B, L)
         result["cpu_baseline"] = {k: (round(v, 2) if isinstance(v, float) else v)
                                   for k, v in cb.items()}
+        result["parity"] = parity_of_run(first, o, tgt, B, L)
     print(json.dumps(result), flush=True)
     return 0
 

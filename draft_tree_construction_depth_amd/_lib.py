@@ -54,6 +54,8 @@ def lib() -> C.CDLL:
         L.ddtree_accept.argtypes = [p, p, p, p, i64, i32, i32, p, p, p, p]
         L.ddtree_compact_kv.restype = C.c_int
         L.ddtree_compact_kv.argtypes = [p, p, i64, i64, i32, i64, i32, p, p, p, i32, p, p]
+        L.ddtree_read_probe.restype = C.c_int
+        L.ddtree_read_probe.argtypes = [p, i64, i64, p, p]
         L.ddtree_row_topk.restype = C.c_int
         L.ddtree_row_topk.argtypes = [p, C.c_int, i64, i64, i32, p, p, p, p, sz, p]
         L.treespark_workspace_size.restype = sz
@@ -271,6 +273,21 @@ def ddtree_row_topk(logits: torch.Tensor, K: int, *, out: dict | None = None,
 
 
 _BF16 = (torch.bfloat16,)
+
+
+def ddtree_read_probe(src: torch.Tensor, rows: int, row_bytes: int,
+                      sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Measurement probe: stream rows x row_bytes bytes of src (stage 1's
+    launch geometry, no compute); returns the XOR sink [rows, 4] (uint32 as int32)."""
+    if not isinstance(src, torch.Tensor) or not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    if rows * row_bytes > src.numel() * src.element_size():
+        raise ValueError("rows x row_bytes exceeds src")
+    if sink is None:
+        sink = torch.empty((rows, 4), dtype=torch.int32, device=src.device)
+    _check("ddtree_read_probe", lib().ddtree_read_probe(_ptr(src), rows, row_bytes, _ptr(sink),
+                                                        _stream(src.device)))
+    return sink
 
 
 def treespark_expand(backbone: torch.Tensor, W: torch.Tensor, E: torch.Tensor,

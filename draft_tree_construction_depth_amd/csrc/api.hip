@@ -12,6 +12,7 @@
 #include "sparkling.hpp"
 #include "dspark.hpp"
 #include "beam.hpp"
+#include "probe.hpp"
 
 namespace {
 
@@ -497,6 +498,21 @@ int ddtree_accept(const int32_t* tree_tokens, const int32_t* parents, const int3
   wp.accept_len = accept_len;
   wp.next_token = next_token;
   hipLaunchKernelGGL(ddt::walk_kernel, dim3((unsigned)batch), dim3(ddt::kWave), 0, stream, wp);
+  return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
+}
+
+int ddtree_read_probe(const void* src, int64_t rows, int64_t row_bytes, uint32_t* sink,
+                      hipStream_t stream) {
+  if (rows < 0 || row_bytes <= 0) return DDT_EINVAL;
+  if (rows == 0) return DDT_OK;
+  if (!src || !sink || (uintptr_t)src % 16 != 0 || row_bytes % 16 != 0) return DDT_EINVAL;
+  if (rows > 0x7FFFFFFFLL || row_bytes > 0x7FFFFFFFLL) return DDT_ENOTSUP;
+  ddt::ProbeParams pp;
+  pp.src = (const char*)src;
+  pp.row_bytes = row_bytes;
+  pp.sink = sink;
+  hipLaunchKernelGGL(ddt::read_probe_kernel<8>, dim3((unsigned)rows), dim3(ddt::kS1Threads), 0,
+                     stream, pp);
   return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
 }
 

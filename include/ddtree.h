@@ -338,6 +338,21 @@ int dspark_budget(const float* conf, int64_t batch, int32_t P, const float* cost
  * on C, R, L and V (DDT_ENOTSUP); a negative width or B = 0: DDT_EINVAL.
  * Workspace: sparkling_build_workspace_size(batch, L, V, C, R, B, dtype) bytes.
  */
+/*
+ * ddtree_read_probe -- measurement probe: the practical read ceiling of stage
+ * 1 (SparklingTree post, "Step 1": every drafter row is read once). Streams
+ * rows x row_bytes bytes from src (device, 16-byte aligned, row_bytes a
+ * multiple of 16) with stage 1's launch geometry and load path (one
+ * 256-thread workgroup per row, nontemporal 16-byte buffer loads, double
+ * buffered) and computes nothing but an XOR of the words, written to
+ * sink[rows][4] (device uint32, one word per wave) so the loads stay live.
+ * Its rate is what the stage-1 kernel's bandwidth is reported against.
+ * DDT_EINVAL for null or misaligned pointers and bad sizes; DDT_ENOTSUP for
+ * rows or row_bytes above 2^31 - 1.
+ */
+int ddtree_read_probe(const void* src, int64_t rows, int64_t row_bytes, uint32_t* sink,
+                      hipStream_t stream);
+
 int sparkling_beam(const void* logits, int dtype, const uint16_t* W1, const uint16_t* W2t,
                    int64_t batch, int32_t L, int64_t V, int32_t C, int32_t R,
                    const int32_t* widths, int32_t budget, int32_t* tree_tokens,

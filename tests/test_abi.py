@@ -240,3 +240,4 @@ def test_sparkling_beam_even_schedule_on_the_host(L):
     assert call(15 * 65) == -2           # above DDT_MAX_B
     assert call(3 * 65, Lr=3) == -2      # 65 per depth: above the 64 a depth holds
     assert call(512, Lr=8, batch=0) == 0  # exactly 64 per depth
+
