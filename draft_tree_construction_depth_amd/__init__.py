@@ -4,6 +4,7 @@ The compute lives in libddtree.so (hand-written HIP for gfx950, C ABI in
 include/ddtree.h); this package only binds it:
 
     ddtree_build     logits [batch, L, V] -> top-B prefix tree (+ ancestor mask)
+    ddtree_build_noalloc  the same on the library's static scratch (no workspace)
     ddtree_select    stage 2 alone, from stage-1 tables (+ mask)
     ddtree_mask      parents -> bit-packed ancestor-only attention mask
     ddtree_accept    tree + target tokens -> accepted path, new bonus token
@@ -17,12 +18,13 @@ include/ddtree.h); this package only binds it:
 """
 
 from ._lib import (DDT_BF16, DDT_F32, DDTreeError, ddtree_accept, ddtree_build,
-                   ddtree_compact_kv,
+                   ddtree_build_noalloc, ddtree_compact_kv,
                    ddtree_mask, ddtree_read_probe, ddtree_row_topk, ddtree_select,
                    dspark_budget, lib,
                    sparkling_beam, sparkling_build, status_string, treespark_expand)
 
 __all__ = ["DDT_BF16", "DDT_F32", "DDTreeError", "ddtree_accept", "ddtree_build",
+           "ddtree_build_noalloc",
            "ddtree_compact_kv", "ddtree_mask", "ddtree_read_probe", "ddtree_row_topk",
            "ddtree_select", "dspark_budget",
            "lib", "sparkling_beam", "sparkling_build", "status_string",

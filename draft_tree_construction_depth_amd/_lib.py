@@ -46,6 +46,8 @@ def lib() -> C.CDLL:
         L.ddtree_row_topk_workspace_size.argtypes = [i64, i64, i32, C.c_int]
         L.ddtree_build.restype = C.c_int
         L.ddtree_build.argtypes = [p, C.c_int, i64, i32, i64, i32, p, p, p, p, p, p, p, sz, p]
+        L.ddtree_build_noalloc.restype = C.c_int
+        L.ddtree_build_noalloc.argtypes = [p, C.c_int, i64, i32, i64, i32, p, p, p, p, p, p, p]
         L.ddtree_select.restype = C.c_int
         L.ddtree_select.argtypes = [p, p, p, i64, i32, i32, i32, p, p, p, p, p, p, p]
         L.ddtree_mask.restype = C.c_int
@@ -159,6 +161,26 @@ def ddtree_build(logits: torch.Tensor, B: int, *, with_mask: bool = True, out: d
                             _ptr(out["num_nodes"]), _ptr(out.get("mask")), _ptr(ws),
                             ws.numel(), _stream(dev))
     _check("ddtree_build", rc)
+    return out
+
+
+def ddtree_build_noalloc(logits: torch.Tensor, B: int, *, with_mask: bool = True,
+                         out: dict | None = None) -> dict:
+    """ddtree_build on the library's static scratch (no workspace; the call
+    allocates nothing on the device when out is given)."""
+    _arg(logits, "logits", _LOGITS)
+    if logits.dim() != 3:
+        raise ValueError("logits must be [batch, L, V]")
+    batch, L, V = logits.shape
+    dev = logits.device
+    dt = _dtype_code(logits)
+    if out is None:
+        out = _tree_out(batch, B, dev, with_mask)
+    rc = lib().ddtree_build_noalloc(_ptr(logits), dt, batch, L, V, B, _ptr(out["tree_tokens"]),
+                                    _ptr(out["parents"]), _ptr(out["logq"]),
+                                    _ptr(out.get("depths")), _ptr(out["num_nodes"]),
+                                    _ptr(out.get("mask")), _stream(dev))
+    _check("ddtree_build_noalloc", rc)
     return out
 
 

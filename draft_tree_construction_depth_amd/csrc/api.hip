@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "select.hpp"
 #include "stage1.hpp"
 #include "treespark.hpp"
@@ -368,6 +370,68 @@ int sp_check(int dtype, int64_t batch, int32_t L, int64_t V, int32_t C, int32_t 
   return DDT_OK;
 }
 
+// ---- ddtree_build: shared checks and launches -------------------------------
+int build_check(const void* logits, int dtype, int64_t batch, int32_t L, int64_t V, int32_t B,
+                const int32_t* tree_tokens, const int32_t* parents, const float* logq,
+                const int32_t* num_nodes, BuildLayout& lay) {
+  if (!valid_dtype(dtype) || batch < 0 || L <= 0 || V <= 0 || B <= 0) return DDT_EINVAL;
+  if (batch == 0) return DDT_OK;
+  if (!logits || !tree_tokens || !parents || !logq || !num_nodes) return DDT_EINVAL;
+  if ((uintptr_t)logits % 16 != 0) return DDT_EINVAL;
+  if (B > DDT_MAX_B || L > DDT_MAX_L || V > 0x7FFFFFFFLL) return DDT_ENOTSUP;
+  const int K = (int)(B < V ? B : V);
+  const int bpd = ceil_log2(K) < 1 ? 1 : ceil_log2(K);
+  if ((int64_t)L * K > DDT_MAX_LK || L * bpd > 122) return DDT_ENOTSUP;
+  const int64_t rows = batch * L;
+  const S1Plan pl = plan_stage1(rows, V, dtype, K);
+  if (!pl.ok || rows * pl.S > 0x7FFFFFFFLL || batch > 0x7FFFFFFFLL) return DDT_ENOTSUP;
+  lay = build_layout(batch, L, V, B, dtype);
+  return DDT_OK;
+}
+
+int build_launch(const void* logits, int dtype, int64_t batch, int32_t L, int64_t V, int32_t B,
+                 int32_t* tree_tokens, int32_t* parents, float* logq, int32_t* depths,
+                 int32_t* num_nodes, uint64_t* mask, const BuildLayout& lay, char* ws,
+                 hipStream_t stream) {
+  const int K = (int)(B < V ? B : V);
+  const int bpd = ceil_log2(K) < 1 ? 1 : ceil_log2(K);
+  const int64_t rows = batch * L;
+  const S1Plan pl = plan_stage1(rows, V, dtype, K);
+  float* tv = (float*)(ws + lay.vals);
+  int32_t* ti = (int32_t*)(ws + lay.ids);
+  double* tz = (double*)(ws + lay.lse);
+  hipError_t e = launch_stage1(dtype, pl, logits, rows, V, K, lay.s1, ws, ti, tv, tz, stream);
+  if (e != hipSuccess) return DDT_EHIP;
+  return launch_select(tv, ti, tz, batch, L, K, B, bpd, tree_tokens, parents, logq, depths,
+                       num_nodes, mask, stream);
+}
+
+// ---- the static scratch of ddtree_build_noalloc ------------------------------
+// One array per GPU, held until the process ends. In host code `scratch`
+// names a host-side stand-in, never the device memory: every use goes
+// through the address hipGetSymbolAddress returns for the current device,
+// taken once per device and kept.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+constexpr int kNoAllocMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kNoAllocMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+char* noalloc_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = (char*)ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 }  // namespace
 
 extern "C" {
@@ -420,28 +484,29 @@ int ddtree_build(const void* logits, int dtype, int64_t batch, int32_t L, int64_
                  int32_t* tree_tokens, int32_t* parents, float* logq, int32_t* depths,
                  int32_t* num_nodes, uint64_t* mask, void* workspace, size_t workspace_bytes,
                  hipStream_t stream) {
-  if (!valid_dtype(dtype) || batch < 0 || L <= 0 || V <= 0 || B <= 0) return DDT_EINVAL;
-  if (batch == 0) return DDT_OK;
-  if (!logits || !tree_tokens || !parents || !logq || !num_nodes || !workspace)
-    return DDT_EINVAL;
-  if ((uintptr_t)logits % 16 != 0) return DDT_EINVAL;
-  if (B > DDT_MAX_B || L > DDT_MAX_L || V > 0x7FFFFFFFLL) return DDT_ENOTSUP;
-  const int K = (int)(B < V ? B : V);
-  const int bpd = ceil_log2(K) < 1 ? 1 : ceil_log2(K);
-  if ((int64_t)L * K > DDT_MAX_LK || L * bpd > 122) return DDT_ENOTSUP;
-  const int64_t rows = batch * L;
-  const S1Plan pl = plan_stage1(rows, V, dtype, K);
-  if (!pl.ok || rows * pl.S > 0x7FFFFFFFLL || batch > 0x7FFFFFFFLL) return DDT_ENOTSUP;
-  const BuildLayout lay = build_layout(batch, L, V, B, dtype);
+  BuildLayout lay;
+  const int chk = build_check(logits, dtype, batch, L, V, B, tree_tokens, parents, logq,
+                              num_nodes, lay);
+  if (chk != DDT_OK || batch == 0) return chk;
+  if (!workspace) return DDT_EINVAL;
   if (workspace_bytes < lay.end) return DDT_EWORKSPACE;
-  char* ws = (char*)workspace;
-  float* tv = (float*)(ws + lay.vals);
-  int32_t* ti = (int32_t*)(ws + lay.ids);
-  double* tz = (double*)(ws + lay.lse);
-  hipError_t e = launch_stage1(dtype, pl, logits, rows, V, K, lay.s1, ws, ti, tv, tz, stream);
-  if (e != hipSuccess) return DDT_EHIP;
-  return launch_select(tv, ti, tz, batch, L, K, B, bpd, tree_tokens, parents, logq, depths,
-                       num_nodes, mask, stream);
+  return build_launch(logits, dtype, batch, L, V, B, tree_tokens, parents, logq, depths,
+                      num_nodes, mask, lay, (char*)workspace, stream);
+}
+
+int ddtree_build_noalloc(const void* logits, int dtype, int64_t batch, int32_t L, int64_t V,
+                         int32_t B, int32_t* tree_tokens, int32_t* parents, float* logq,
+                         int32_t* depths, int32_t* num_nodes, uint64_t* mask,
+                         hipStream_t stream) {
+  BuildLayout lay;
+  const int chk = build_check(logits, dtype, batch, L, V, B, tree_tokens, parents, logq,
+                              num_nodes, lay);
+  if (chk != DDT_OK || batch == 0) return chk;
+  if (lay.end > kNoAllocScratchBytes) return DDT_ENOTSUP;
+  char* ws = noalloc_scratch();
+  if (!ws) return DDT_EHIP;
+  return build_launch(logits, dtype, batch, L, V, B, tree_tokens, parents, logq, depths,
+                      num_nodes, mask, lay, ws, stream);
 }
 
 int ddtree_select(const float* vals, const int32_t* ids, const double* lse, int64_t batch,

@@ -137,6 +137,25 @@ int ddtree_build(const void* logits, int dtype, int64_t batch, int32_t L, int64_
                  hipStream_t stream);
 
 /*
+ * ddtree_build_noalloc -- ddtree_build without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Arguments and
+ * outputs as ddtree_build. The scratch space is a static 16 MiB device array
+ * of the library (one per GPU, held until the process ends), so no call
+ * allocates anything. Shapes whose ddtree_build_workspace_size() exceeds
+ * 16 MiB return DDT_ENOTSUP before anything is enqueued (the batch-256,
+ * B = 256 workload needs 7.5 MiB). Every call on one GPU shares that GPU's
+ * array: calls that can overlap on one GPU (two streams, or two host threads)
+ * race and give undefined results. No kernel reads scratch it did not write
+ * in the same call, so nothing needs clearing between calls. DDT_EHIP if the
+ * array's device address cannot be obtained.
+ */
+int ddtree_build_noalloc(const void* logits, int dtype, int64_t batch, int32_t L, int64_t V,
+                         int32_t B, int32_t* tree_tokens, int32_t* parents, float* logq,
+                         int32_t* depths, int32_t* num_nodes, uint64_t* mask,
+                         hipStream_t stream);
+
+/*
  * ddtree_select -- stage 2 alone (plus the optional fused mask): the tree of
  * ddtree_build from per-row tables, e.g. those of ddtree_row_topk.
  * vals [batch][L][K] float and ids [batch][L][K] int32: each row's K largest

@@ -241,3 +241,19 @@ def test_sparkling_beam_even_schedule_on_the_host(L):
     assert call(3 * 65, Lr=3) == -2      # 65 per depth: above the 64 a depth holds
     assert call(512, Lr=8, batch=0) == 0  # exactly 64 per depth
 
+
+def test_build_noalloc_host_checks(L):
+    """ddtree_build_noalloc validates on the host and rejects shapes beyond its
+    16 MiB static scratch before touching the device."""
+    f = L.ddtree_build_noalloc
+
+    def call(batch=2, Lr=15, V=151936, B=128, out=FAKE, logits=FAKE):
+        return f(logits, 0, batch, Lr, V, B, out, out, out, out, out, out, None)
+    assert L.ddtree_build_workspace_size(1100, 15, 2048, 512, 0) > 16 << 20
+    assert call(batch=1100, V=2048, B=512) == -2
+    assert L.ddtree_build_workspace_size(256, 15, 151936, 256, 0) < 16 << 20
+    assert call(B=0) == -1
+    assert call(out=None) == -1
+    assert call(logits=C.c_void_p(0x100008)) == -1   # not 16-byte aligned
+    assert call(B=513) == -2
+    assert call(batch=0) == 0
