@@ -584,94 +584,143 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
         __syncthreads();
         break;
       }
-      // each parent labels its new anchors' slots with (parent, rank)
+      // parents' first anchor slots (their exclusive offsets, which do not
+      // decrease with the parent index): each anchor finds its parent by
+      // binary search, so no thread writes a long run of labels
+      uint32_t* poff = en.own;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int i = tid * ppt + k;
-        if (k < ppt && i < np) {
-          const int o = off + (k ? cpar[0] : 0);
-          for (int c = 0; c < cpar[k]; ++c) en.own[o + c] = ((uint32_t)i << 16) | (uint32_t)(c + 1);
-        }
+        if (k < ppt && i < np) poff[i] = (uint32_t)(off + (k ? cpar[0] : 0));
       }
       __syncthreads();
-      for (int a = tid; a < A; a += kSelThreads) {
-        const uint32_t ow = en.own[a];
-        const int u = (int)(ow >> 16);
-        const int r = (int)(ow & 0xFFFFu);
-        double Su = 0.0, scu = 0.0;
-        int du = 0, pe = -1;
-        uint64_t lh = 0, ll = 0;
-        if (!(root && u == 0)) {
-          pe = g0 + u - root;
-          Su = en.eS[pe];
-          scu = en.eSc[pe];
-          du = en.eDep[pe];
-          lh = en.eLh[pe];
-          ll = en.eLl[pe] & ~63ull;
-        }
-        const int d = du + 1;
-        const double S = Su + (double)sm.v[(d - 1) * K + r];
-        const double raw = S - sm.Z[d - 1];
-        const double sc = raw > scu ? scu : raw;
-        lex_set_digit(lh, ll, d, (uint32_t)r, bpd);
-        // chain length: the anchor, then rank-0 extensions while they reach
-        // tau (the next depth's spine values are read one step ahead)
-        int ell = 1;
-        {
-          double S2 = S, sc2 = sc;
-          float vn = sm.v[(d < L ? d : L - 1) * K];
-          double zn = sm.Z[d < L ? d : L - 1];
-          for (int dd = d + 1; dd <= L; ++dd) {
-            const double v0 = (double)vn, Zm = zn;
-            const int nx = dd < L ? dd : L - 1;
-            vn = sm.v[nx * K];
-            zn = sm.Z[nx];
-            S2 += v0;
-            const double raw2 = S2 - Zm;
-            sc2 = raw2 > sc2 ? sc2 : raw2;
-            if (sc2 < tau) break;
-            ++ell;
+      const int nE0 = sm.nE;
+      // anchors, consecutive per thread (1, or 2 when A > kSelThreads): the
+      // parent, S and score, and the chain length -- the anchor, then its
+      // rank-0 extensions while they reach tau (S summed left to right, the
+      // next four depths' spine values read per step)
+      const int apt = A > kSelThreads ? 2 : 1;
+      double aS[2] = {0.0, 0.0}, aSc[2] = {0.0, 0.0};
+      uint64_t aLh[2] = {0, 0}, aLl[2] = {0, 0};
+      int aD[2] = {0, 0}, aPe[2] = {-1, -1}, aR[2] = {0, 0}, aEll[2] = {0, 0};
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int a = tid * apt + k;
+        if (k < apt && a < A) {
+          int lo = 0, hi = np - 1;  // the last parent whose first slot is <= a
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((int)poff[mid] <= a) lo = mid;
+            else hi = mid - 1;
           }
-        }
-        const int pos = atomicAdd(&sm.nE, ell);
-        if (pos + ell > kECap) {
-          // slots of this chain below the capacity stay unwritten: mark them
-          for (int q = pos; q < kECap; ++q) en.eSc[q] = -INFINITY;
-          sm.ovf = 1;
-          continue;
-        }
-        en.eS[pos] = S;
-        en.eSc[pos] = sc;
-        en.ePar[pos] = (int16_t)pe;
-        en.eRank[pos] = (uint16_t)r;
-        en.eDep[pos] = (uint8_t)d;
-        en.eLh[pos] = lh;
-        en.eLl[pos] = ll | (uint64_t)d;
-        {
+          const int u = lo;
+          const int r = a - (int)poff[u] + 1;
+          double Su = 0.0, scu = 0.0;
+          int du = 0, pe = -1;
+          uint64_t lh = 0, ll = 0;
+          if (!(root && u == 0)) {
+            pe = g0 + u - root;
+            Su = en.eS[pe];
+            scu = en.eSc[pe];
+            du = en.eDep[pe];
+            lh = en.eLh[pe];
+            ll = en.eLl[pe] & ~63ull;
+          }
+          const int d = du + 1;
+          const double S = Su + (double)sm.v[(d - 1) * K + r];
+          const double raw = S - sm.Z[d - 1];
+          const double sc = raw > scu ? scu : raw;
+          lex_set_digit(lh, ll, d, (uint32_t)r, bpd);
+          int ell = 1;
+          bool alive = true;
           double S2 = S, sc2 = sc;
-          float vn = sm.v[(d < L ? d : L - 1) * K];
-          double zn = sm.Z[d < L ? d : L - 1];
-          for (int i = 1; i < ell; ++i) {
-            const int dd = d + i;
-            const double v0 = (double)vn, Zm = zn;
-            const int nx = dd < L ? dd : L - 1;
-            vn = sm.v[nx * K];
-            zn = sm.Z[nx];
-            S2 += v0;
-            const double raw2 = S2 - Zm;
-            sc2 = raw2 > sc2 ? sc2 : raw2;
-            {
-              const int q = pos + i;
-              en.eS[q] = S2;
-              en.eSc[q] = sc2;
-              en.ePar[q] = (int16_t)(q - 1);
-              en.eRank[q] = 0;
-              en.eDep[q] = (uint8_t)dd;
-              en.eLh[q] = lh;
-              en.eLl[q] = ll | (uint64_t)dd;
+          for (int dd0 = d + 1; dd0 <= L && alive; dd0 += 4) {
+            float v4[4];
+            double z4[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int row = (dd0 + q <= L ? dd0 + q : L) - 1;
+              v4[q] = sm.v[row * K];
+              z4[q] = sm.Z[row];
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const bool valid = alive && dd0 + q <= L;
+              const double S3 = S2 + (double)v4[q];
+              const double raw2 = S3 - z4[q];
+              const double sc3 = raw2 > sc2 ? sc2 : raw2;
+              alive = valid && sc3 >= tau;
+              S2 = alive ? S3 : S2;
+              sc2 = alive ? sc3 : sc2;
+              ell += alive ? 1 : 0;
             }
           }
+          aS[k] = S;
+          aSc[k] = sc;
+          aLh[k] = lh;
+          aLl[k] = ll;
+          aD[k] = d;
+          aPe[k] = pe;
+          aR[k] = r;
+          aEll[k] = ell;
         }
+      }
+      // slots in anchor order: a block scan of the chain lengths; the
+      // anchor entries first, their positions kept for the chain entries
+      int T;
+      const int aoff = block_excl_scan_reg<kSelThreads>(aEll[0] + aEll[1], sm.wsum, T);
+      int* apos = en.cnt;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int a = tid * apt + k;
+        if (k < apt && a < A) {
+          const int pos = nE0 + aoff + (k ? aEll[0] : 0);
+          apos[a] = pos;
+          if (pos < kECap) {
+            en.eS[pos] = aS[k];
+            en.eSc[pos] = aSc[k];
+            en.ePar[pos] = (int16_t)aPe[k];
+            en.eRank[pos] = (uint16_t)aR[k];
+            en.eDep[pos] = (uint8_t)aD[k];
+            en.eLh[pos] = aLh[k];
+            en.eLl[pos] = aLl[k] | (uint64_t)aD[k];
+          }
+        }
+      }
+      const int nEnd = nE0 + T < kECap ? nE0 + T : kECap;
+      __syncthreads();
+      if (tid == 0) {
+        sm.nE = nE0 + T;
+        // entries [0, kECap) stay valid prefixes scoring >= tau
+        if (nE0 + T > kECap) sm.ovf = 1;
+      }
+      // chain entries, one thread per slot: its anchor by binary search over
+      // the anchors' slots, then S summed left to right from the anchor's
+      // and the score's running minimum along the chain
+      for (int q = nE0 + tid; q < nEnd; q += kSelThreads) {
+        int lo = 0, hi = A - 1;  // the last anchor whose slot is <= q
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (apos[mid] <= q) lo = mid;
+          else hi = mid - 1;
+        }
+        const int pa = apos[lo], j = q - pa;
+        if (j == 0) continue;
+        const int d = en.eDep[pa];
+        double S2 = en.eS[pa], sc2 = en.eSc[pa];
+        for (int i = 1; i <= j; ++i) {
+          const int row = d + i - 1;  // depth d + i
+          S2 += (double)sm.v[row * K];
+          const double raw2 = S2 - sm.Z[row];
+          sc2 = raw2 > sc2 ? sc2 : raw2;
+        }
+        en.eS[q] = S2;
+        en.eSc[q] = sc2;
+        en.ePar[q] = (int16_t)(q - 1);
+        en.eRank[q] = 0;
+        en.eDep[q] = (uint8_t)(d + j);
+        en.eLh[q] = en.eLh[pa];
+        en.eLl[q] = (en.eLl[pa] & ~63ull) | (uint64_t)(d + j);
       }
       __syncthreads();
       if (sm.ovf) break;
@@ -681,8 +730,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
       if (g0 == g1) break;
     }
     if (!sm.ovf) break;
-    // overflow: entries [0, n) are prefixes scoring >= tau, except slots
-    // marked -inf
+    // overflow: entries [0, n) are prefixes scoring >= tau
     const int n = sm.nE < kECap ? sm.nE : kECap;
     if (attempt == kSelRetries || n < B) break;
     const double t1 = sel_tau_hist(
