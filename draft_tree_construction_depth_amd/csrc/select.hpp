@@ -128,6 +128,8 @@ struct SelectSmem {
   int nE;
   int ovf;
   int nsel;
+  uint32_t wbad[kSelWaves];  // per wave: some value outside the exact-sum window
+  int f2;                    // every row's top log-probability is clearly negative
 };
 
 __device__ __forceinline__ void lex_set_digit(uint64_t& hi, uint64_t& lo, int d, uint32_t r,
@@ -244,7 +246,11 @@ __device__ void heap_fallback(const SelectParams& p, SelectSmem& sm, int64_t b) 
 // value whose minimum over wave 0 is a lower bound with >= B scores at or
 // above it. mem (memcap doubles of LDS, not read by onedev) holds the cut
 // bin's members.
-template <class OD, class LB>
+// With EXACT false the result is instead the lower edge of the bin holding
+// the B-th, moved down by a millionth of a bin: at or below every member of
+// that bin, so a valid lower bound with the same guarantee, found without
+// ranking the bin (a slightly larger E to enumerate).
+template <bool EXACT = true, class OD, class LB>
 __device__ double sel_tau_hist(SelectSmem& sm, int LK, int B, OD onedev, LB lane_bound,
                                double* mem = nullptr, int memcap = kMergeCap) {
   if (mem == nullptr) mem = sm.u.mt.a;
@@ -286,6 +292,12 @@ __device__ double sel_tau_hist(SelectSmem& sm, int LK, int B, OD onedev, LB lane
     sm.kexc = exc;
   }
   __syncthreads();
+  if constexpr (!EXACT) {
+    const int kc = sm.kcut;
+    if (!(scale > 0.0) || kc >= kSelThreads - 1) return mn;
+    const double edge = top - ((double)kc + 1.000001) / scale;
+    return edge > mn ? edge : mn;
+  }
   const int kb = sm.kcut, t = B - 1 - sm.kexc;  // the B-th is member t of bin kb
   for (int i = tid; i < LK; i += kSelThreads) {
     const double sc = onedev(i);
@@ -482,27 +494,77 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   const int L = p.L, K = p.K, B = p.B, LK = L * K, bpd = p.bpd;
   const float* vals = p.vals + (size_t)b * LK;
 
-  for (int i = tid; i < LK; i += kSelThreads) sm.v[i] = vals[i];
-  if (tid < L) sm.lse[tid] = p.lse[(size_t)b * L + tid];
-  __syncthreads();
-  if (tid == 0) {
-    // Z_d and the spine (all ranks 0): float64, left to right.
-    double acc = 0.0, S = 0.0, sc = 0.0;
-    sm.P0[0] = 0.0;
-    sm.sig[0] = 0.0;
-    for (int d = 1; d <= L; ++d) {
-      acc += sm.lse[d - 1];
-      sm.Z[d - 1] = acc;
-      S += (double)sm.v[(d - 1) * K];
-      const double raw = S - acc;
-      sc = raw > sc ? sc : raw;
-      sm.P0[d] = S;
-      sm.sig[d] = sc;
+  if (tid < kWave) {
+    // Z_d and the spine (all ranks 0): float64, left to right, in wave 0's
+    // registers while the other waves stage the table; four rows' values
+    // are read across lanes per step, so only the additions are serial
+    const int lane = tid;
+    // lane d holds row d's normaliser, top value and last value
+    const double zl = lane < L ? p.lse[(size_t)b * L + lane] : 0.0;
+    const float vl = lane < L ? vals[(size_t)lane * K] : 0.0f;
+    const float vk = lane < L ? vals[(size_t)lane * K + K - 1] : 0.0f;
+    double acc = 0.0, S = 0.0, sc = 0.0, myZ = 0.0, myP = 0.0, mySig = 0.0;
+    double zmax = 0.0, sabs = 0.0;  // magnitude bounds of every Z_d and every S
+    for (int d0 = 0; d0 < L; d0 += 4) {
+      double z4[4];
+      float v4[4], w4[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        z4[q] = lane_value(zl, d0 + q);  // d0 + q < kMaxL + 4 <= 64
+        v4[q] = lane_value(vl, d0 + q);
+        w4[q] = lane_value(vk, d0 + q);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (d0 + q < L) {
+          acc += z4[q];
+          S += (double)v4[q];
+          const double raw = S - acc;
+          sc = raw > sc ? sc : raw;
+          zmax = fmax(zmax, fabs(acc));
+          sabs += (double)fmaxf(fabsf(v4[q]), fabsf(w4[q]));
+          if (lane == d0 + q) {
+            myZ = acc;
+            myP = S;
+            mySig = sc;
+          }
+        }
+      }
     }
-    sm.nE = 0;
-    sm.ovf = 0;
+    // every row's top log-probability below -M, M far above the rounding of
+    // any score (a difference of sums of magnitude <= zmax + sabs)
+    const double M = 1e-12 * (1.0 + zmax + sabs);
+    const uint64_t ok = __ballot(lane >= L || (double)vl - zl < -M);
+    if (lane < L) {
+      sm.Z[lane] = myZ;
+      sm.P0[lane + 1] = myP;
+      sm.sig[lane + 1] = mySig;
+    }
+    if (lane == 0) {
+      sm.P0[0] = 0.0;
+      sm.sig[0] = 0.0;
+      sm.nE = 0;
+      sm.ovf = 0;
+      sm.f2 = ok == ~0ull ? 1 : 0;
+    }
+  }
+  {
+    // exact-sum window: every nonzero value's exponent within 11 of the
+    // first row's top value's (denormals count as exponent 1)
+    const int eref = (int)((__float_as_uint(vals[0]) >> 23) & 0xFFu);
+    bool bad = false;
+    for (int i = tid; i < LK; i += kSelThreads) {
+      const float v = vals[i];
+      sm.v[i] = v;
+      int e = (int)((__float_as_uint(v) >> 23) & 0xFFu);
+      e = e == 0 ? 1 : e;
+      bad |= v != 0.0f && (e == 255 || e < eref - 11 || e > eref + 11);
+    }
+    const uint64_t wb = __ballot(bad);
+    if ((tid & 63) == 0) sm.wbad[tid >> 6] = wb != 0 ? 1u : 0u;
   }
   __syncthreads();
+
 
   // ---- 1. threshold from the one-deviation prefixes -------------------------
   double tau = -INFINITY;
@@ -515,10 +577,19 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
       return raw > sm.sig[d] ? sm.sig[d] : raw;
     };
     const int q = (B + L - 1) / L < K ? (B + L - 1) / L : K;
-    tau = sel_tau_hist(sm, LK, B, onedev,
-                       [&](int lane) { return lane < L ? onedev(lane * K + q - 1) : INFINITY; });
+    tau = sel_tau_hist<false>(
+        sm, LK, B, onedev,
+        [&](int lane) { return lane < L ? onedev(lane * K + q - 1) : INFINITY; });
   }
 
+  // Fast path: sums of row values are exact (their exponents span <= 22, so
+  // every S is the same whatever the summation order) and no score clamps
+  // (every step along a path lowers the score by more than any rounding).
+  // Then a rank-0 extension to depth e scores (S + (P0[e] - P0[d])) - Z[e-1]
+  // directly, strictly decreasing in e: chains are found by binary search.
+  bool fast = sm.f2 != 0;
+#pragma unroll
+  for (int i = 0; i < kSelWaves; ++i) fast = fast && sm.wbad[i] == 0;
   // ---- 2. enumerate E = {score >= tau} by chains ----------------------------
   // If E outgrows its capacity, every entry found so far is a valid prefix
   // scoring >= tau: the B-th best of them is a valid, usually much tighter,
@@ -632,8 +703,19 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
           const double sc = raw > scu ? scu : raw;
           lex_set_digit(lh, ll, d, (uint32_t)r, bpd);
           int ell = 1;
-          bool alive = true;
+          bool alive = !fast;
           double S2 = S, sc2 = sc;
+          if (fast) {
+            // the deepest e in [d, L] with (S + (P0[e] - P0[d])) - Z[e-1] >= tau
+            const double pd = sm.P0[d];
+            int lo2 = d, hi2 = L;
+            while (lo2 < hi2) {
+              const int mid = (lo2 + hi2 + 1) >> 1;
+              if ((S + (sm.P0[mid] - pd)) - sm.Z[mid - 1] >= tau) lo2 = mid;
+              else hi2 = mid - 1;
+            }
+            ell = lo2 - d + 1;
+          }
           for (int dd0 = d + 1; dd0 <= L && alive; dd0 += 4) {
             float v4[4];
             double z4[4];
@@ -708,11 +790,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
         if (j == 0) continue;
         const int d = en.eDep[pa];
         double S2 = en.eS[pa], sc2 = en.eSc[pa];
-        for (int i = 1; i <= j; ++i) {
-          const int row = d + i - 1;  // depth d + i
-          S2 += (double)sm.v[row * K];
-          const double raw2 = S2 - sm.Z[row];
-          sc2 = raw2 > sc2 ? sc2 : raw2;
+        if (fast) {
+          S2 += sm.P0[d + j] - sm.P0[d];
+          sc2 = S2 - sm.Z[d + j - 1];
+        } else {
+          for (int i = 1; i <= j; ++i) {
+            const int row = d + i - 1;  // depth d + i
+            S2 += (double)sm.v[row * K];
+            const double raw2 = S2 - sm.Z[row];
+            sc2 = raw2 > sc2 ? sc2 : raw2;
+          }
         }
         en.eS[q] = S2;
         en.eSc[q] = sc2;
