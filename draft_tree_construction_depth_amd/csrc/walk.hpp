@@ -5,11 +5,12 @@
 // 64-bit words; one thread builds one row by walking the parent chain.
 //
 // Walk: DDTree explainer, section 5 (verifier walk), TreeSpark README item 4
-// (argmax-following acceptance walk). One wavefront per request holds the
-// request's parent, token and target-token arrays in registers (B <= 512, so
-// <= 8 nodes per lane); each step is one compare and one ballot per held
-// slot plus one cross-lane read of the next target, and the walk takes at
-// most L steps.
+// (argmax-following acceptance walk). One wavefront per request loads the
+// request's parent, token and target-token arrays (B <= 512, so <= 8 nodes
+// per lane), stages the targets in LDS, and marks in parallel, for every
+// node, the child that carries the node's target token (at most one: the
+// siblings are distinct tokens of one row). The walk then follows those
+// marks from the root, one LDS read per accepted node, at most L steps.
 #pragma once
 
 #include "common.hpp"
@@ -74,6 +75,11 @@ struct WalkParams {
 };
 
 __global__ __launch_bounds__(kWave) void walk_kernel(WalkParams p) {
+  // LDS: every node's target token, and for every node the lowest-numbered
+  // child that carries that token (kNone: none)
+  constexpr int kNone = 0x7FFFFFFF;
+  __shared__ int s_tgt[kWalkMaxPerLane * kWave + 1];
+  __shared__ int s_next[kWalkMaxPerLane * kWave + 1];
   const int64_t b = blockIdx.x;
   const int lane = threadIdx.x;
   const int B = p.B, L = p.L;
@@ -86,43 +92,54 @@ __global__ __launch_bounds__(kWave) void walk_kernel(WalkParams p) {
   for (int t = 0; t < kWalkMaxPerLane; ++t) {
     const int j = lane + t * kWave;
     const bool in = j < B;
-    par[t] = in ? p.parents[(size_t)b * B + j] : -2;
+    par[t] = in ? p.parents[(size_t)b * B + j] : -1;
     tok[t] = in ? p.tree_tokens[(size_t)b * B + j] : 0;
     tg[t] = in ? tgt[j + 1] : 0;
   }
   const int root_tgt = tgt[0];
   int n = p.num_nodes[b];
   n = n < 0 ? 0 : (n > B ? B : n);
-  const int slots = (n + kWave - 1) / kWave;  // uniform
-#pragma unroll
-  for (int t = 0; t < kWalkMaxPerLane; ++t)
-    if (lane + t * kWave >= n) par[t] = -2;  // never a child
-  int cur = 0, len = 0, want = root_tgt;
-  while (len < L) {
-    // the child of cur carrying the wanted token (lowest node number if
-    // several); its target token is read from its lane
-    int found = 0, next = 0;
-#pragma unroll
-    for (int t = 0; t < kWalkMaxPerLane; ++t) {
-      if (t < slots && found == 0) {
-        const uint64_t M = __ballot(par[t] == cur && tok[t] == want);
-        if (M) {
-          const int src = __builtin_ctzll(M);
-          found = t * kWave + src + 1;
-          next = __builtin_amdgcn_readlane(tg[t], src);
-        }
-      }
-    }
-    if (found == 0) break;
-    if (lane == 0) p.accepted_nodes[(size_t)b * L + len] = found;
-    ++len;
-    cur = found;
-    want = next;
+  if (lane == 0) {
+    s_tgt[0] = root_tgt;
+    s_next[0] = kNone;
   }
-  for (int i = len + lane; i < L; i += kWave) p.accepted_nodes[(size_t)b * L + i] = -1;
+#pragma unroll
+  for (int t = 0; t < kWalkMaxPerLane; ++t) {
+    const int j = lane + t * kWave;
+    if (j < B) {
+      s_tgt[j + 1] = tg[t];
+      s_next[j + 1] = kNone;
+    }
+  }
+  // (one wavefront: its LDS operations take effect in program order)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // a node whose token is its parent's target token is that parent's next
+  // step (siblings carry distinct tokens; with equal ones the lowest node
+  // number wins); malformed parents (not an earlier node) never match
+#pragma unroll
+  for (int t = 0; t < kWalkMaxPerLane; ++t) {
+    const int j = lane + t * kWave;
+    if (j < n && par[t] >= 0 && par[t] <= j && tok[t] == s_tgt[par[t]])
+      atomicMin(&s_next[par[t]], j + 1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // the walk itself: one LDS read per accepted node
+  int cur = 0, len = 0, path = -1;
+  while (len < L) {
+    const int nx = s_next[cur];
+    if (nx == kNone) break;
+    if (lane == len) path = nx;
+    ++len;
+    cur = nx;
+  }
+  for (int i = lane; i < L; i += kWave) p.accepted_nodes[(size_t)b * L + i] = i == lane ? path : -1;
   if (lane == 0) {
     p.accept_len[b] = len;
-    p.next_token[b] = want;
+    p.next_token[b] = s_tgt[cur];
   }
 }
 
