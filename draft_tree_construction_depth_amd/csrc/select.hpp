@@ -129,6 +129,7 @@ struct SelectSmem {
   int ovf;
   int nsel;
   uint32_t wbad[kSelWaves];  // per wave: some value outside the exact-sum window
+  int more;                  // some entry of this generation has a deviating child
   int f2;                    // every row's top log-probability is clearly negative
 };
 
@@ -327,6 +328,7 @@ __device__ double sel_tau_hist(SelectSmem& sm, int LK, int B, OD onedev, LB lane
 // Phase 3 (after an enumeration without overflow): order E, emit the
 // first B (tokens, parents, log-probs, depths, node count). en.eRank holds
 // each entry's index into its row's candidate table.
+template <bool ZERO_HIST = true>
 __device__ __forceinline__ void sel_order_emit(const SelectParams& p, SelectSmem& sm, int64_t b,
                                                double tau) {
   SelEnum& en = sm.u.en;
@@ -358,8 +360,10 @@ __device__ __forceinline__ void sel_order_emit(const SelectParams& p, SelectSmem
     const double t = (top - sc) * scale;
     return t >= (double)(kSelThreads - 1) ? kSelThreads - 1 : (t > 0.0 ? (int)t : 0);
   };
-  sm.hist[tid] = 0;
-  __syncthreads();
+  if constexpr (ZERO_HIST) {
+    sm.hist[tid] = 0;
+    __syncthreads();
+  }
   int ebin[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
@@ -609,6 +613,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
       en.eLl[d] = (uint64_t)(d + 1);
     }
     if (tid == 0) sm.nE = D0;
+    sm.hist[tid] = 0;  // the ordering's histogram (no threshold pass follows)
     __syncthreads();
     int g0 = 0, g1 = D0, root = 1;
     for (;;) {
@@ -666,6 +671,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
       }
       __syncthreads();
       const int nE0 = sm.nE;
+      if (tid == 0) sm.more = 0;  // set below, read after this generation's last barrier
+      // does an entry at depth dd with sum S have a deviating child (rank 1
+      // of the next row) reaching tau? the count search's own test
+      auto has_child = [&](int dd, double S) {
+        return dd < L && K > 1 && (S + (double)sm.v[dd * K + 1]) - sm.Z[dd] >= tau;
+      };
       // anchors, consecutive per thread (1, or 2 when A > kSelThreads): the
       // parent, S and score, and the chain length -- the anchor, then its
       // rank-0 extensions while they reach tau (S summed left to right, the
@@ -759,6 +770,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
           const int pos = nE0 + aoff + (k ? aEll[0] : 0);
           apos[a] = pos;
           if (pos < kECap) {
+            if (has_child(aD[k], aS[k])) sm.more = 1;
             en.eS[pos] = aS[k];
             en.eSc[pos] = aSc[k];
             en.ePar[pos] = (int16_t)aPe[k];
@@ -801,6 +813,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
             sc2 = raw2 > sc2 ? sc2 : raw2;
           }
         }
+        if (has_child(d + j, S2)) sm.more = 1;
         en.eS[q] = S2;
         en.eSc[q] = sc2;
         en.ePar[q] = (int16_t)(q - 1);
@@ -810,6 +823,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
         en.eLl[q] = (en.eLl[pa] & ~63ull) | (uint64_t)(d + j);
       }
       __syncthreads();
+      // no entry of this generation has a deviating child: the next
+      // generation would find no anchors
+      if (!sm.more && !sm.ovf) break;
       if (sm.ovf) break;
       g0 = g1;
       g1 = sm.nE;
@@ -834,7 +850,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     if (tid == 0) heap_fallback(p, sm, b);
     __syncthreads();
   } else {
-    sel_order_emit(p, sm, b, tau);
+    sel_order_emit<false>(p, sm, b, tau);
   }
   sel_mask(p, sm, b);
 }
