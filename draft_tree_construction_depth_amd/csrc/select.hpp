@@ -23,20 +23,35 @@
 //     least tau.
 //  2. Enumerate E = {prefixes with score >= tau} by "chains": a chain is an
 //     anchor prefix whose last rank is >= 1 followed by its rank-0
-//     extensions, which one thread walks in registers. Generation g holds
-//     the chains with g nonzero ranks; a generation's deviating children
-//     are counted by binary search over the sorted row, allocated by a block
-//     scan (DPP inside waves) and walked in parallel. Drafter trees have <= 3 deviations per
-//     path in practice, so this needs a few block-synchronous steps instead
-//     of one per tree level.
+//     extensions. Generation g holds the chains with g nonzero ranks; a
+//     generation's deviating children are counted by binary search over the
+//     sorted row, allocated by a block scan (DPP inside waves), each new
+//     anchor finds its parent by binary search over the parents' offsets,
+//     the chain lengths are summed by a second block scan, and every chain
+//     entry is then written by its own thread. The generations stop as soon
+//     as no new entry has a deviating child reaching tau. Drafter trees
+//     have <= 3 deviations per path in practice, so this needs a few
+//     block-synchronous steps instead of one per tree level.
+//     Fast path (decided per request): when every nonzero row value's binary
+//     exponent lies within 11 of the first row's top value's, every sum of
+//     <= 32 row values is exact in float64 (a 22-binade span, 24-bit
+//     mantissas and 5 bits of carries fit in 53 bits), so a rank-0
+//     extension's score is (S + P0[e] - P0[d]) - Z[e-1] whatever the order
+//     of summation; when in
+//     addition every row's top log-probability is clearly negative no score
+//     clamps, so a chain's scores strictly decrease and its length is one
+//     binary search. Otherwise chains are walked step by step with the
+//     clamp, in the same arithmetic as the canonical score.
 //  3. Histogram E's scores into bins over [tau, best]; the first bins that
 //     hold >= B entries form E2, which contains the output. Place each entry
 //     of E2 in the order (score, then 128-bit lexicographic rank key) by
 //     counting the entries before it. Emit the first B, mapping parents to
 //     output node numbers (a parent is in the output and precedes it).
 //  4. Write the bit-packed ancestor mask rows from the parents in LDS.
-// If E would exceed kECap entries (flat rows with V < B, massive ties), the
-// block instead runs the pages' best-first heap in one thread, in LDS:
+// If E would exceed kECap entries, the B-th best of the entries found so far
+// is a valid, tighter threshold and the enumeration restarts from it (at most
+// kSelRetries times); only if that does not help (massive exact ties, V < B)
+// does the block run the pages' best-first heap in one thread, in LDS:
 // exact, slower, and only for such inputs.
 #pragma once
 
