@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "select.hpp"
@@ -121,6 +122,22 @@ BuildLayout build_layout(int64_t batch, int32_t L, int64_t V, int32_t B, int dty
   return l;
 }
 
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 template <int DT, int NV, int GS>
 void launch_chunks(bool aligned, dim3 grid, const ddt::Stage1Params& prm, hipStream_t st) {
   if (aligned) {
@@ -136,8 +153,13 @@ template <int DT>
 hipError_t launch_stage1_dt(const S1Plan& pl, bool aligned, int64_t rows,
                             const ddt::Stage1Params& prm, hipStream_t st) {
   if (pl.row) {
-    hipLaunchKernelGGL((ddt::stage1_row_kernel<DT, 8, 4>), dim3((unsigned)rows),
-                       dim3(ddt::kS1Threads), 0, st, prm);
+    // the row kernel holds four workgroups per CU
+    if (rows <= 4 * (int64_t)cu_count())
+      hipLaunchKernelGGL((ddt::stage1_row_kernel<DT, 8, 4, true>), dim3((unsigned)rows),
+                         dim3(ddt::kS1Threads), 0, st, prm);
+    else
+      hipLaunchKernelGGL((ddt::stage1_row_kernel<DT, 8, 4, false>), dim3((unsigned)rows),
+                         dim3(ddt::kS1Threads), 0, st, prm);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)(rows * pl.S));

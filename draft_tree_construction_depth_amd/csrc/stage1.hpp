@@ -969,6 +969,9 @@ __device__ __forceinline__ int b3_of(const int (&k)[kS1Waves]) { return k[0] + k
 // nearly alone, with little to hide its latency. Lowering a wave's priority
 // as it advances (four levels over the row) keeps the rows of a CU closer
 // together (batch 64: rows end 45-54 us into the launch instead of 35-61).
+// Only when every row is resident at once (PRIO): while more rows wait for a
+// slot, staggered ends keep the CUs' slots refilling evenly (batch 256: 2%
+// slower with the schedule on every row, 3% with it on the last generation).
 __device__ __forceinline__ void progress_priority(int c, int S) {
   const int q = (4 * c) / S;
   if (q <= 0)
@@ -981,7 +984,7 @@ __device__ __forceinline__ void progress_priority(int c, int S) {
     __builtin_amdgcn_s_setprio(0);
 }
 
-template <int DT, int NV, int GS>
+template <int DT, int NV, int GS, bool PRIO>
 __global__ __launch_bounds__(kS1Threads, 4) void stage1_row_kernel(Stage1Params p) {
   constexpr int EPV = DT == 0 ? 8 : 4;
   __shared__ RowSmem sm;
@@ -1012,15 +1015,15 @@ __global__ __launch_bounds__(kS1Threads, 4) void stage1_row_kernel(Stage1Params 
   v4u32 A[NV], Bf[NV];
   load_chunk_buf<NV>(A, rowp, 0, rowbytes);
   load_chunk_buf<NV>(Bf, rowp, CB, rowbytes);
-  progress_priority(0, S);
+  if (PRIO) progress_priority(0, S);
   row_chunk<DT, NV, GS, true>(A, sm, 0, nvec_of(0), need, lregs, st, true);
   load_chunk_buf<NV>(A, rowp, 2 * CB, rowbytes);
   for (int c = 1; c < S; c += 2) {
-    progress_priority(c, S);
+    if (PRIO) progress_priority(c, S);
     row_chunk<DT, NV, GS, false>(Bf, sm, (int64_t)c * CH, nvec_of(c), need, lregs, st,
                                  claim_due(c));
     load_chunk_buf<NV>(Bf, rowp, (int64_t)(c + 2) * CB, rowbytes);
-    progress_priority(c + 1, S);
+    if (PRIO) progress_priority(c + 1, S);
     if (c + 1 < S)
       row_chunk<DT, NV, GS, false>(A, sm, (int64_t)(c + 1) * CH, nvec_of(c + 1), need, lregs, st,
                                    claim_due(c + 1));
