@@ -16,8 +16,8 @@
 //                   then per parent column the tile's max, sum of exp and
 //                   top-k -> one partial record per (128-row tile, parent).
 //                   W (V x H bf16, 778 MB at the README shape) streams from
-//                   HBM once per depth; the parents' embedding rows are
-//                   shared by the four waves through LDS.
+//                   HBM once per depth through an LDS ring; each wave takes
+//                   32 parents' embedding rows straight into registers.
 //  ts_merge_kernel  per request: each parent's log-sum-exp (float64) and
 //                   top-k from the partials; children scored parent score +
 //                   z - lse; the frontier for d+1 = the best F children.
@@ -36,10 +36,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTsThreads = 256;
-constexpr int kTsBV = 128;     // W rows per workgroup (4 waves x 32)
-constexpr int kTsBM = 128;     // parent columns per workgroup (4 MFMA tiles of 32)
+constexpr int kTsBV = 128;     // W rows per workgroup (4 MFMA tiles of 32)
+constexpr int kTsBM = 128;     // parent columns per workgroup (32 per wave)
 constexpr int kTsKT = 64;      // reduction elements per step
-constexpr int kTsGPad = 8;     // LDS row padding (bf16) against bank conflicts
 constexpr int kTsKMax = 8;     // largest branching factor k
 constexpr int kTsFMax = 8;     // largest frontier width F
 constexpr int kTsDMax = 16;    // largest depth (4-bit digits in a 64-bit key)
@@ -57,20 +56,6 @@ struct TsGemmParams {
   float* psum;             // [nvt][Mtot] sum of exp(z - pmax)
   float* pval;             // [nvt][Mtot][kTsKMax] top-k z, best first
   int32_t* pid;            // [nvt][Mtot][kTsKMax]
-};
-
-// 16-byte aligned so that the fragment reads and the staging stores are
-// single 16-byte LDS instructions.
-struct alignas(16) TsGemmSmem {
-  union {
-    uint16_t g[2][kTsBM][kTsKT + kTsGPad];  // parents' embedding rows, double buffered
-    struct {
-      float mx[4][kTsBM];
-      float sm[4][kTsBM];
-      float val[4][kTsBM][kTsKMax];
-      int id[4][kTsBM][kTsKMax];
-    } red;  // per-wave partials of the epilogue
-  };
 };
 
 constexpr int kTsPad = 0x7FFFFFFF;  // id of an empty list slot (value -inf)
@@ -135,8 +120,27 @@ __device__ __forceinline__ void ts_merge_sorted(float (&av)[KK], int (&ai)[KK], 
       if ((i & d) == 0) ts_cas(av[i], ai[i], av[i + d], ai[i + d]);
 }
 
+// ---------------------------------------------------------------------------
+// GEMM schedule: the head weight W streams into an LDS ring by direct
+// buffer-to-LDS loads, each wave instruction reading eight whole 128-byte row
+// segments, three k-steps ahead; the parents' embedding chunks go straight
+// into registers in the MFMA B layout, two steps ahead, from the L2. Wave w
+// owns parent columns [32 w, 32 w + 32) against all 128 vocabulary rows of
+// the tile, so each parent's partial record comes out of one wave, with no
+// cross-wave combine.
+constexpr int kTsStages = 4;  // W ring depth (16 KiB per stage)
+
+// LDS row r, 16-byte chunk c holds W chunk c ^ (r & 7) of that row's step
+// segment, so that a fragment read of 32 consecutive rows spreads over all
+// banks.
+struct alignas(16) TsGemmSmem {
+  uint16_t w[kTsStages][kTsBV][kTsKT];
+};
+
+typedef __attribute__((address_space(3))) void* ts_lds_ptr;
+
 template <int KK>
-__global__ __launch_bounds__(kTsThreads) void ts_gemm_kernel(TsGemmParams p) {
+__global__ __launch_bounds__(kTsThreads, 2) void ts_gemm_kernel(TsGemmParams p) {
   __shared__ TsGemmSmem sm;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int vt = blockIdx.x;
@@ -144,215 +148,209 @@ __global__ __launch_bounds__(kTsThreads) void ts_gemm_kernel(TsGemmParams p) {
   const int H = p.H;
   const int64_t V = p.V;
   const int ncols = p.M - m0 < kTsBM ? p.M - m0 : kTsBM;
-  const int nct = (ncols + 31) >> 5;  // MFMA column tiles in use
-
-  // W through a buffer resource over this workgroup's rows: the lane's byte
-  // offset is fixed, the k-step's goes in a scalar, so no address arithmetic
-  // per step (A operand: row l % 32 of the wave's 32 rows; rows past V read
-  // row V-1 and are masked later)
+  const bool active = 32 * w < ncols;  // wave-uniform: this wave has parents
+  const int ws = __builtin_amdgcn_readfirstlane(w);  // the wave index in a scalar register
   const int64_t vt0 = (int64_t)vt * kTsBV;
-  const int64_t vrow = vt0 + w * 32 + (l & 31);
-  const int64_t vload = vrow < V ? vrow : V - 1;
+  const int nks = H / kTsKT;
+
+  // W loads: instruction i of wave w covers tile rows 8 g .. 8 g + 7, g = 4 i
+  // + w; lane l takes row 8 g + l / 8 and chunk (l % 8) ^ (l / 8) of it, and
+  // lands at LDS chunk l % 8 of that row (the instruction writes 64
+  // consecutive 16-byte slots). Rows past V read row V - 1 (masked later).
+  // (buffer loads over this tile's rows: a fixed per-lane byte offset and the
+  // step's offset in a scalar, so no per-step vector address temporaries)
   const int64_t wbytes = (V - vt0) * H * 2;
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.W + vt0 * H), (short)0, (int)(wbytes < 0x7FFFFFFF ? wbytes : 0x7FFFFFFF), 0x00020000);
-  const uint32_t woff = (uint32_t)((vload - vt0) * H * 2 + 16 * (l >> 5));  // < V * H * 2 < 2^32
-
-  // embedding-row staging: thread t copies 16-byte chunk (t % 8) of rows t/8 + 32 i
-  const int gch = tid & 7, grow0 = tid >> 3;
-  // E as one buffer resource: byte offsets are unsigned 32-bit (the host
-  // rejects tables of 4 GiB or more)
-  const uint32_t ebytes = (uint32_t)(V * H * 2);
-  const __amdgpu_buffer_rsrc_t ers =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p.E, (short)0, (int)ebytes, 0x00020000);
-  uint32_t eoff[4];
+  uint32_t woff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = grow0 + 32 * i;
-    const int m = m0 + (r < ncols ? r : 0);
-    eoff[i] = (uint32_t)p.ptok[m] * (uint32_t)H * 2u + 16u * (uint32_t)gch;
+    const int64_t v = vt0 + 8 * (4 * i + w) + (l >> 3);
+    woff[i] = (uint32_t)(((v < V ? v : V - 1) - vt0) * H * 2 + (((l & 7) ^ (l >> 3)) << 4));
   }
+  // E: lane l holds parent column 32 w + l % 32 (clamped to the last parent;
+  // masked later), k half l / 32 of each 16-element MFMA step, through a
+  // buffer resource over the table (byte offsets are unsigned 32-bit: the
+  // host rejects tables of 4 GiB or more; a token past the table reads zeros)
+  int pcol = m0 + 32 * w + (l & 31);
+  pcol = pcol < p.M ? pcol : p.M - 1;
+  const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.E, (short)0, (int)(uint32_t)(V * H * 2), 0x00020000);
+  const uint32_t eoff = (uint32_t)p.ptok[pcol] * (uint32_t)H * 2u + 16u * (uint32_t)(l >> 5);
 
-  const int nks = H / kTsKT;
-  u32x4 wx0[4], wx1[4], wx2[4], gy0[4], gy1[4];
-  auto load_w = [&](u32x4 (&dst)[4], int ks) {
+  // always issue (clamped past the last step): the wait counts stay static
+  auto load_w = [&](int ks) {
+    const int kc = ks < nks ? ks : nks - 1;
+    const int st = ks % kTsStages;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (ts_lds_ptr)&sm.w[st][8 * (4 * i + ws)][0], 16,
+                                               woff[i], kc * kTsKT * 2, 0, 0);
+  };
+  auto load_e = [&](u32x4 (&dst)[4], int ks) {
+    const int kc = ks < nks ? ks : nks - 1;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       dst[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             wrs, (int)woff, ks * kTsKT * 2 + 32 * s, 0));
+                                             ers, (int)eoff, kc * kTsKT * 2 + 32 * s, 0));
   };
-  auto load_g = [&](u32x4 (&dst)[4], int ks) {
+
+  // LDS byte address, in stage 0, of this lane's A fragment for MFMA step s
+  // of vocabulary tile 0 (tile m adds m * 4096): row l % 32, chunk 2 s + l / 32
+  // swizzled by the row's low three bits (row & 7 == l & 7)
+  const uint32_t wbase = (uint32_t)(uintptr_t)(ts_lds_ptr)&sm.w[0][0][0];
+  uint32_t fa[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      dst[i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ers, (int)eoff[i], ks * kTsKT * 2, 0));
-  };
-  auto store_g = [&](const u32x4 (&src)[4], int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4*)&sm.g[buf][grow0 + 32 * i][8 * gch] = src[i];
-  };
-  // Workgroup barrier for the LDS double buffer only: waits for this wave's
-  // LDS traffic, not for its global loads in flight (a full __syncthreads
-  // fence would drain them and undo the prefetch).
-  auto lds_barrier = [&]() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  };
+  for (int s = 0; s < 4; ++s)
+    fa[s] = wbase + (uint32_t)((l & 31) * kTsKT * 2) + (uint32_t)(((2 * s + (l >> 5)) ^ (l & 7)) * 16);
 
   f32x16 acc[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) acc[m][r] = 0.0f;
 
-  // Step ks multiplies W(ks) with the parents' chunk in LDS buffer ks & 1,
-  // issues the loads of W(ks+2) and of the parents' chunk ks+2, and stores
-  // chunk ks+1 (loaded during step ks-1) into the other buffer: two steps of
-  // latency hidden for both streams. Three W and two chunk register sets
-  // rotate by name (six steps unrolled), so no copy waits on a load.
-  auto step = [&](int ks, u32x4 (&wu)[4], u32x4 (&wl)[4], u32x4 (&gs)[4], u32x4 (&gl)[4]) {
-    const int buf = ks & 1;
-    const int kn = ks + 2 < nks ? ks + 2 : nks - 1;  // always issue, so wait counts stay static
-    load_w(wl, kn);
-    load_g(gl, kn);
-    // every B fragment of the step read before the first MFMA, so that the
-    // LDS latency is paid once per step, not once per MFMA
-    u32x4 braw[4][4];
+  // Step ks: wait for this thread's loads of W(ks) and E(ks) (the eight
+  // memory instructions issued since, W(ks + 2) and E(ks + 1), may stay in
+  // flight), barrier (every wave's W(ks) is in LDS, and every wave is done
+  // with the stage W(ks + 3) will overwrite), issue W(ks + 3) and E(ks + 2),
+  // read the step's 16 A fragments in one asm block that waits for them (the
+  // compiler would wait for every direct-to-LDS load in flight before an LDS
+  // read it can see), then the 16 MFMAs.
+  auto step = [&](int ks, u32x4 (&ec)[4], u32x4 (&en)[4]) {
+    // the wait as a builtin, so that the compiler knows E(ks) has arrived and
+    // adds no wait of its own before the MFMAs
+    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8), expcnt and lgkmcnt unrestricted
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // no memory access moves across the barrier
+    load_w(ks + 3);
+    load_e(en, ks + 2);
+    if (active) {
+      const uint32_t sa = (uint32_t)(ks % kTsStages) * (uint32_t)sizeof(sm.w[0]);
+      u32x4 a[4][4];
+      asm volatile(
+          "ds_read_b128 %0, %16\n\t"
+          "ds_read_b128 %1, %16 offset:4096\n\t"
+          "ds_read_b128 %2, %16 offset:8192\n\t"
+          "ds_read_b128 %3, %16 offset:12288\n\t"
+          "ds_read_b128 %4, %17\n\t"
+          "ds_read_b128 %5, %17 offset:4096\n\t"
+          "ds_read_b128 %6, %17 offset:8192\n\t"
+          "ds_read_b128 %7, %17 offset:12288\n\t"
+          "ds_read_b128 %8, %18\n\t"
+          "ds_read_b128 %9, %18 offset:4096\n\t"
+          "ds_read_b128 %10, %18 offset:8192\n\t"
+          "ds_read_b128 %11, %18 offset:12288\n\t"
+          "ds_read_b128 %12, %19\n\t"
+          "ds_read_b128 %13, %19 offset:4096\n\t"
+          "ds_read_b128 %14, %19 offset:8192\n\t"
+          "ds_read_b128 %15, %19 offset:12288\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(a[0][0]), "=&v"(a[1][0]), "=&v"(a[2][0]), "=&v"(a[3][0]),
+            "=&v"(a[0][1]), "=&v"(a[1][1]), "=&v"(a[2][1]), "=&v"(a[3][1]),
+            "=&v"(a[0][2]), "=&v"(a[1][2]), "=&v"(a[2][2]), "=&v"(a[3][2]),
+            "=&v"(a[0][3]), "=&v"(a[1][3]), "=&v"(a[2][3]), "=&v"(a[3][3])
+          : "v"(fa[0] + sa), "v"(fa[1] + sa), "v"(fa[2] + sa), "v"(fa[3] + sa));
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (c < nct)
-          braw[s][c] = *(const u32x4*)&sm.g[buf][c * 32 + (l & 31)][16 * s + 8 * (l >> 5)];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, wu[s]);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (c < nct)
-          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              a, __builtin_bit_cast(bf16x8, braw[s][c]), acc[c], 0, 0, 0);
-      }
+        for (int m = 0; m < 4; ++m)
+          acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, a[m][s]), __builtin_bit_cast(bf16x8, ec[s]), acc[m], 0, 0,
+              0);
+    } else {
+      // consume E(ks) here too, so that on both paths its registers are known
+      // to have arrived before the next loads reuse them (else the compiler
+      // drains every load in flight at the loop's back edge)
+      asm volatile("" ::"v"(ec[0]), "v"(ec[1]), "v"(ec[2]), "v"(ec[3]));
     }
-    if (ks + 1 < nks) store_g(gs, buf ^ 1);
-    lds_barrier();
   };
 
-  load_w(wx0, 0);
-  load_w(wx1, nks > 1 ? 1 : 0);
-  load_g(gy0, 0);
-  load_g(gy1, nks > 1 ? 1 : 0);
-  store_g(gy0, 0);
-  lds_barrier();
-  for (int ks = 0; ks < nks; ks += 6) {
-    step(ks, wx0, wx2, gy1, gy0);
+  u32x4 e0[4], e1[4], e2[4];
+  load_w(0);
+  load_w(1);
+  load_e(e0, 0);
+  load_w(2);
+  load_e(e1, 1);
+  for (int ks = 0; ks < nks; ks += 3) {
+    step(ks, e0, e2);
     if (ks + 1 >= nks) break;
-    step(ks + 1, wx1, wx0, gy0, gy1);
+    step(ks + 1, e1, e0);
     if (ks + 2 >= nks) break;
-    step(ks + 2, wx2, wx1, gy1, gy0);
-    if (ks + 3 >= nks) break;
-    step(ks + 3, wx0, wx2, gy0, gy1);
-    if (ks + 4 >= nks) break;
-    step(ks + 4, wx1, wx0, gy1, gy0);
-    if (ks + 5 >= nks) break;
-    step(ks + 5, wx2, wx1, gy0, gy1);
+    step(ks + 2, e2, e1);
   }
-  __syncthreads();
+  // drain the look-ahead loads (they target LDS this workgroup owns)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (!active) return;
 
-  // ---- epilogue: z = Z + l_d; per column the wave's max, exp sum and top-k
-  // acc[c][r] holds row 8 (r / 4) + 4 (l / 32) + r % 4 of the wave's 32 rows,
-  // column c * 32 + l % 32; lanes l and l ^ 32 share a column.
-  const int64_t vbase = (int64_t)vt * kTsBV + w * 32;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    if (c >= nct) continue;
-    const int col = c * 32 + (l & 31);
-    const bool colok = col < ncols;
-    const int m = m0 + (colok ? col : 0);
-    const int req = m / p.Fd;
-    const uint16_t* lrow = p.bb + ((int64_t)req * p.D + p.d) * V;
-    float z[16];
-    float mx = -INFINITY;
+  // ---- epilogue: z = Z + l_d; per parent column the tile's max, exp sum and
+  // top-k. acc[m][r] holds vocabulary row 32 m + 8 (r / 4) + 4 (l / 32) + r % 4
+  // of the tile and parent column 32 w + l % 32; lanes l and l ^ 32 share a
+  // column. Rows visited in (m, r) order increase.
+  const int col = 32 * w + (l & 31);
+  const bool colok = col < ncols;
+  const int m = m0 + (colok ? col : 0);
+  const int req = m / p.Fd;
+  // the backbone row of the parent's request; rows past V read row V - 1,
+  // and the logit is added after the mask (-inf plus a finite logit) so that
+  // every load is used and all 64 issue unconditionally, back to back
+  const uint16_t* lrow = p.bb + ((int64_t)req * p.D + p.d) * V;
+  // one vocabulary tile's 16 logits per batch of loads, the next batch in
+  // flight while the current one is used
+  uint16_t lb[2][16];
+  auto load_l = [&](uint16_t (&dst)[16], int t) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t v = vbase + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-      const bool ok = v < V;
-      const float lv = __uint_as_float((uint32_t)lrow[ok ? v : V - 1] << 16);  // in-bounds read
-      z[r] = ok ? acc[c][r] + lv : -INFINITY;
-      mx = fmaxf(mx, z[r]);
+      const int64_t v = vt0 + 32 * t + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+      dst[r] = lrow[v < V ? v : V - 1];
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    float s = 0.0f;
+  };
+  float z[64];
+  float mx = -INFINITY;
+  load_l(lb[0], 0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s += z[r] == -INFINITY ? 0.0f : __expf(z[r] - mx);
-    s += __shfl_xor(s, 32);
-    // the lane's best KK of its 16 rows (ids increase with r): the first KK
-    // sorted, the rest inserted; rows past V are empty slots
-    float tv[KK];
-    int ti[KK];
+  for (int t = 0; t < 4; ++t) {
+    if (t + 1 < 4) load_l(lb[(t + 1) & 1], t + 1);
+    asm volatile("" ::: "memory");  // the next batch issued before this one is used
 #pragma unroll
-    for (int r = 0; r < KK; ++r) {
-      const int64_t v = vbase + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-      tv[r] = z[r];
-      ti[r] = v < V ? (int)v : kTsPad;
-    }
-    ts_sort<KK>(tv, ti);
-#pragma unroll
-    for (int r = KK; r < 16; ++r) {
-      const int64_t v = vbase + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-      if (v < V) ts_insert_inc<KK>(tv, ti, z[r], (int)v);
-    }
-    // merge the partner lane's list
-    float ov[KK];
-    int oi[KK];
-#pragma unroll
-    for (int i = 0; i < KK; ++i) {
-      ov[i] = __shfl_xor(tv[i], 32);
-      oi[i] = __shfl_xor(ti[i], 32);
-    }
-    ts_merge_sorted<KK>(tv, ti, ov, oi);
-    if (l < 32) {
-      sm.red.mx[w][col] = mx;
-      sm.red.sm[w][col] = s;
-#pragma unroll
-      for (int i = 0; i < KK; ++i) {
-        sm.red.val[w][col][i] = tv[i];
-        sm.red.id[w][col][i] = ti[i];
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int64_t v = vt0 + 32 * t + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+      const float lv = __uint_as_float((uint32_t)lb[t & 1][r] << 16);
+      z[16 * t + r] = (v < V ? acc[t][r] : -INFINITY) + lv;
+      mx = fmaxf(mx, z[16 * t + r]);
     }
   }
-  __syncthreads();
-  // combine the four waves: one thread per column
-  if (tid < ncols) {
-    const int col = tid;
-    float mx = -INFINITY;
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  float sacc = 0.0f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) mx = fmaxf(mx, sm.red.mx[q][col]);
-    float s = 0.0f;
-    float tv[KK];
-    int ti[KK];
+  for (int q = 0; q < 64; ++q) sacc += z[q] == -INFINITY ? 0.0f : __expf(z[q] - mx);
+  sacc += __shfl_xor(sacc, 32);
+  float tv[KK];
+  int ti[KK];
 #pragma unroll
-    for (int i = 0; i < KK; ++i) {
-      tv[i] = sm.red.val[0][col][i];
-      ti[i] = sm.red.id[0][col][i];
-    }
+  for (int q = 0; q < KK; ++q) {
+    const int64_t v = vt0 + 32 * (q >> 4) + 8 * ((q & 15) >> 2) + 4 * (l >> 5) + (q & 3);
+    tv[q] = z[q];
+    ti[q] = v < V ? (int)v : kTsPad;
+  }
+  ts_sort<KK>(tv, ti);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float mq = sm.red.mx[q][col];
-      if (mq != -INFINITY) s += sm.red.sm[q][col] * __expf(mq - mx);
-      if (q > 0) {
-        float bv[KK];
-        int bi[KK];
+  for (int q = KK; q < 64; ++q) {
+    const int64_t v = vt0 + 32 * (q >> 4) + 8 * ((q & 15) >> 2) + 4 * (l >> 5) + (q & 3);
+    if (v < V) ts_insert_inc<KK>(tv, ti, z[q], (int)v);
+  }
+  float ov[KK];
+  int oi[KK];
 #pragma unroll
-        for (int i = 0; i < KK; ++i) {
-          bv[i] = sm.red.val[q][col][i];
-          bi[i] = sm.red.id[q][col][i];
-        }
-        ts_merge_sorted<KK>(tv, ti, bv, bi);
-      }
-    }
+  for (int i = 0; i < KK; ++i) {
+    ov[i] = __shfl_xor(tv[i], 32);
+    oi[i] = __shfl_xor(ti[i], 32);
+  }
+  ts_merge_sorted<KK>(tv, ti, ov, oi);
+  if (l < 32 && colok) {
     const size_t o = (size_t)vt * p.Mtot + m0 + col;
     p.pmax[o] = mx;
-    p.psum[o] = s;
+    p.psum[o] = sacc;
 #pragma unroll
     for (int i = 0; i < KK; ++i) {
       p.pval[o * kTsKMax + i] = tv[i];
