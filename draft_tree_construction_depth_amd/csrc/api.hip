@@ -257,7 +257,7 @@ struct TsShape {
   int Fmax;        // largest of them
   int cmax;        // candidates per request
   int64_t nvt;     // 128-row tiles of the vocabulary
-  int64_t Mtot;    // partial-record columns (batch * Fmax)
+  int64_t Mtot;    // partial-record parent slots (batch * Fmax); records are [Mtot][nvt]
 };
 
 TsShape ts_shape(int64_t batch, int D, int64_t V, int k, int F) {
@@ -694,6 +694,7 @@ int treespark_expand(const void* backbone, const void* W, const void* E, const i
     gp.Fd = Fd;
     gp.k = sh.kk;
     gp.Mtot = (int32_t)sh.Mtot;
+    gp.nvt = (int32_t)sh.nvt;
     gp.pmax = pmax;
     gp.psum = psum;
     gp.pval = pval;

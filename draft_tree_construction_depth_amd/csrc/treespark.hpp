@@ -19,8 +19,9 @@
 //                   HBM once per depth through an LDS ring; each wave takes
 //                   32 parents' embedding rows straight into registers.
 //  ts_merge_kernel  per request: each parent's log-sum-exp (float64) and
-//                   top-k from the partials; children scored parent score +
-//                   z - lse; the frontier for d+1 = the best F children.
+//                   top-k from the partials (the k best lie in the k tiles
+//                   with the best tile maxima); children scored parent score
+//                   + z - lse; the frontier for d+1 = the best F children.
 // Then ts_pack_kernel ranks every candidate and keeps the best N.
 // Order everywhere: score desc, then rank tuple lexicographic asc, the rank
 // tuple held as 4-bit digits (j + 1) from the top of a 64-bit key so that a
@@ -51,11 +52,12 @@ struct TsGemmParams {
   int64_t V;
   int32_t H, D, d;         // d: 0-based depth
   int32_t M, Fd, k;        // parents, parents per request, branching factor
-  int32_t Mtot;            // column stride of the partial records
-  float* pmax;             // [nvt][Mtot]
-  float* psum;             // [nvt][Mtot] sum of exp(z - pmax)
-  float* pval;             // [nvt][Mtot][kTsKMax] top-k z, best first
-  int32_t* pid;            // [nvt][Mtot][kTsKMax]
+  int32_t Mtot;            // parent slots of the partial records
+  int32_t nvt;             // 128-row vocabulary tiles
+  float* pmax;             // [Mtot][nvt] (parent-major: the merge reads a parent's tiles in a row)
+  float* psum;             // [Mtot][nvt] sum of exp(z - pmax)
+  float* pval;             // [Mtot][nvt][kTsKMax] top-k z, best first
+  int32_t* pid;            // [Mtot][nvt][kTsKMax]
 };
 
 constexpr int kTsPad = 0x7FFFFFFF;  // id of an empty list slot (value -inf)
@@ -348,7 +350,7 @@ __global__ __launch_bounds__(kTsThreads, 2) void ts_gemm_kernel(TsGemmParams p) 
   }
   ts_merge_sorted<KK>(tv, ti, ov, oi);
   if (l < 32 && colok) {
-    const size_t o = (size_t)vt * p.Mtot + m0 + col;
+    const size_t o = (size_t)(m0 + col) * p.nvt + vt;
     p.pmax[o] = mx;
     p.psum[o] = sacc;
 #pragma unroll
@@ -400,9 +402,10 @@ __device__ __forceinline__ uint64_t ts_zkey(float x, int id) {
 }
 
 // One 1024-thread workgroup per request; the four waves of group g merge
-// parents g, g + 4, ...: a pass over the tiles' maxima, then one over their
-// exp sums (float32 terms relative to the parent's maximum, float64 total)
-// and their top-KK lists; groups combine through LDS.
+// parents g, g + 4, ...: one pass over the tiles' maxima, exp sums (float32
+// terms, float64 totals, rescaled to the running maximum) and best entries,
+// which names the k tiles that hold the parent's k best children; only those
+// tiles' lists are then read. Groups combine through LDS.
 constexpr int kTsMergeThreads = 1024;
 constexpr int kTsMergeGroups = 4;
 constexpr int kTsGroupWaves = kTsMergeThreads / kWave / kTsMergeGroups;
@@ -414,6 +417,7 @@ __global__ __launch_bounds__(kTsMergeThreads) void ts_merge_kernel(TsMergeParams
   __shared__ uint64_t ch_key[kTsFMax * kTsKMax];
   __shared__ int32_t ch_cand[kTsFMax * kTsKMax];
   __shared__ double red_d[kTsMergeGroups][kTsGroupWaves];
+  __shared__ float red_m[kTsMergeGroups][kTsGroupWaves];
   __shared__ uint64_t red_k[kTsMergeGroups][kTsGroupWaves][KK];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int g = w / kTsGroupWaves, gw = w - g * kTsGroupWaves;
@@ -431,59 +435,66 @@ __global__ __launch_bounds__(kTsMergeThreads) void ts_merge_kernel(TsMergeParams
     const int i = rd * kTsMergeGroups + g;
     const bool act = i < nf;
     const int m = (int)b * p.Fd + (act ? i : 0);
-    // pass 1: the parent's maximum z
+    // One pass over the parent's tiles: each thread loads, for a batch of its
+    // tiles at once (consecutive in memory for consecutive threads), the
+    // tile's maximum, exp sum and best entry, and keeps its own maximum, its
+    // exp sum relative to that and its KK best tile-best keys. The parent's k
+    // best entries all lie in the k tiles with the best tile-best keys (any
+    // tile holding one of them has a best key at least the k-th best overall,
+    // which is at least the k-th best of those k distinct tile bests), so only
+    // those tiles' lists are read afterwards.
+    constexpr int TB = 8;  // tiles per thread per batch
+    const size_t pb = (size_t)m * p.nvt;
     float mx = -INFINITY;
-    for (int t = gt; t < p.nvt; t += GT) mx = fmaxf(mx, p.pmax[(size_t)t * p.Mtot + m]);
-    mx = wave_max(mx);
-    if (lane == 0) red_d[g][gw] = mx;
-    __syncthreads();
-    float M = -INFINITY;
-#pragma unroll
-    for (int q = 0; q < kTsGroupWaves; ++q) M = fmaxf(M, (float)red_d[g][q]);
-    __syncthreads();
-    // pass 2: exp sums and top-KK lists
     double s = 0.0;
-    float tv[KK];
-    int ti[KK];
+    uint64_t tk[KK];  // this thread's best tile keys, best first (0 = none)
 #pragma unroll
-    for (int j = 0; j < KK; ++j) {
-      tv[j] = -INFINITY;
-      ti[j] = 0x7FFFFFFF;
-    }
-    for (int t = gt; t < p.nvt; t += GT) {
-      const size_t o = (size_t)t * p.Mtot + m;
-      const float x = p.pmax[o];
-      const float y = p.psum[o];
-      float pv[KK];
-      int pi[KK];
+    for (int j = 0; j < KK; ++j) tk[j] = 0;
+    for (int t0 = 0; t0 < p.nvt; t0 += TB * GT) {
+      float bx[TB], by[TB], bv[TB];
+      int bi[TB];
 #pragma unroll
-      for (int j = 0; j < KK; ++j) {
-        pv[j] = p.pval[o * kTsKMax + j];
-        pi[j] = p.pid[o * kTsKMax + j];
+      for (int u = 0; u < TB; ++u) {
+        const int t = t0 + u * GT + gt;
+        const bool ok = t < p.nvt;
+        const size_t o = pb + (ok ? t : 0);
+        bx[u] = ok ? p.pmax[o] : -INFINITY;
+        by[u] = ok ? p.psum[o] : 0.0f;
+        bv[u] = ok ? p.pval[o * kTsKMax] : -INFINITY;
+        bi[u] = ok ? p.pid[o * kTsKMax] : 0x7FFFFFFF;
       }
-      if (x != -INFINITY) s += (double)(y * __expf(x - M));
+      float bm = mx;
 #pragma unroll
-      for (int j = 0; j < KK; ++j) {
-        if (j < K && pi[j] != 0x7FFFFFFF) {
-          // (val, id) into the sorted list, branch-free
-          const float xv = pv[j];
-          const int id = pi[j];
-          bool bt[KK];
+      for (int u = 0; u < TB; ++u) bm = fmaxf(bm, bx[u]);
+      if (bm != -INFINITY) {
+        if (mx != -INFINITY && bm != mx) s *= (double)__expf(mx - bm);
 #pragma unroll
-          for (int q = 0; q < KK; ++q) bt[q] = q < K && (xv > tv[q] || (xv == tv[q] && id < ti[q]));
+        for (int u = 0; u < TB; ++u)
+          if (bx[u] != -INFINITY) s += (double)(by[u] * __expf(bx[u] - bm));
+        mx = bm;
+      }
 #pragma unroll
-          for (int q = KK - 1; q >= 0; --q) {
-            const bool sh = q > 0 && bt[q > 0 ? q - 1 : 0];
-            const float v1 = q > 0 ? tv[q > 0 ? q - 1 : 0] : xv;
-            const int i1 = q > 0 ? ti[q > 0 ? q - 1 : 0] : id;
-            tv[q] = sh ? v1 : (bt[q] ? xv : tv[q]);
-            ti[q] = sh ? i1 : (bt[q] ? id : ti[q]);
-          }
+      for (int u = 0; u < TB; ++u) {
+        // the tile's best key into the sorted list (keys are unique)
+        const uint64_t x = bi[u] != 0x7FFFFFFF ? ts_zkey(bv[u], bi[u]) : 0ull;
+#pragma unroll
+        for (int q = KK - 1; q >= 0; --q) {
+          const bool above = q > 0 && x > tk[q > 0 ? q - 1 : 0];
+          tk[q] = above ? tk[q > 0 ? q - 1 : 0] : (x > tk[q] ? x : tk[q]);
         }
       }
     }
+    // the group's maximum, then every thread's sum rescaled to it
+    const float wm = wave_max(mx);
+    if (lane == 0) red_m[g][gw] = wm;
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kTsGroupWaves; ++q) M = fmaxf(M, red_m[g][q]);
+    if (mx != -INFINITY) s *= (double)__expf(mx - M);
     s = wave_sum(s);
-    // the group's top-KK: KK rounds of a max over each lane's best untaken key
+    // the wave's KK best tile keys: KK rounds of a max over each lane's best
+    // untaken key
     int head = 0;
     uint64_t wbest[KK];
 #pragma unroll
@@ -491,7 +502,7 @@ __global__ __launch_bounds__(kTsMergeThreads) void ts_merge_kernel(TsMergeParams
       uint64_t mine = 0;
 #pragma unroll
       for (int j = 0; j < KK; ++j)
-        if (j == head && ti[j] != 0x7FFFFFFF) mine = ts_zkey(tv[j], ti[j]);
+        if (j == head) mine = tk[j];
       const uint64_t best = wave_max(mine);
       if (mine == best && best != 0) ++head;
       wbest[r] = best;
@@ -502,35 +513,60 @@ __global__ __launch_bounds__(kTsMergeThreads) void ts_merge_kernel(TsMergeParams
       for (int r = 0; r < KK; ++r) red_k[g][gw][r] = wbest[r];
     }
     __syncthreads();
-    if (act && gw == 0 && lane < K) {
-      // lane r picks the r-th best of the group's waves' lists (keys unique)
-      uint64_t all[kTsGroupWaves * KK];
+    if (act && gw == 0) {
+      // lane r < K takes the r-th best tile of the group (keys unique)
+      uint64_t tile_key = 0;
+      if (lane < K) {
+        uint64_t all[kTsGroupWaves * KK];
 #pragma unroll
-      for (int q = 0; q < kTsGroupWaves; ++q)
+        for (int q = 0; q < kTsGroupWaves; ++q)
 #pragma unroll
-        for (int r = 0; r < KK; ++r) all[q * KK + r] = red_k[g][q][r];
+          for (int r = 0; r < KK; ++r) all[q * KK + r] = red_k[g][q][r];
+        for (int r = 0; r <= lane; ++r) {
+          uint64_t bst = 0;
+#pragma unroll
+          for (int q = 0; q < kTsGroupWaves * KK; ++q) {
+            const uint64_t x = all[q];
+            if (x > bst && (r == 0 || x < tile_key)) bst = x;
+          }
+          tile_key = bst;
+        }
+      }
+      // lane q < K * K reads entry q % K of the (q / K)-th best tile's list;
+      // then K rounds of a wave maximum give the parent's k best, lane r
+      // keeping the r-th
+      uint64_t cand = 0;
+      {
+        const int r = lane / K, j = lane - r * K;
+        const uint64_t tkr = (uint64_t)(uint32_t)__shfl((int)(tile_key >> 32), r) << 32 |
+                             (uint32_t)__shfl((int)(uint32_t)tile_key, r);
+        if (lane < K * K && tkr != 0) {
+          const int tile = (int)((0xFFFFFFFFu - (uint32_t)tkr) / (uint32_t)kTsBV);
+          const size_t o = pb + tile;
+          const int id = p.pid[o * kTsKMax + j];
+          if (id != 0x7FFFFFFF) cand = ts_zkey(p.pval[o * kTsKMax + j], id);
+        }
+      }
+      uint64_t pick = 0;
+      for (int r = 0; r < K; ++r) {
+        const uint64_t best = wave_max(cand);
+        if (cand == best) cand = 0;
+        if (lane == r) pick = best;
+      }
       double tot = 0.0;
 #pragma unroll
       for (int q = 0; q < kTsGroupWaves; ++q) tot += red_d[g][q];
       const double lse = (double)M + log(tot);
-      uint64_t pick = 0;
-      for (int r = 0; r <= lane; ++r) {
-        uint64_t bst = 0;
-#pragma unroll
-        for (int q = 0; q < kTsGroupWaves * KK; ++q) {
-          const uint64_t x = all[q];
-          if (x > bst && (r == 0 || x < pick)) bst = x;
-        }
-        pick = bst;
+      if (lane < K) {
+        const int pc = st.pcand[par][m];
+        const double pscore = pc < 0 ? 0.0 : st.cscore[b * st.cmax + pc];
+        const uint64_t pkey = pc < 0 ? 0ull : st.ckey[b * st.cmax + pc];
+        const int c = i * K + lane;
+        ch_tok[c] = (int32_t)(0xFFFFFFFFu - (uint32_t)pick);
+        ch_score[c] = pscore + ((double)key_value((uint32_t)(pick >> 32)) - lse);
+        ch_key[c] = pkey | ((uint64_t)(lane + 1) << shift);
+        ch_cand[c] = pc;
       }
-      const int pc = st.pcand[par][m];
-      const double pscore = pc < 0 ? 0.0 : st.cscore[b * st.cmax + pc];
-      const uint64_t pkey = pc < 0 ? 0ull : st.ckey[b * st.cmax + pc];
-      const int c = i * K + lane;
-      ch_tok[c] = (int32_t)(0xFFFFFFFFu - (uint32_t)pick);
-      ch_score[c] = pscore + ((double)key_value((uint32_t)(pick >> 32)) - lse);
-      ch_key[c] = pkey | ((uint64_t)(lane + 1) << shift);
-      ch_cand[c] = pc;
     }
     __syncthreads();
   }
