@@ -245,7 +245,7 @@ int launch_select(const float* vals, const int32_t* ids, const double* lse, int6
   sp.sp_lp = nullptr;
   sp.sp_best = nullptr;
   sp.sp_blp = nullptr;
-  hipLaunchKernelGGL(ddt::select_kernel, dim3((unsigned)batch), dim3(ddt::kSelThreads), 0, stream,
+  hipLaunchKernelGGL(ddt::select_kernel, dim3((unsigned)batch), dim3(ddt::kSelNT), 0, stream,
                      sp);
   return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
 }

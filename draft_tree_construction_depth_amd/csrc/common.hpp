@@ -108,20 +108,24 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
-// Sum of the first w of NW per-wave totals in LDS (16-byte aligned, NW a
-// multiple of 4), read four at a time; total gets the sum of all NW.
+// Sum of the first w of NW <= 16 per-wave totals in LDS (16-byte aligned);
+// total gets the sum of all NW. Lane l < NW reads total l, a DPP scan inside
+// the first row of 16 lanes forms the prefixes, and two readlanes at the
+// wave's own (uniform) index pick them: no per-wave-index selects. Every
+// lane of the wave must be active.
 template <int NW>
 __device__ __forceinline__ int waves_before(const int* wsum, int w, int& total) {
-  static_assert(NW % 4 == 0, "int4 reads of the wave totals");
-  int pre = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < NW; i += 4) {
-    const int4 t = *(const int4*)&wsum[i];
-    pre += (i < w ? t.x : 0) + (i + 1 < w ? t.y : 0) + (i + 2 < w ? t.z : 0) + (i + 3 < w ? t.w : 0);
-    tot += t.x + t.y + t.z + t.w;
-  }
-  total = tot;
-  return pre;
+  static_assert(NW % 4 == 0 && NW <= 16, "at most 16 waves, int4-aligned totals");
+  const int lane = threadIdx.x & 63;
+  int x = lane < NW ? wsum[lane] : 0;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  const int ws = __builtin_amdgcn_readfirstlane(w);
+  total = __builtin_amdgcn_readlane(x, NW - 1);
+  const int pre = __builtin_amdgcn_readlane(x, ws > 0 ? ws - 1 : 0);
+  return ws > 0 ? pre : 0;
 }
 
 // Exclusive scan of one int per thread over the block (every thread calls

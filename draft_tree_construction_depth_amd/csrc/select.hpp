@@ -59,9 +59,12 @@
 
 namespace ddt {
 
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = 1024;  // conditioned-row selection's workgroup
 constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kSelNT = 1024;  // independent-row selection's workgroup
+constexpr int kSelBins = 1024;  // histogram bins of the threshold and the ordering
 constexpr int kECap = 2048;
+static_assert(kECap / kSelNT >= 2, "two entries per thread at least");
 constexpr int kSelRetries = 3;  // threshold raises after an enumeration overflow
 constexpr int kMaxLK = 8192;
 constexpr int kMaxL = 32;
@@ -137,8 +140,8 @@ struct SelectSmem {
   int kexc;  // entries before the threshold's bin
   int n2;
   int kcut;
-  int hist[kSelThreads];
-  int hexc[kSelThreads];  // entries in the bins before each bin
+  alignas(16) int hist[kSelBins];
+  int hexc[kSelBins];  // entries in the bins before each bin
   double tau;
   int nE;
   int ovf;
@@ -254,7 +257,7 @@ __device__ void heap_fallback(const SelectParams& p, SelectSmem& sm, int64_t b) 
 // s_d(r) = min(sig_d, P0_d + v_d[r] - Z_d) do not increase with r. Lower
 // bound mn: the q-th score of every row, q = min(ceil(B / L), K), leaves
 // >= B scores at or above the smallest of them. The scores in [mn, best]
-// fall into kSelThreads bins (index monotone in the score, equal scores share
+// fall into kSelBins bins (index monotone in the score, equal scores share
 // a bin); one scan finds the bin holding the B-th, whose few members are
 // ranked exactly. Members beyond kMergeCap (flat rows) return mn instead, a
 // valid lower bound.
@@ -266,13 +269,17 @@ __device__ void heap_fallback(const SelectParams& p, SelectSmem& sm, int64_t b) 
 // the B-th, moved down by a millionth of a bin: at or below every member of
 // that bin, so a valid lower bound with the same guarantee, found without
 // ranking the bin (a slightly larger E to enumerate).
-template <bool EXACT = true, class OD, class LB>
+// With PRE the caller has already cleared the histogram and stored the lower
+// bound in sm.tau, before a barrier (lane_bound is then unused).
+template <bool EXACT = true, int NT = kSelThreads, bool PRE = false, class OD, class LB>
 __device__ double sel_tau_hist(SelectSmem& sm, int LK, int B, OD onedev, LB lane_bound,
                                double* mem = nullptr, int memcap = kMergeCap) {
+  constexpr int NW = NT / kWave, BPT = kSelBins / NT;  // bins per thread in the scan
+  static_assert(BPT * NT == kSelBins, "whole bins per thread");
   if (mem == nullptr) mem = sm.u.mt.a;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  sm.hist[tid] = 0;
-  if (w == 0) {
+  if (!PRE) for (int j = tid; j < kSelBins; j += NT) sm.hist[j] = 0;
+  if (!PRE && w == 0) {
     double x = lane_bound(lane);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -284,38 +291,49 @@ __device__ double sel_tau_hist(SelectSmem& sm, int LK, int B, OD onedev, LB lane
       sm.n2 = 0;
     }
   }
-  __syncthreads();
+  if (!PRE) __syncthreads();
   const double mn = sm.tau, top = sm.sig[1];
   const double span = top - mn;
-  const double scale = span > 0.0 ? (double)kSelThreads / span : 0.0;
+  const double scale = span > 0.0 ? (double)kSelBins / span : 0.0;
   auto bin_of = [&](double sc) -> int {
     const double t = (top - sc) * scale;
-    return t >= (double)(kSelThreads - 1) ? kSelThreads - 1 : (t > 0.0 ? (int)t : 0);
+    return t >= (double)(kSelBins - 1) ? kSelBins - 1 : (t > 0.0 ? (int)t : 0);
   };
-  for (int i = tid; i < LK; i += kSelThreads) {
+  for (int i = tid; i < LK; i += NT) {
     const double sc = onedev(i);
     if (sc >= mn) atomicAdd(&sm.hist[bin_of(sc)], 1);
   }
   __syncthreads();
-  const int h = sm.hist[tid];
-  const int x = wave_incl_scan(h);
+  // scan: this thread's BPT consecutive bins, then the waves' totals
+  int h[BPT], hs = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    h[j] = sm.hist[tid * BPT + j];
+    hs += h[j];
+  }
+  const int x = wave_incl_scan(hs);
   if (lane == kWave - 1) sm.wsum[w] = x;
   __syncthreads();
   int tot;
-  const int inc = waves_before<kSelWaves>(sm.wsum, w, tot) + x, exc = inc - h;
-  if (inc >= B && exc < B) {
-    sm.kcut = tid;
-    sm.kexc = exc;
+  int run = waves_before<NW>(sm.wsum, w, tot) + x - hs;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    const int exc = run;
+    run += h[j];
+    if (run >= B && exc < B) {
+      sm.kcut = tid * BPT + j;
+      sm.kexc = exc;
+    }
   }
   __syncthreads();
   if constexpr (!EXACT) {
     const int kc = sm.kcut;
-    if (!(scale > 0.0) || kc >= kSelThreads - 1) return mn;
+    if (!(scale > 0.0) || kc >= kSelBins - 1) return mn;
     const double edge = top - ((double)kc + 1.000001) / scale;
     return edge > mn ? edge : mn;
   }
   const int kb = sm.kcut, t = B - 1 - sm.kexc;  // the B-th is member t of bin kb
-  for (int i = tid; i < LK; i += kSelThreads) {
+  for (int i = tid; i < LK; i += NT) {
     const double sc = onedev(i);
     if (sc >= mn && bin_of(sc) == kb) {
       const int k = atomicAdd(&sm.n2, 1);
@@ -325,7 +343,7 @@ __device__ double sel_tau_hist(SelectSmem& sm, int LK, int B, OD onedev, LB lane
   __syncthreads();
   const int m = sm.n2;
   if (m > memcap) return mn;
-  for (int k = tid; k < m; k += kSelThreads) {
+  for (int k = tid; k < m; k += NT) {
     const double v = mem[k];
     int gt = 0, ge = 0;
     for (int j = 0; j < m; ++j) {
@@ -343,15 +361,17 @@ __device__ double sel_tau_hist(SelectSmem& sm, int LK, int B, OD onedev, LB lane
 // Phase 3 (after an enumeration without overflow): order E, emit the
 // first B (tokens, parents, log-probs, depths, node count). en.eRank holds
 // each entry's index into its row's candidate table.
-template <bool ZERO_HIST = true>
+template <bool ZERO_HIST = true, int NT = kSelThreads>
 __device__ __forceinline__ void sel_order_emit(const SelectParams& p, SelectSmem& sm, int64_t b,
                                                double tau) {
+  constexpr int NPT = kECap / NT, NW = NT / kWave, BPT = kSelBins / NT;
+  static_assert(NPT * NT == kECap && BPT * NT == kSelBins, "whole entries and bins per thread");
   SelEnum& en = sm.u.en;
   const int tid = threadIdx.x;
   const int L = p.L, K = p.K, B = p.B, LK = L * K;
   (void)L;
   // ---- 3. order E, emit the first B ----------------------------------------
-  // E's scores fall into kSelThreads bins over [tau, best] (bin index
+  // E's scores fall into kSelBins bins over [tau, best] (bin index
   // monotone in the score, so equal scores share a bin and a lower bin
   // holds only better scores). E2 = the entries of the first bins that
   // hold >= B of them (all of E when nE <= B); it is closed upwards in the
@@ -359,48 +379,56 @@ __device__ __forceinline__ void sel_order_emit(const SelectParams& p, SelectSmem
   // entry's position is its bin's offset plus the members of its own bin
   // before it (score, then the 128-bit lexicographic rank key).
   const int nE = sm.nE;
-  static_assert(kECap <= 2 * kSelThreads, "two entries per thread at most");
   // token ids of this thread's entries, loaded now so that the ordering's
   // barriers cover the global-load latency
-  int etok[2];
+  int etok[NPT];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int i = tid + k * kSelThreads;
+  for (int k = 0; k < NPT; ++k) {
+    const int i = tid + k * NT;
     etok[k] = i < nE ? p.ids[(size_t)b * LK + (size_t)(en.eDep[i] - 1) * K + en.eRank[i]] : -1;
   }
   const double top = sm.sig[1];  // the best prefix: depth 1, rank 0
   const double span = top - tau;
-  const double scale = span > 0.0 ? (double)kSelThreads / span : 0.0;
+  const double scale = span > 0.0 ? (double)kSelBins / span : 0.0;
   auto bin_of = [&](double sc) -> int {
     const double t = (top - sc) * scale;
-    return t >= (double)(kSelThreads - 1) ? kSelThreads - 1 : (t > 0.0 ? (int)t : 0);
+    return t >= (double)(kSelBins - 1) ? kSelBins - 1 : (t > 0.0 ? (int)t : 0);
   };
   if constexpr (ZERO_HIST) {
-    sm.hist[tid] = 0;
+    for (int j = tid; j < kSelBins; j += NT) sm.hist[j] = 0;
     __syncthreads();
   }
-  int ebin[2];
+  int ebin[NPT];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int i = tid + k * kSelThreads;
-    ebin[k] = i < nE ? bin_of(en.eSc[i]) : kSelThreads;
+  for (int k = 0; k < NPT; ++k) {
+    const int i = tid + k * NT;
+    ebin[k] = i < nE ? bin_of(en.eSc[i]) : kSelBins;
     if (i < nE) atomicAdd(&sm.hist[ebin[k]], 1);
   }
   __syncthreads();
   {
-    const int h = sm.hist[tid];
-    const int x = wave_incl_scan(h);
+    // scan: this thread's BPT consecutive bins, then the waves' totals
+    int h[BPT], hs = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      h[j] = sm.hist[tid * BPT + j];
+      hs += h[j];
+    }
+    const int x = wave_incl_scan(hs);
     const int lane = tid & 63, w = tid >> 6;
     if (lane == kWave - 1) sm.wsum[w] = x;
     __syncthreads();
     int tot;
-    const int inc = waves_before<kSelWaves>(sm.wsum, w, tot) + x, exc = inc - h;
-    // the first bin reaching B is the cut (the last bin when nE <= B)
-    if (nE > B ? (inc >= B && exc < B) : tid == kSelThreads - 1) {
-      sm.kcut = tid;
+    int run = waves_before<NW>(sm.wsum, w, tot) + x - hs;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      const int bin = tid * BPT + j, exc = run;
+      run += h[j];
+      // the first bin reaching B is the cut (the last bin when nE <= B)
+      if (nE > B ? (run >= B && exc < B) : bin == kSelBins - 1) sm.kcut = bin;
+      sm.hexc[bin] = exc;
+      sm.hist[bin] = 0;  // now the bins' fill counters (only this thread read it)
     }
-    sm.hexc[tid] = exc;
-    sm.hist[tid] = 0;  // now the bins' fill counters (only this thread read it)
   }
   __syncthreads();
   const int kcut = sm.kcut;
@@ -410,10 +438,10 @@ __device__ __forceinline__ void sel_order_emit(const SelectParams& p, SelectSmem
   uint64_t* h2 = (uint64_t*)sm.v;
   uint64_t* l2 = h2 + kECap;
   static_assert(2 * kECap * sizeof(uint64_t) <= sizeof(sm.v), "rank keys fit the row table");
-  int epos[2];
+  int epos[NPT];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int i = tid + k * kSelThreads;
+  for (int k = 0; k < NPT; ++k) {
+    const int i = tid + k * NT;
     epos[k] = -1;
     if (i < nE && ebin[k] <= kcut) {
       const int q = sm.hexc[ebin[k]] + atomicAdd(&sm.hist[ebin[k]], 1);
@@ -425,18 +453,31 @@ __device__ __forceinline__ void sel_order_emit(const SelectParams& p, SelectSmem
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int i = tid + k * kSelThreads;
+  for (int k = 0; k < NPT; ++k) {
+    const int i = tid + k * NT;
     if (epos[k] >= 0) {
       const int bb = ebin[k], me = epos[k];
-      const int lo = sm.hexc[bb], hi = bb + 1 < kSelThreads ? sm.hexc[bb + 1] : nE;
+      const int lo = sm.hexc[bb], hi = bb + 1 < kSelBins ? sm.hexc[bb + 1] : nE;
       const double si = s2[me];
       const uint64_t hi_i = h2[me], lo_i = l2[me];
       int rank = lo;
-      for (int q = lo; q < hi; ++q) {
-        const double sq = s2[q];
-        const uint64_t hq = h2[q], lq = l2[q];
-        rank += (sq > si || (sq == si && (hq < hi_i || (hq == hi_i && lq < lo_i)))) ? 1 : 0;
+      // the bin's members four at a time, their loads issued together (an
+      // index past the bin reads this entry itself, which never precedes it)
+      for (int q = lo; q < hi; q += 4) {
+        double sq[4];
+        uint64_t hq[4], lq[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int qq = q + j < hi ? q + j : me;
+          sq[j] = s2[qq];
+          hq[j] = h2[qq];
+          lq[j] = l2[qq];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          rank += (sq[j] > si || (sq[j] == si && (hq[j] < hi_i || (hq[j] == hi_i && lq[j] < lo_i))))
+                      ? 1
+                      : 0;
       }
       en.cnt[i] = rank;
     }
@@ -444,8 +485,8 @@ __device__ __forceinline__ void sel_order_emit(const SelectParams& p, SelectSmem
   __syncthreads();
   const int nsel = nE < B ? nE : B;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int i = tid + k * kSelThreads;
+  for (int k = 0; k < NPT; ++k) {
+    const int i = tid + k * NT;
     if (epos[k] >= 0) {
       const int j = en.cnt[i];
       if (j < nsel) {
@@ -461,7 +502,7 @@ __device__ __forceinline__ void sel_order_emit(const SelectParams& p, SelectSmem
       }
     }
   }
-  for (int j = nsel + tid; j < B; j += kSelThreads) {
+  for (int j = nsel + tid; j < B; j += NT) {
     const size_t o = (size_t)b * B + j;
     p.tree_tokens[o] = -1;
     p.parents[o] = -1;
@@ -501,63 +542,134 @@ __device__ __forceinline__ void sel_mask_rows(const SelectParams& p, const int* 
   }
 }
 
+template <int NT = kSelThreads>
 __device__ __forceinline__ void sel_mask(const SelectParams& p, SelectSmem& sm, int64_t b) {
-  sel_mask_rows(p, sm.opar, sm.nsel, b);
+  sel_mask_rows<NT>(p, sm.opar, sm.nsel, b);
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
+// Inclusive scan over the wave of op(a, b) = (b > a ? a : b), a from the
+// earlier lanes: the running minimum in which a later equal value replaces
+// an earlier one. By DPP, in the order of the integer scan above (shifts by
+// 1, 2, 4, 8 inside rows, then row broadcasts); a lane without a partner
+// sees +inf. For non-NaN values op is associative, so every lane gets the
+// left-to-right fold's value bit for bit.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64_or_inf(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROWS, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)0x7FF00000, (int)(uint32_t)(u >> 32),
+                                                            CTRL, ROWS, 0xf, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double wave_runmin_scan(double x) {
+  auto op = [](double a, double b) { return b > a ? a : b; };
+  x = op(dpp_f64_or_inf<0x111, 0xf>(x), x);  // row_shr:1
+  x = op(dpp_f64_or_inf<0x112, 0xf>(x), x);  // row_shr:2
+  x = op(dpp_f64_or_inf<0x114, 0xf>(x), x);  // row_shr:4
+  x = op(dpp_f64_or_inf<0x118, 0xf>(x), x);  // row_shr:8
+  x = op(dpp_f64_or_inf<0x142, 0xa>(x), x);  // row_bcast:15
+  x = op(dpp_f64_or_inf<0x143, 0xc>(x), x);  // row_bcast:31
+  return x;
+}
+
+__global__ __launch_bounds__(kSelNT) void select_kernel(SelectParams p) {
+  constexpr int NT = kSelNT, NW = NT / kWave, NPT = kECap / NT;
+  static_assert(NPT * NT == kECap, "whole entries per thread");
   __shared__ SelectSmem sm;
   SelEnum& en = sm.u.en;
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.x;
   const int L = p.L, K = p.K, B = p.B, LK = L * K, bpd = p.bpd;
   const float* vals = p.vals + (size_t)b * LK;
+  // the threshold's lower-bound rank: the q1-th one-deviation score of every
+  // row, q1 = min(ceil(B / L), K), leaves >= B scores at or above the smallest
+  const int q1 = (B + L - 1) / L < K ? (B + L - 1) / L : K;  // in [1, K]
 
   if (tid < kWave) {
-    // Z_d and the spine (all ranks 0): float64, left to right, in wave 0's
-    // registers while the other waves stage the table; four rows' values
-    // are read across lanes per step, so only the additions are serial
+    // Z_d and the spine (all ranks 0), float64, in wave 0's registers while
+    // the other waves stage the table. Lane d sums rows 0..d-1 itself, left
+    // to right, so every lane gets its own prefix with the additions of the
+    // serial definition; the chain is unrolled over the first rows, whose
+    // values every lane loads (same addresses across the wave), and the
+    // lanes past their own row sit out the additions.
     const int lane = tid;
-    // lane d holds row d's normaliser, top value and last value
-    const double zl = lane < L ? p.lse[(size_t)b * L + lane] : 0.0;
-    const float vl = lane < L ? vals[(size_t)lane * K] : 0.0f;
-    const float vk = lane < L ? vals[(size_t)lane * K + K - 1] : 0.0f;
-    double acc = 0.0, S = 0.0, sc = 0.0, myZ = 0.0, myP = 0.0, mySig = 0.0;
-    double zmax = 0.0, sabs = 0.0;  // magnitude bounds of every Z_d and every S
-    for (int d0 = 0; d0 < L; d0 += 4) {
-      double z4[4];
-      float v4[4], w4[4];
+    // lane d holds row d's normaliser, top value, last value and rank-q1
+    // value (four loads issued together: clamped addresses, no branches)
+    const int lc = lane < L ? lane : 0;
+    const double zl0 = p.lse[(size_t)b * L + lc];
+    const float* vrow = vals + (size_t)lc * K;
+    const float vl0 = vrow[0], vk0 = vrow[K - 1], vq0 = vrow[q1 - 1];
+    const double zl = lane < L ? zl0 : 0.0;
+    const float vl = lane < L ? vl0 : 0.0f, vk = lane < L ? vk0 : 0.0f;
+    const float vq = lane < L ? vq0 : 0.0f;
+    constexpr int kPre = 15;  // rows whose values every lane holds
+    double zr[kPre];
+    float vr[kPre];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        z4[q] = lane_value(zl, d0 + q);  // d0 + q < kMaxL + 4 <= 64
-        v4[q] = lane_value(vl, d0 + q);
-        w4[q] = lane_value(vk, d0 + q);
+    for (int j = 0; j < kPre; ++j) {
+      const int jj = j < L ? j : 0;  // rows past L only reach lanes past L
+      zr[j] = p.lse[(size_t)b * L + jj];
+      vr[j] = vals[(size_t)jj * K];
+    }
+    double Zx = 0.0, Sx = 0.0;  // rows < d
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {
+      if (j < lane) {
+        Zx += zr[j];
+        Sx += (double)vr[j];
       }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (d0 + q < L) {
-          acc += z4[q];
-          S += (double)v4[q];
-          const double raw = S - acc;
-          sc = raw > sc ? sc : raw;
-          zmax = fmax(zmax, fabs(acc));
-          sabs += (double)fmaxf(fabsf(v4[q]), fabsf(w4[q]));
-          if (lane == d0 + q) {
-            myZ = acc;
-            myP = S;
-            mySig = sc;
-          }
-        }
+    }
+    for (int j = kPre; j < L - 1; ++j) {  // deeper trees: broadcast by readlane
+      const double zj = lane_value(zl, j);
+      const double vj = (double)lane_value(vl, j);
+      if (j < lane) {
+        Zx += zj;
+        Sx += vj;
+      }
+    }
+    const double Zi = Zx + zl, Si = Sx + (double)vl;  // rows <= d: Z_d, P0[d+1]
+    const double raw = lane < L ? Si - Zi : INFINITY;
+    // spine scores sig[d+1] = the running minimum of 0, raw_0 .. raw_d (a
+    // later equal value replaces an earlier one): a DPP scan when no score
+    // is NaN (the operation is then associative), else serially
+    double sg;
+    if (__ballot(raw != raw) == 0) {
+      sg = wave_runmin_scan(raw);
+      sg = sg > 0.0 ? 0.0 : sg;
+    } else {
+      double sc = 0.0;
+      sg = 0.0;
+      for (int j = 0; j < L; ++j) {
+        const double r = lane_value(raw, j);
+        sc = r > sc ? sc : r;
+        if (lane == j) sg = sc;
       }
     }
     // every row's top log-probability below -M, M far above the rounding of
-    // any score (a difference of sums of magnitude <= zmax + sabs)
-    const double M = 1e-12 * (1.0 + zmax + sabs);
+    // any score (a difference of sums of magnitude <= the sum of every |Z_d|
+    // and every row's largest |value|)
+    const double mag = wave_sum(lane < L ? fabs(Zi) + (double)fmaxf(fabsf(vl), fabsf(vk)) : 0.0);
+    const double M = 1e-12 * (1.0 + mag);
     const uint64_t ok = __ballot(lane >= L || (double)vl - zl < -M);
+    if (LK >= B) {
+      // the threshold's lower bound: the smallest rank-q one-deviation score
+      // over the rows (the same arithmetic as the histogram's)
+      double sgx = __shfl_up(sg, 1);  // sig[d]
+      sgx = lane == 0 ? 0.0 : sgx;
+      const double r1 = (Sx + (double)vq) - Zi;
+      const double od = lane < L ? (r1 > sgx ? sgx : r1) : INFINITY;
+      const double mn = wave_min(od);
+      if (lane == 0) {
+        sm.tau = mn;
+        sm.n2 = 0;
+      }
+    }
     if (lane < L) {
-      sm.Z[lane] = myZ;
-      sm.P0[lane + 1] = myP;
-      sm.sig[lane + 1] = mySig;
+      sm.Z[lane] = Zi;
+      sm.P0[lane + 1] = Si;
+      sm.sig[lane + 1] = sg;
     }
     if (lane == 0) {
       sm.P0[0] = 0.0;
@@ -565,20 +677,31 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
       sm.nE = 0;
       sm.ovf = 0;
       sm.f2 = ok == ~0ull ? 1 : 0;
+      sm.wbad[0] = 0;
     }
-  }
-  {
-    // exact-sum window: every nonzero value's exponent within 11 of the
+  } else {
+    // waves 1..: stage the table, clear the threshold's histogram, and check
+    // the exact-sum window: every nonzero value's exponent within 11 of the
     // first row's top value's (denormals count as exponent 1)
+    constexpr int NS = NT - kWave;  // staging threads
     const int eref = (int)((__float_as_uint(vals[0]) >> 23) & 0xFFu);
     bool bad = false;
-    for (int i = tid; i < LK; i += kSelThreads) {
-      const float v = vals[i];
-      sm.v[i] = v;
+    auto check = [&](float v) {
       int e = (int)((__float_as_uint(v) >> 23) & 0xFFu);
       e = e == 0 ? 1 : e;
       bad |= v != 0.0f && (e == 255 || e < eref - 11 || e > eref + 11);
+    };
+    // two values per thread per step, both loads in flight together
+    for (int i = tid - kWave; i < LK; i += 2 * NS) {
+      const bool two = i + NS < LK;
+      const float v0 = vals[i], v1 = vals[two ? i + NS : i];
+      __builtin_amdgcn_sched_barrier(0);  // both loads issued before the first store
+      sm.v[i] = v0;
+      if (two) sm.v[i + NS] = v1;
+      check(v0);
+      check(v1);
     }
+    for (int j = tid - kWave; j < kSelBins; j += NT - kWave) sm.hist[j] = 0;
     const uint64_t wb = __ballot(bad);
     if ((tid & 63) == 0) sm.wbad[tid >> 6] = wb != 0 ? 1u : 0u;
   }
@@ -588,17 +711,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   // ---- 1. threshold from the one-deviation prefixes -------------------------
   double tau = -INFINITY;
   if (LK >= B) {
-    // rows' one-deviation scores; lower bound: the q-th of every row,
-    // q = min(ceil(B / L), K), leaves >= B scores at or above the smallest
+    // rows' one-deviation scores (row d = i / K by a multiply: i * K < 2^32);
+    // the lower bound, with the histogram cleared, is already in place
+    const uint64_t kmag = ((1ull << 32) + (uint64_t)K - 1) / (uint64_t)K;
     auto onedev = [&](int i) -> double {
-      const int d = i / K;
+      const int d = (int)(((uint64_t)(uint32_t)i * kmag) >> 32);
       const double raw = (sm.P0[d] + (double)sm.v[i]) - sm.Z[d];
       return raw > sm.sig[d] ? sm.sig[d] : raw;
     };
-    const int q = (B + L - 1) / L < K ? (B + L - 1) / L : K;
-    tau = sel_tau_hist<false>(
-        sm, LK, B, onedev,
-        [&](int lane) { return lane < L ? onedev(lane * K + q - 1) : INFINITY; });
+    tau = sel_tau_hist<false, NT, true>(sm, LK, B, onedev, [](int) { return INFINITY; });
   }
 
   // Fast path: sums of row values are exact (their exponents span <= 22, so
@@ -608,7 +729,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   // directly, strictly decreasing in e: chains are found by binary search.
   bool fast = sm.f2 != 0;
 #pragma unroll
-  for (int i = 0; i < kSelWaves; ++i) fast = fast && sm.wbad[i] == 0;
+  for (int i = 0; i < NW; ++i) fast = fast && sm.wbad[i] == 0;
   // ---- 2. enumerate E = {score >= tau} by chains ----------------------------
   // If E outgrows its capacity, every entry found so far is a valid prefix
   // scoring >= tau: the B-th best of them is a valid, usually much tighter,
@@ -618,7 +739,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     // spine prefixes reaching tau (the spine's scores do not increase): one
     // ballot over L <= 32 lanes
     const int D0 = __popcll(__ballot((tid & 63) < L && sm.sig[(tid & 63) + 1] >= tau));
-    for (int d = tid; d < D0; d += kSelThreads) {
+    for (int d = tid; d < D0; d += NT) {
       en.eS[d] = sm.P0[d + 1];
       en.eSc[d] = sm.sig[d + 1];
       en.ePar[d] = (int16_t)(d - 1);
@@ -628,7 +749,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
       en.eLl[d] = (uint64_t)(d + 1);
     }
     if (tid == 0) sm.nE = D0;
-    sm.hist[tid] = 0;  // the ordering's histogram (no threshold pass follows)
+    for (int j = tid; j < kSelBins; j += NT) sm.hist[j] = 0;  // the ordering's histogram
     __syncthreads();
     int g0 = 0, g1 = D0, root = 1;
     for (;;) {
@@ -639,12 +760,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
         break;
       }
       // deviating children (rank >= 1) of each parent that reach tau, counted
-      // by binary search in the sorted row; parents per thread: 1, or 2 when
-      // np > kSelThreads (consecutive, so the offsets follow parent order)
-      const int ppt = np > kSelThreads ? 2 : 1;
-      int cpar[2] = {0, 0};
+      // by binary search in the sorted row; ceil(np / NT) <= NPT parents per
+      // thread, consecutive, so the offsets follow parent order
+      const int ppt = (np + NT - 1) / NT;
+      int cpar[NPT], csum = 0;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
+      for (int k = 0; k < NPT; ++k) {
+        cpar[k] = 0;
         const int i = tid * ppt + k;
         if (k < ppt && i < np) {
           double S = 0.0;
@@ -666,9 +788,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
             cpar[k] = lo - 1;
           }
         }
+        csum += cpar[k];
       }
       int A;
-      const int off = block_excl_scan_reg<kSelThreads>(cpar[0] + cpar[1], sm.wsum, A);
+      const int off = block_excl_scan_reg<NT>(csum, sm.wsum, A);
       if (A == 0) break;
       if (A > kECap) {  // more new anchors than entries fit
         if (tid == 0) sm.ovf = 1;
@@ -679,10 +802,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
       // decrease with the parent index): each anchor finds its parent by
       // binary search, so no thread writes a long run of labels
       uint32_t* poff = en.own;
+      {
+        int run = off;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int i = tid * ppt + k;
-        if (k < ppt && i < np) poff[i] = (uint32_t)(off + (k ? cpar[0] : 0));
+        for (int k = 0; k < NPT; ++k) {
+          const int i = tid * ppt + k;
+          if (k < ppt && i < np) poff[i] = (uint32_t)run;
+          run += cpar[k];
+        }
       }
       __syncthreads();
       const int nE0 = sm.nE;
@@ -692,16 +819,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
       auto has_child = [&](int dd, double S) {
         return dd < L && K > 1 && (S + (double)sm.v[dd * K + 1]) - sm.Z[dd] >= tau;
       };
-      // anchors, consecutive per thread (1, or 2 when A > kSelThreads): the
+      // anchors, consecutive per thread (ceil(A / NT) <= NPT of them): the
       // parent, S and score, and the chain length -- the anchor, then its
       // rank-0 extensions while they reach tau (S summed left to right, the
       // next four depths' spine values read per step)
-      const int apt = A > kSelThreads ? 2 : 1;
-      double aS[2] = {0.0, 0.0}, aSc[2] = {0.0, 0.0};
-      uint64_t aLh[2] = {0, 0}, aLl[2] = {0, 0};
-      int aD[2] = {0, 0}, aPe[2] = {-1, -1}, aR[2] = {0, 0}, aEll[2] = {0, 0};
+      const int apt = (A + NT - 1) / NT;
+      double aS[NPT], aSc[NPT];
+      uint64_t aLh[NPT], aLl[NPT];
+      int aD[NPT], aPe[NPT], aR[NPT], aEll[NPT], esum = 0;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
+      for (int k = 0; k < NPT; ++k) {
+        aEll[k] = 0;  // 0: no anchor in this slot
         const int a = tid * apt + k;
         if (k < apt && a < A) {
           int lo = 0, hi = np - 1;  // the last parent whose first slot is <= a
@@ -772,18 +900,28 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
           aR[k] = r;
           aEll[k] = ell;
         }
+        esum += aEll[k];
       }
       // slots in anchor order: a block scan of the chain lengths; the
-      // anchor entries first, their positions kept for the chain entries
+      // anchor entries first, and every slot of a chain labelled with its
+      // anchor's slot (the parents' offsets are dead after the scan)
       int T;
-      const int aoff = block_excl_scan_reg<kSelThreads>(aEll[0] + aEll[1], sm.wsum, T);
-      int* apos = en.cnt;
+      const int aoff = block_excl_scan_reg<NT>(esum, sm.wsum, T);
+      uint32_t* aslot = en.own;
+      int arun = nE0 + aoff;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
+      for (int k = 0; k < NPT; ++k) {
         const int a = tid * apt + k;
+        const int pos = arun;
+        arun += aEll[k];
         if (k < apt && a < A) {
-          const int pos = nE0 + aoff + (k ? aEll[0] : 0);
-          apos[a] = pos;
+          const int pend = pos + aEll[k] < kECap ? pos + aEll[k] : kECap;
+          for (int q = pos; q < pend; q += 4) {  // four labels per step
+            aslot[q] = (uint32_t)pos;
+            if (q + 1 < pend) aslot[q + 1] = (uint32_t)pos;
+            if (q + 2 < pend) aslot[q + 2] = (uint32_t)pos;
+            if (q + 3 < pend) aslot[q + 3] = (uint32_t)pos;
+          }
           if (pos < kECap) {
             if (has_child(aD[k], aS[k])) sm.more = 1;
             en.eS[pos] = aS[k];
@@ -803,17 +941,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
         // entries [0, kECap) stay valid prefixes scoring >= tau
         if (nE0 + T > kECap) sm.ovf = 1;
       }
-      // chain entries, one thread per slot: its anchor by binary search over
-      // the anchors' slots, then S summed left to right from the anchor's
-      // and the score's running minimum along the chain
-      for (int q = nE0 + tid; q < nEnd; q += kSelThreads) {
-        int lo = 0, hi = A - 1;  // the last anchor whose slot is <= q
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (apos[mid] <= q) lo = mid;
-          else hi = mid - 1;
-        }
-        const int pa = apos[lo], j = q - pa;
+      // chain entries, one thread per slot: its anchor's slot from the
+      // label, then S summed left to right from the anchor's and the
+      // score's running minimum along the chain
+      for (int q = nE0 + tid; q < nEnd; q += NT) {
+        const int pa = (int)aslot[q], j = q - pa;
         if (j == 0) continue;
         const int d = en.eDep[pa];
         double S2 = en.eS[pa], sc2 = en.eSc[pa];
@@ -851,7 +983,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     // overflow: entries [0, n) are prefixes scoring >= tau
     const int n = sm.nE < kECap ? sm.nE : kECap;
     if (attempt == kSelRetries || n < B) break;
-    const double t1 = sel_tau_hist(
+    const double t1 = sel_tau_hist<true, NT>(
         sm, n, B, [&](int i) { return en.eSc[i]; }, [&](int) { return tau; },
         reinterpret_cast<double*>(en.eLh), kECap);
     if (!(t1 > tau)) break;
@@ -865,9 +997,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     if (tid == 0) heap_fallback(p, sm, b);
     __syncthreads();
   } else {
-    sel_order_emit<false>(p, sm, b, tau);
+    sel_order_emit<false, NT>(p, sm, b, tau);
   }
-  sel_mask(p, sm, b);
+  sel_mask<NT>(p, sm, b);
 }
 
 }  // namespace ddt
