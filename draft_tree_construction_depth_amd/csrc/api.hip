@@ -222,6 +222,18 @@ int ceil_log2(int x) {
 
 bool valid_dtype(int dtype) { return dtype == DDT_BF16 || dtype == DDT_F32; }
 
+// Host-side constants of a selection launch: multipliers for the kernels'
+// divisions by K and W (exact for the table and mask indices, < 2^13) and the
+// threshold's lower-bound rank.
+void select_derived(ddt::SelectParams& sp) {
+  const uint64_t k = (uint64_t)(sp.K > 0 ? sp.K : 1), w = (uint64_t)(sp.W > 0 ? sp.W : 1);
+  sp.kmag = ((1ull << 32) + k - 1) / k;
+  sp.wmag = ((1ull << 32) + w - 1) / w;
+  const int c = (sp.B + sp.L - 1) / (sp.L > 0 ? sp.L : 1);
+  sp.q1 = c < sp.K ? c : sp.K;
+  if (sp.q1 < 1) sp.q1 = 1;
+}
+
 int launch_select(const float* vals, const int32_t* ids, const double* lse, int64_t batch,
                   int32_t L, int32_t K, int32_t B, int bpd, int32_t* tree_tokens,
                   int32_t* parents, float* logq, int32_t* depths, int32_t* num_nodes,
@@ -245,6 +257,7 @@ int launch_select(const float* vals, const int32_t* ids, const double* lse, int6
   sp.sp_lp = nullptr;
   sp.sp_best = nullptr;
   sp.sp_blp = nullptr;
+  select_derived(sp);
   hipLaunchKernelGGL(ddt::select_kernel, dim3((unsigned)batch), dim3(ddt::kSelNT), 0, stream,
                      sp);
   return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
@@ -793,6 +806,7 @@ int sparkling_build(const void* logits, int dtype, const uint16_t* W1, const uin
   sp.sp_lp = lp;
   sp.sp_best = best;
   sp.sp_blp = blp;
+  select_derived(sp);
   hipLaunchKernelGGL(ddt::sp_select_kernel, dim3((unsigned)batch), dim3(ddt::kSelThreads), 0,
                      stream, sp);
   return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
@@ -875,6 +889,7 @@ int sparkling_beam(const void* logits, int dtype, const uint16_t* W1, const uint
   sp.sp_lp = (const float*)(ws + lay.lp);
   sp.sp_best = (const uint8_t*)(ws + lay.best);
   sp.sp_blp = (const float*)(ws + lay.blp);
+  select_derived(sp);
   for (int d = 0; d < ddt::kMaxL; ++d) bp.widths[d] = d < L ? w[d] : 0;
   hipLaunchKernelGGL(ddt::beam_kernel, dim3((unsigned)batch), dim3(ddt::kBmThreads), 0, stream,
                      bp);

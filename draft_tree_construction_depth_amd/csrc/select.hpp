@@ -88,6 +88,11 @@ struct SelectParams {
   int32_t* num_nodes;
   uint64_t* mask;  // may be null; [batch][B+1][W]
   int32_t W;
+  // derived on the host (select_derived): i / K = (i * kmag) >> 32 and
+  // t / W = (t * wmag) >> 32 for i, t < 2^13 (exact while i * K < 2^32),
+  // and q1 = min(ceil(B / L), K)
+  uint64_t kmag, wmag;
+  int32_t q1;
   // conditioned rows (SparklingTree; null for independent rows)
   const float* sp_lp;      // [batch][L-1][K][K] child row d, parent candidate, child candidate
   const uint8_t* sp_best;  // [batch][L-1][K] each row's best child
@@ -143,10 +148,13 @@ struct SelectSmem {
   alignas(16) int hist[kSelBins];
   int hexc[kSelBins];  // entries in the bins before each bin
   double tau;
+  double hscale;  // the threshold histogram's bins per unit score
+  double tcut;    // the threshold found by the thread holding the cut bin
+  double oscale;  // the ordering histogram's bins per unit score (independent rows)
   int nE;
   int ovf;
   int nsel;
-  uint32_t wbad[kSelWaves];  // per wave: some value outside the exact-sum window
+  alignas(16) uint32_t wbad[kSelWaves];  // per wave: some value outside the exact-sum window
   int more;                  // some entry of this generation has a deviating child
   int f2;                    // every row's top log-probability is clearly negative
 };
@@ -289,12 +297,13 @@ __device__ double sel_tau_hist(SelectSmem& sm, int LK, int B, OD onedev, LB lane
     if (lane == 0) {
       sm.tau = x;
       sm.n2 = 0;
+      const double span = sm.sig[1] - x;
+      sm.hscale = span > 0.0 ? (double)kSelBins / span : 0.0;
     }
   }
   if (!PRE) __syncthreads();
-  const double mn = sm.tau, top = sm.sig[1];
-  const double span = top - mn;
-  const double scale = span > 0.0 ? (double)kSelBins / span : 0.0;
+  // one thread divided: scale = kSelBins / (top - mn), or 0 for an empty span
+  const double mn = sm.tau, top = sm.sig[1], scale = sm.hscale;
   auto bin_of = [&](double sc) -> int {
     const double t = (top - sc) * scale;
     return t >= (double)(kSelBins - 1) ? kSelBins - 1 : (t > 0.0 ? (int)t : 0);
@@ -321,17 +330,21 @@ __device__ double sel_tau_hist(SelectSmem& sm, int LK, int B, OD onedev, LB lane
     const int exc = run;
     run += h[j];
     if (run >= B && exc < B) {
-      sm.kcut = tid * BPT + j;
+      const int kc = tid * BPT + j;
+      sm.kcut = kc;
       sm.kexc = exc;
+      if (!EXACT) {
+        double e = mn;
+        if (scale > 0.0 && kc < kSelBins - 1) {
+          const double edge = top - ((double)kc + 1.000001) / scale;
+          e = edge > mn ? edge : mn;
+        }
+        sm.tcut = e;
+      }
     }
   }
   __syncthreads();
-  if constexpr (!EXACT) {
-    const int kc = sm.kcut;
-    if (!(scale > 0.0) || kc >= kSelBins - 1) return mn;
-    const double edge = top - ((double)kc + 1.000001) / scale;
-    return edge > mn ? edge : mn;
-  }
+  if constexpr (!EXACT) return sm.tcut;
   const int kb = sm.kcut, t = B - 1 - sm.kexc;  // the B-th is member t of bin kb
   for (int i = tid; i < LK; i += NT) {
     const double sc = onedev(i);
@@ -361,7 +374,9 @@ __device__ double sel_tau_hist(SelectSmem& sm, int LK, int B, OD onedev, LB lane
 // Phase 3 (after an enumeration without overflow): order E, emit the
 // first B (tokens, parents, log-probs, depths, node count). en.eRank holds
 // each entry's index into its row's candidate table.
-template <bool ZERO_HIST = true, int NT = kSelThreads>
+// With PRE_SCALE the caller has stored kSelBins / (best - tau) (0 for an
+// empty span) in sm.oscale before a barrier.
+template <bool ZERO_HIST = true, int NT = kSelThreads, bool PRE_SCALE = false>
 __device__ __forceinline__ void sel_order_emit(const SelectParams& p, SelectSmem& sm, int64_t b,
                                                double tau) {
   constexpr int NPT = kECap / NT, NW = NT / kWave, BPT = kSelBins / NT;
@@ -389,7 +404,7 @@ __device__ __forceinline__ void sel_order_emit(const SelectParams& p, SelectSmem
   }
   const double top = sm.sig[1];  // the best prefix: depth 1, rank 0
   const double span = top - tau;
-  const double scale = span > 0.0 ? (double)kSelBins / span : 0.0;
+  const double scale = PRE_SCALE ? sm.oscale : (span > 0.0 ? (double)kSelBins / span : 0.0);
   auto bin_of = [&](double sc) -> int {
     const double t = (top - sc) * scale;
     return t >= (double)(kSelBins - 1) ? kSelBins - 1 : (t > 0.0 ? (int)t : 0);
@@ -528,7 +543,7 @@ __device__ __forceinline__ void sel_mask_rows(const SelectParams& p, const int* 
   const int B = p.B, W = p.W;
   uint64_t* dst = p.mask + (size_t)b * (B + 1) * W;
   for (int t = threadIdx.x; t < (B + 1) * W; t += NT) {
-    const int i = t / W, q = t - i * W;
+    const int i = (int)(((uint64_t)(uint32_t)t * p.wmag) >> 32), q = t - i * W;  // t / W
     uint64_t m = 0;
     if (i <= nsel) {
       int u = i;
@@ -584,8 +599,9 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(SelectParams p) {
   const int L = p.L, K = p.K, B = p.B, LK = L * K, bpd = p.bpd;
   const float* vals = p.vals + (size_t)b * LK;
   // the threshold's lower-bound rank: the q1-th one-deviation score of every
-  // row, q1 = min(ceil(B / L), K), leaves >= B scores at or above the smallest
-  const int q1 = (B + L - 1) / L < K ? (B + L - 1) / L : K;  // in [1, K]
+  // row, q1 = min(ceil(B / L), K) in [1, K], leaves >= B scores at or above
+  // the smallest
+  const int q1 = p.q1;
 
   if (tid < kWave) {
     // Z_d and the spine (all ranks 0), float64, in wave 0's registers while
@@ -661,9 +677,11 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(SelectParams p) {
       const double r1 = (Sx + (double)vq) - Zi;
       const double od = lane < L ? (r1 > sgx ? sgx : r1) : INFINITY;
       const double mn = wave_min(od);
-      if (lane == 0) {
+      if (lane == 0) {  // lane 0's sg is sig[1], the best score
         sm.tau = mn;
         sm.n2 = 0;
+        const double span = sg - mn;
+        sm.hscale = span > 0.0 ? (double)kSelBins / span : 0.0;
       }
     }
     if (lane < L) {
@@ -711,9 +729,9 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(SelectParams p) {
   // ---- 1. threshold from the one-deviation prefixes -------------------------
   double tau = -INFINITY;
   if (LK >= B) {
-    // rows' one-deviation scores (row d = i / K by a multiply: i * K < 2^32);
-    // the lower bound, with the histogram cleared, is already in place
-    const uint64_t kmag = ((1ull << 32) + (uint64_t)K - 1) / (uint64_t)K;
+    // rows' one-deviation scores (row d = i / K by a multiply); the lower
+    // bound, with the histogram cleared, is already in place
+    const uint64_t kmag = p.kmag;
     auto onedev = [&](int i) -> double {
       const int d = (int)(((uint64_t)(uint32_t)i * kmag) >> 32);
       const double raw = (sm.P0[d] + (double)sm.v[i]) - sm.Z[d];
@@ -727,9 +745,13 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(SelectParams p) {
   // (every step along a path lowers the score by more than any rounding).
   // Then a rank-0 extension to depth e scores (S + (P0[e] - P0[d])) - Z[e-1]
   // directly, strictly decreasing in e: chains are found by binary search.
-  bool fast = sm.f2 != 0;
+  uint32_t anybad = 0;  // the waves' flags, four per 16-byte read
 #pragma unroll
-  for (int i = 0; i < NW; ++i) fast = fast && sm.wbad[i] == 0;
+  for (int i = 0; i < NW; i += 4) {
+    const uint4 t = *(const uint4*)&sm.wbad[i];
+    anybad |= t.x | t.y | t.z | t.w;
+  }
+  const bool fast = sm.f2 != 0 && anybad == 0;
   // ---- 2. enumerate E = {score >= tau} by chains ----------------------------
   // If E outgrows its capacity, every entry found so far is a valid prefix
   // scoring >= tau: the B-th best of them is a valid, usually much tighter,
@@ -748,7 +770,11 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(SelectParams p) {
       en.eLh[d] = 0;
       en.eLl[d] = (uint64_t)(d + 1);
     }
-    if (tid == 0) sm.nE = D0;
+    if (tid == 0) {
+      sm.nE = D0;
+      const double span = sm.sig[1] - tau;  // the ordering's scale for this tau
+      sm.oscale = span > 0.0 ? (double)kSelBins / span : 0.0;
+    }
     for (int j = tid; j < kSelBins; j += NT) sm.hist[j] = 0;  // the ordering's histogram
     __syncthreads();
     int g0 = 0, g1 = D0, root = 1;
@@ -997,7 +1023,7 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(SelectParams p) {
     if (tid == 0) heap_fallback(p, sm, b);
     __syncthreads();
   } else {
-    sel_order_emit<false, NT>(p, sm, b, tau);
+    sel_order_emit<false, NT, true>(p, sm, b, tau);
   }
   sel_mask<NT>(p, sm, b);
 }
