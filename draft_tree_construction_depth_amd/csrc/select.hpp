@@ -142,11 +142,12 @@ struct SelectSmem {
   } u;
   int opar[kMaxB];  // parent node number of output node j+1
   alignas(16) int wsum[kSelWaves];
+  int A1;    // the first generation's anchors (counted by wave 0)
   int kexc;  // entries before the threshold's bin
   int n2;
   int kcut;
   alignas(16) int hist[kSelBins];
-  int hexc[kSelBins];  // entries in the bins before each bin
+  alignas(16) int hexc[kSelBins];  // entries in the bins before each bin
   double tau;
   double hscale;  // the threshold histogram's bins per unit score
   double tcut;    // the threshold found by the thread holding the cut bin
@@ -277,17 +278,15 @@ __device__ void heap_fallback(const SelectParams& p, SelectSmem& sm, int64_t b) 
 // the B-th, moved down by a millionth of a bin: at or below every member of
 // that bin, so a valid lower bound with the same guarantee, found without
 // ranking the bin (a slightly larger E to enumerate).
-// With PRE the caller has already cleared the histogram and stored the lower
-// bound in sm.tau, before a barrier (lane_bound is then unused).
-template <bool EXACT = true, int NT = kSelThreads, bool PRE = false, class OD, class LB>
+template <bool EXACT = true, int NT = kSelThreads, class OD, class LB>
 __device__ double sel_tau_hist(SelectSmem& sm, int LK, int B, OD onedev, LB lane_bound,
                                double* mem = nullptr, int memcap = kMergeCap) {
   constexpr int NW = NT / kWave, BPT = kSelBins / NT;  // bins per thread in the scan
   static_assert(BPT * NT == kSelBins, "whole bins per thread");
   if (mem == nullptr) mem = sm.u.mt.a;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (!PRE) for (int j = tid; j < kSelBins; j += NT) sm.hist[j] = 0;
-  if (!PRE && w == 0) {
+  for (int j = tid; j < kSelBins; j += NT) sm.hist[j] = 0;
+  if (w == 0) {
     double x = lane_bound(lane);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -301,7 +300,7 @@ __device__ double sel_tau_hist(SelectSmem& sm, int LK, int B, OD onedev, LB lane
       sm.hscale = span > 0.0 ? (double)kSelBins / span : 0.0;
     }
   }
-  if (!PRE) __syncthreads();
+  __syncthreads();
   // one thread divided: scale = kSelBins / (top - mn), or 0 for an empty span
   const double mn = sm.tau, top = sm.sig[1], scale = sm.hscale;
   auto bin_of = [&](double sc) -> int {
@@ -727,18 +726,99 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(SelectParams p) {
 
 
   // ---- 1. threshold from the one-deviation prefixes -------------------------
-  double tau = -INFINITY;
+  // The rows' one-deviation scores fall into kSelBins bins over [mn, best]
+  // (mn, the lower bound, and the bins' scale are in place, the histogram
+  // cleared); wave 0 then finds the bin holding the B-th and sets tau to its
+  // lower edge moved down by a millionth of a bin (at or below every member
+  // of that bin, so >= B scores reach it), and without a barrier goes on to
+  // the spine entries reaching tau and the first generation's child counts.
   if (LK >= B) {
-    // rows' one-deviation scores (row d = i / K by a multiply); the lower
-    // bound, with the histogram cleared, is already in place
-    const uint64_t kmag = p.kmag;
-    auto onedev = [&](int i) -> double {
+    const uint64_t kmag = p.kmag;  // row d = i / K by a multiply
+    const double mn = sm.tau, top = sm.sig[1], scale = sm.hscale;
+    for (int i = tid; i < LK; i += NT) {
       const int d = (int)(((uint64_t)(uint32_t)i * kmag) >> 32);
       const double raw = (sm.P0[d] + (double)sm.v[i]) - sm.Z[d];
-      return raw > sm.sig[d] ? sm.sig[d] : raw;
-    };
-    tau = sel_tau_hist<false, NT, true>(sm, LK, B, onedev, [](int) { return INFINITY; });
+      const double sc = raw > sm.sig[d] ? sm.sig[d] : raw;
+      if (sc >= mn) {
+        const double t = (top - sc) * scale;
+        atomicAdd(&sm.hist[t >= (double)(kSelBins - 1) ? kSelBins - 1 : (t > 0.0 ? (int)t : 0)], 1);
+      }
+    }
+    __syncthreads();
   }
+  if (tid < kWave) {
+    const int lane = tid;
+    double t = -INFINITY;
+    if (LK >= B) {
+      // lane l sums bins [16 l, 16 l + 16); a wave scan; the lane whose
+      // range reaches B walks its bins to the cut
+      constexpr int BPL = kSelBins / kWave;
+      int h[BPL], hs = 0;
+#pragma unroll
+      for (int j = 0; j < BPL; j += 4) {
+        const int4 q = *(const int4*)&sm.hist[lane * BPL + j];
+        h[j] = q.x;
+        h[j + 1] = q.y;
+        h[j + 2] = q.z;
+        h[j + 3] = q.w;
+        hs += q.x + q.y + q.z + q.w;
+      }
+      const int inc = wave_incl_scan(hs);
+      int run = inc - hs, kc = kSelBins;
+#pragma unroll
+      for (int j = 0; j < BPL; ++j) {
+        const int exc = run;
+        run += h[j];
+        if (run >= B && exc < B) kc = lane * BPL + j;
+      }
+      kc = wave_min(kc);  // the one lane that holds the cut
+      const double mn = sm.tau, top = sm.sig[1], scale = sm.hscale;
+      t = mn;
+      if (scale > 0.0 && kc < kSelBins - 1) {
+        const double edge = top - ((double)kc + 1.000001) / scale;
+        t = edge > mn ? edge : mn;
+      }
+    }
+    // spine prefixes reaching t (the spine's scores do not increase)
+    const int D0 = __popcll(__ballot(lane < L && sm.sig[lane + 1] >= t));
+    if (lane < D0) {
+      en.eS[lane] = sm.P0[lane + 1];
+      en.eSc[lane] = sm.sig[lane + 1];
+      en.ePar[lane] = (int16_t)(lane - 1);
+      en.eRank[lane] = 0;
+      en.eDep[lane] = (uint8_t)(lane + 1);
+      en.eLh[lane] = 0;
+      en.eLl[lane] = (uint64_t)(lane + 1);
+    }
+    // the first generation's parents: the root (lane 0, depth 0) and spine
+    // entry u - 1 (lane u, depth u, sum P0[u]); deviating children reaching
+    // t counted by binary search in the sorted row, the count search's test
+    int c = 0;
+    if (lane <= D0 && lane < L) {
+      const double S = lane == 0 ? 0.0 : sm.P0[lane];
+      const float* row = sm.v + lane * K;
+      const double Zd = sm.Z[lane];
+      int lo = 1, hi = K;  // first failing rank lies in [lo, hi]
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((S + (double)row[mid]) - Zd >= t) lo = mid + 1;
+        else hi = mid;
+      }
+      c = lo - 1;
+    }
+    const int cinc = wave_incl_scan(c);
+    if (lane <= D0) en.own[lane] = (uint32_t)(cinc - c);  // parents' first anchor slots
+    if (lane == kWave - 1) sm.A1 = cinc;
+    if (lane == 0) {
+      sm.tau = t;
+      sm.nE = D0;
+      sm.more = 0;
+      const double span = sm.sig[1] - t;  // the ordering's scale for this tau
+      sm.oscale = span > 0.0 ? (double)kSelBins / span : 0.0;
+    }
+  }
+  __syncthreads();
+  double tau = sm.tau;
 
   // Fast path: sums of row values are exact (their exponents span <= 22, so
   // every S is the same whatever the summation order) and no score clamps
@@ -758,28 +838,48 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(SelectParams p) {
   // threshold, and the enumeration restarts from it (kSelRetries times at
   // most, then the heap).
   for (int attempt = 0;; ++attempt) {
-    // spine prefixes reaching tau (the spine's scores do not increase): one
-    // ballot over L <= 32 lanes
-    const int D0 = __popcll(__ballot((tid & 63) < L && sm.sig[(tid & 63) + 1] >= tau));
-    for (int d = tid; d < D0; d += NT) {
-      en.eS[d] = sm.P0[d + 1];
-      en.eSc[d] = sm.sig[d + 1];
-      en.ePar[d] = (int16_t)(d - 1);
-      en.eRank[d] = 0;
-      en.eDep[d] = (uint8_t)(d + 1);
-      en.eLh[d] = 0;
-      en.eLl[d] = (uint64_t)(d + 1);
+    int D0;
+    if (attempt == 0) {
+      D0 = sm.nE;  // wave 0's spine entries, counts and offsets are in place
+    } else {
+      // spine prefixes reaching tau (the spine's scores do not increase):
+      // one ballot over L <= 32 lanes
+      D0 = __popcll(__ballot((tid & 63) < L && sm.sig[(tid & 63) + 1] >= tau));
+      for (int d = tid; d < D0; d += NT) {
+        en.eS[d] = sm.P0[d + 1];
+        en.eSc[d] = sm.sig[d + 1];
+        en.ePar[d] = (int16_t)(d - 1);
+        en.eRank[d] = 0;
+        en.eDep[d] = (uint8_t)(d + 1);
+        en.eLh[d] = 0;
+        en.eLl[d] = (uint64_t)(d + 1);
+      }
+      if (tid == 0) {
+        sm.nE = D0;
+        const double span = sm.sig[1] - tau;  // the ordering's scale for this tau
+        sm.oscale = span > 0.0 ? (double)kSelBins / span : 0.0;
+      }
+      for (int j = tid; j < kSelBins; j += NT) sm.hist[j] = 0;  // the ordering's histogram
+      __syncthreads();
     }
-    if (tid == 0) {
-      sm.nE = D0;
-      const double span = sm.sig[1] - tau;  // the ordering's scale for this tau
-      sm.oscale = span > 0.0 ? (double)kSelBins / span : 0.0;
-    }
-    for (int j = tid; j < kSelBins; j += NT) sm.hist[j] = 0;  // the ordering's histogram
-    __syncthreads();
     int g0 = 0, g1 = D0, root = 1;
+    bool counted = attempt == 0;  // the first generation counted by wave 0
     for (;;) {
       const int np = root + (g1 - g0);
+      uint32_t* poff = en.own;  // parents' first anchor slots
+      int A;
+      if (counted) {
+        counted = false;
+        A = sm.A1;
+        // the ordering's histogram (the threshold's scan read it before the
+        // last barrier)
+        for (int j = tid; j < kSelBins; j += NT) sm.hist[j] = 0;
+        if (A == 0 || A > kECap) {
+          if (tid == 0 && A > kECap) sm.ovf = 1;  // more new anchors than entries fit
+          __syncthreads();
+          break;
+        }
+      } else {
       if (np > kECap) {  // parents must fit the count array
         if (tid == 0) sm.ovf = 1;
         __syncthreads();
@@ -816,7 +916,6 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(SelectParams p) {
         }
         csum += cpar[k];
       }
-      int A;
       const int off = block_excl_scan_reg<NT>(csum, sm.wsum, A);
       if (A == 0) break;
       if (A > kECap) {  // more new anchors than entries fit
@@ -827,7 +926,6 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(SelectParams p) {
       // parents' first anchor slots (their exclusive offsets, which do not
       // decrease with the parent index): each anchor finds its parent by
       // binary search, so no thread writes a long run of labels
-      uint32_t* poff = en.own;
       {
         int run = off;
 #pragma unroll
@@ -838,8 +936,9 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(SelectParams p) {
         }
       }
       __syncthreads();
-      const int nE0 = sm.nE;
       if (tid == 0) sm.more = 0;  // set below, read after this generation's last barrier
+      }
+      const int nE0 = sm.nE;
       // does an entry at depth dd with sum S have a deviating child (rank 1
       // of the next row) reaching tau? the count search's own test
       auto has_child = [&](int dd, double S) {
