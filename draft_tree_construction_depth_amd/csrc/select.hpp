@@ -156,7 +156,10 @@ struct SelectSmem {
   int ovf;
   int nsel;
   alignas(16) uint32_t wbad[kSelWaves];  // per wave: some value outside the exact-sum window
-  int more;                  // some entry of this generation has a deviating child
+  int ncand;                 // entries of this generation with a deviating child
+  int np1;                   // parents listed for a generation counted by wave 0
+  int cand[kWave];           // the first kWave of them
+  int pcand[kWave];          // the listed parents of the current generation
   int f2;                    // every row's top log-probability is clearly negative
 };
 
@@ -812,7 +815,7 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(SelectParams p) {
     if (lane == 0) {
       sm.tau = t;
       sm.nE = D0;
-      sm.more = 0;
+      sm.ncand = 0;
       const double span = sm.sig[1] - t;  // the ordering's scale for this tau
       sm.oscale = span > 0.0 ? (double)kSelBins / span : 0.0;
     }
@@ -863,17 +866,24 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(SelectParams p) {
       __syncthreads();
     }
     int g0 = 0, g1 = D0, root = 1;
+    // A generation's parents are either all entries of the previous one
+    // ([g0, g1), after the root for the first), counted by the whole block,
+    // or, when at most kWave of them have deviating children, just those
+    // (listed while they were written), counted by wave 0 alone.
     bool counted = attempt == 0;  // the first generation counted by wave 0
+    bool listed = false;          // parents are pcand[0 .. np)
     for (;;) {
-      const int np = root + (g1 - g0);
+      int np = root + (g1 - g0);
       uint32_t* poff = en.own;  // parents' first anchor slots
       int A;
       if (counted) {
         counted = false;
         A = sm.A1;
+        if (listed) np = sm.np1;
+        if (tid == 0) sm.ncand = 0;  // every wave read it before the last barrier
         // the ordering's histogram (the threshold's scan read it before the
         // last barrier)
-        for (int j = tid; j < kSelBins; j += NT) sm.hist[j] = 0;
+        if (root) for (int j = tid; j < kSelBins; j += NT) sm.hist[j] = 0;
         if (A == 0 || A > kECap) {
           if (tid == 0 && A > kECap) sm.ovf = 1;  // more new anchors than entries fit
           __syncthreads();
@@ -936,13 +946,17 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(SelectParams p) {
         }
       }
       __syncthreads();
-      if (tid == 0) sm.more = 0;  // set below, read after this generation's last barrier
+      if (tid == 0) sm.ncand = 0;  // set below, read after this generation's last barrier
       }
       const int nE0 = sm.nE;
       // does an entry at depth dd with sum S have a deviating child (rank 1
       // of the next row) reaching tau? the count search's own test
       auto has_child = [&](int dd, double S) {
         return dd < L && K > 1 && (S + (double)sm.v[dd * K + 1]) - sm.Z[dd] >= tau;
+      };
+      auto note_child = [&](int e) {  // entry e has a deviating child
+        const int ci = atomicAdd(&sm.ncand, 1);
+        if (ci < kWave) sm.cand[ci] = e;
       };
       // anchors, consecutive per thread (ceil(A / NT) <= NPT of them): the
       // parent, S and score, and the chain length -- the anchor, then its
@@ -969,7 +983,7 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(SelectParams p) {
           int du = 0, pe = -1;
           uint64_t lh = 0, ll = 0;
           if (!(root && u == 0)) {
-            pe = g0 + u - root;
+            pe = listed ? sm.pcand[u] : g0 + u - root;
             Su = en.eS[pe];
             scu = en.eSc[pe];
             du = en.eDep[pe];
@@ -1048,7 +1062,7 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(SelectParams p) {
             if (q + 3 < pend) aslot[q + 3] = (uint32_t)pos;
           }
           if (pos < kECap) {
-            if (has_child(aD[k], aS[k])) sm.more = 1;
+            if (has_child(aD[k], aS[k])) note_child(pos);
             en.eS[pos] = aS[k];
             en.eSc[pos] = aSc[k];
             en.ePar[pos] = (int16_t)aPe[k];
@@ -1085,7 +1099,7 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(SelectParams p) {
             sc2 = raw2 > sc2 ? sc2 : raw2;
           }
         }
-        if (has_child(d + j, S2)) sm.more = 1;
+        if (has_child(d + j, S2)) note_child(q);
         en.eS[q] = S2;
         en.eSc[q] = sc2;
         en.ePar[q] = (int16_t)(q - 1);
@@ -1097,12 +1111,45 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(SelectParams p) {
       __syncthreads();
       // no entry of this generation has a deviating child: the next
       // generation would find no anchors
-      if (!sm.more && !sm.ovf) break;
-      if (sm.ovf) break;
+      const int nc = sm.ncand;
+      if (sm.ovf || nc == 0) break;
       g0 = g1;
       g1 = sm.nE;
       root = 0;
-      if (g0 == g1) break;
+      listed = nc <= kWave;
+      if (listed) {
+        // wave 0 counts the listed parents' deviating children reaching tau
+        // (the count search's test) and lays out their first anchor slots
+        if (tid < kWave) {
+          const int lane = tid;
+          int c = 0, e = 0;
+          if (lane < nc) {
+            e = sm.cand[lane];
+            const double S = en.eS[e];
+            const int d = en.eDep[e];
+            if (d < L) {
+              const float* row = sm.v + d * K;
+              const double Zd = sm.Z[d];
+              int lo = 1, hi = K;  // first failing rank lies in [lo, hi]
+              while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if ((S + (double)row[mid]) - Zd >= tau) lo = mid + 1;
+                else hi = mid;
+              }
+              c = lo - 1;
+            }
+          }
+          const int cinc = wave_incl_scan(c);
+          if (lane < nc) {
+            poff[lane] = (uint32_t)(cinc - c);
+            sm.pcand[lane] = e;
+          }
+          if (lane == kWave - 1) sm.A1 = cinc;
+          if (lane == 0) sm.np1 = nc;
+        }
+        __syncthreads();
+        counted = true;
+      }
     }
     if (!sm.ovf) break;
     // overflow: entries [0, n) are prefixes scoring >= tau
