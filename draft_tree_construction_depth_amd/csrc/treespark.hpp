@@ -131,6 +131,10 @@ __device__ __forceinline__ void ts_merge_sorted(float (&av)[KK], int (&ai)[KK], 
 // the tile, so each parent's partial record comes out of one wave, with no
 // cross-wave combine.
 constexpr int kTsStages = 4;  // W ring depth (16 KiB per stage)
+// W is read once per launch: its loads carry the nontemporal hint, so that
+// they do not push the parents' embedding rows and the partial records (read
+// by the merge next) out of the caches
+constexpr int kTsLoadNT = 2;
 
 // LDS row r, 16-byte chunk c holds W chunk c ^ (r & 7) of that row's step
 // segment, so that a fragment read of 32 consecutive rows spreads over all
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(kTsThreads, 2) void ts_gemm_kernel(TsGemmParams p) 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (ts_lds_ptr)&sm.w[st][8 * (4 * i + ws)][0], 16,
-                                               woff[i], kc * kTsKT * 2, 0, 0);
+                                               woff[i], kc * kTsKT * 2, 0, kTsLoadNT);
   };
   auto load_e = [&](u32x4 (&dst)[4], int ks) {
     const int kc = ks < nks ? ks : nks - 1;
@@ -212,21 +216,23 @@ __global__ __launch_bounds__(kTsThreads, 2) void ts_gemm_kernel(TsGemmParams p) 
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[m][r] = 0.0f;
 
-  // Step ks: wait for this thread's loads of W(ks) and E(ks) (the eight
-  // memory instructions issued since, W(ks + 2) and E(ks + 1), may stay in
-  // flight), barrier (every wave's W(ks) is in LDS, and every wave is done
-  // with the stage W(ks + 3) will overwrite), issue W(ks + 3) and E(ks + 2),
+  // Step ks: wait for this thread's loads of W(ks) and E(ks) (the twelve
+  // memory instructions issued since, W(ks + 1), E(ks + 1) and W(ks + 2), may
+  // stay in flight: E goes out before W in each step, so waiting for E(ks)
+  // does not also wait for W(ks + 1)), barrier (every wave's W(ks) is in
+  // LDS, and every wave is done with the stage W(ks + 3) will overwrite),
+  // issue E(ks + 2) and W(ks + 3),
   // read the step's 16 A fragments in one asm block that waits for them (the
   // compiler would wait for every direct-to-LDS load in flight before an LDS
   // read it can see), then the 16 MFMAs.
   auto step = [&](int ks, u32x4 (&ec)[4], u32x4 (&en)[4]) {
     // the wait as a builtin, so that the compiler knows E(ks) has arrived and
     // adds no wait of its own before the MFMAs
-    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8), expcnt and lgkmcnt unrestricted
+    __builtin_amdgcn_s_waitcnt(0x0F7C);  // vmcnt(12), expcnt and lgkmcnt unrestricted
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");  // no memory access moves across the barrier
-    load_w(ks + 3);
     load_e(en, ks + 2);
+    load_w(ks + 3);
     if (active) {
       const uint32_t sa = (uint32_t)(ks % kTsStages) * (uint32_t)sizeof(sm.w[0]);
       u32x4 a[4][4];
@@ -270,10 +276,10 @@ __global__ __launch_bounds__(kTsThreads, 2) void ts_gemm_kernel(TsGemmParams p) 
 
   u32x4 e0[4], e1[4], e2[4];
   load_w(0);
-  load_w(1);
   load_e(e0, 0);
-  load_w(2);
+  load_w(1);
   load_e(e1, 1);
+  load_w(2);
   for (int ks = 0; ks < nks; ks += 3) {
     step(ks, e0, e2);
     if (ks + 1 >= nks) break;
