@@ -125,22 +125,30 @@ __device__ __forceinline__ void ts_merge_sorted(float (&av)[KK], int (&ai)[KK], 
 // ---------------------------------------------------------------------------
 // GEMM schedule: the head weight W streams into an LDS ring by direct
 // buffer-to-LDS loads, each wave instruction reading eight whole 128-byte row
-// segments, three k-steps ahead; the parents' embedding chunks go straight
-// into registers in the MFMA B layout, two steps ahead, from the L2. Wave w
-// owns parent columns [32 w, 32 w + 32) against all 128 vocabulary rows of
-// the tile, so each parent's partial record comes out of one wave, with no
-// cross-wave combine.
+// segments, three k-steps ahead; the parents' embedding chunks come from the
+// L2 into registers two steps ahead, also as whole 128-byte segments (eight
+// parents per instruction: an instruction in the MFMA B layout would touch 32
+// lines for 32 bytes each, which costs the stream about a third of its rate),
+// and each wave re-lays its own chunk in MFMA order through a private LDS
+// slot at the step that uses it. Wave w owns parent columns [32 w, 32 w + 32)
+// against all 128 vocabulary rows of the tile, so each parent's partial
+// record comes out of one wave, with no cross-wave combine.
 constexpr int kTsStages = 4;  // W ring depth (16 KiB per stage)
-// W is read once per launch: its loads carry the nontemporal hint, so that
-// they do not push the parents' embedding rows and the partial records (read
-// by the merge next) out of the caches
-constexpr int kTsLoadNT = 2;
+// W is read once per launch: its loads carry the nontemporal hint at system
+// scope (sc1 nt), so that they do not push the parents' embedding rows and
+// the partial records (read by the merge next) out of the L2. With nt alone
+// the embedding rows, re-read by every workgroup, kept missing: a load-only
+// copy of this schedule streamed 128 parents' rows at 154 us per launch
+// with nt and 134 us with sc1 nt (8 distinct rows: 125 and 116 us).
+constexpr int kTsLoadNT = 0x12;
 
 // LDS row r, 16-byte chunk c holds W chunk c ^ (r & 7) of that row's step
 // segment, so that a fragment read of 32 consecutive rows spreads over all
-// banks.
+// banks; each wave's embedding slot holds its 32 parents' step segments the
+// same way (80 KiB in all: two workgroups per CU).
 struct alignas(16) TsGemmSmem {
   uint16_t w[kTsStages][kTsBV][kTsKT];
+  uint16_t e[kTsThreads / kWave][32][kTsKT];
 };
 
 typedef __attribute__((address_space(3))) void* ts_lds_ptr;
@@ -174,31 +182,45 @@ __global__ __launch_bounds__(kTsThreads, 2) void ts_gemm_kernel(TsGemmParams p) 
     const int64_t v = vt0 + 8 * (4 * i + w) + (l >> 3);
     woff[i] = (uint32_t)(((v < V ? v : V - 1) - vt0) * H * 2 + (((l & 7) ^ (l >> 3)) << 4));
   }
-  // E: lane l holds parent column 32 w + l % 32 (clamped to the last parent;
-  // masked later), k half l / 32 of each 16-element MFMA step, through a
-  // buffer resource over the table (byte offsets are unsigned 32-bit: the
-  // host rejects tables of 4 GiB or more; a token past the table reads zeros)
-  int pcol = m0 + 32 * w + (l & 31);
-  pcol = pcol < p.M ? pcol : p.M - 1;
+  // E: instruction i of wave w reads the step segments of its parents
+  // 8 i .. 8 i + 7 (column 32 w + j, clamped to the last parent; masked
+  // later); lane l takes parent 8 i + l / 8, chunk (l % 8) ^ (l / 8), so that
+  // the lane-ordered write of the four registers into the wave's slot lands
+  // in the swizzled layout. A buffer resource over the table (byte offsets
+  // are unsigned 32-bit: the host rejects tables of 4 GiB or more; a token
+  // past the table reads zeros).
   const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p.E, (short)0, (int)(uint32_t)(V * H * 2), 0x00020000);
-  const uint32_t eoff = (uint32_t)p.ptok[pcol] * (uint32_t)H * 2u + 16u * (uint32_t)(l >> 5);
+  uint32_t eoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int pcol = m0 + 32 * w + 8 * i + (l >> 3);
+    pcol = pcol < p.M ? pcol : p.M - 1;
+    eoff[i] = (uint32_t)p.ptok[pcol] * (uint32_t)H * 2u + (uint32_t)(((l & 7) ^ (l >> 3)) << 4);
+  }
 
   // always issue (clamped past the last step): the wait counts stay static
+  // (past the last step the four loads still issue, so that the wait counts
+  // stay static, but read the last embedding chunk, which the L2 holds,
+  // instead of W lines from HBM again)
+  // (one code path for both, selected by value: a branch here makes the
+  // compiler add waits of its own in every step)
   auto load_w = [&](int ks) {
-    const int kc = ks < nks ? ks : nks - 1;
     const int st = ks % kTsStages;
+    const bool past = ks >= nks;
+    const __amdgpu_buffer_rsrc_t rs = past ? ers : wrs;
+    const int so = (past ? nks - 1 : ks) * kTsKT * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (ts_lds_ptr)&sm.w[st][8 * (4 * i + ws)][0], 16,
-                                               woff[i], kc * kTsKT * 2, 0, kTsLoadNT);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (ts_lds_ptr)&sm.w[st][8 * (4 * i + ws)][0], 16,
+                                               past ? eoff[i] : woff[i], so, 0, kTsLoadNT);
   };
   auto load_e = [&](u32x4 (&dst)[4], int ks) {
     const int kc = ks < nks ? ks : nks - 1;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      dst[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             ers, (int)eoff, kc * kTsKT * 2 + 32 * s, 0));
+    for (int i = 0; i < 4; ++i)
+      dst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             ers, (int)eoff[i], kc * kTsKT * 2, 0));
   };
 
   // LDS byte address, in stage 0, of this lane's A fragment for MFMA step s
@@ -209,6 +231,14 @@ __global__ __launch_bounds__(kTsThreads, 2) void ts_gemm_kernel(TsGemmParams p) 
 #pragma unroll
   for (int s = 0; s < 4; ++s)
     fa[s] = wbase + (uint32_t)((l & 31) * kTsKT * 2) + (uint32_t)(((2 * s + (l >> 5)) ^ (l & 7)) * 16);
+  // the wave's embedding slot: lane l writes bytes 16 l (+ 1 KiB per
+  // register) and reads its B fragment for MFMA step s, parent column l % 32
+  // and chunk 2 s + l / 32, from the same swizzled place as A's
+  const uint32_t ebase = (uint32_t)(uintptr_t)(ts_lds_ptr)&sm.e[ws][0][0];
+  const uint32_t ewr = ebase + 16u * (uint32_t)l;
+  uint32_t erd[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) erd[s] = fa[s] - wbase + ebase;
 
   f32x16 acc[4];
 #pragma unroll
@@ -222,9 +252,11 @@ __global__ __launch_bounds__(kTsThreads, 2) void ts_gemm_kernel(TsGemmParams p) 
   // does not also wait for W(ks + 1)), barrier (every wave's W(ks) is in
   // LDS, and every wave is done with the stage W(ks + 3) will overwrite),
   // issue E(ks + 2) and W(ks + 3),
-  // read the step's 16 A fragments in one asm block that waits for them (the
-  // compiler would wait for every direct-to-LDS load in flight before an LDS
-  // read it can see), then the 16 MFMAs.
+  // in one asm block that waits for its LDS operations (the compiler would
+  // wait for every direct-to-LDS load in flight before an LDS access it can
+  // see): write E(ks) into the wave's slot, read the step's 4 B and 16 A
+  // fragments (a wave's LDS operations take effect in order), then the 16
+  // MFMAs.
   auto step = [&](int ks, u32x4 (&ec)[4], u32x4 (&en)[4]) {
     // the wait as a builtin, so that the compiler knows E(ks) has arrived and
     // adds no wait of its own before the MFMAs
@@ -235,36 +267,47 @@ __global__ __launch_bounds__(kTsThreads, 2) void ts_gemm_kernel(TsGemmParams p) 
     load_w(ks + 3);
     if (active) {
       const uint32_t sa = (uint32_t)(ks % kTsStages) * (uint32_t)sizeof(sm.w[0]);
-      u32x4 a[4][4];
+      u32x4 a[4][4], bf[4];
       asm volatile(
-          "ds_read_b128 %0, %16\n\t"
-          "ds_read_b128 %1, %16 offset:4096\n\t"
-          "ds_read_b128 %2, %16 offset:8192\n\t"
-          "ds_read_b128 %3, %16 offset:12288\n\t"
-          "ds_read_b128 %4, %17\n\t"
-          "ds_read_b128 %5, %17 offset:4096\n\t"
-          "ds_read_b128 %6, %17 offset:8192\n\t"
-          "ds_read_b128 %7, %17 offset:12288\n\t"
-          "ds_read_b128 %8, %18\n\t"
-          "ds_read_b128 %9, %18 offset:4096\n\t"
-          "ds_read_b128 %10, %18 offset:8192\n\t"
-          "ds_read_b128 %11, %18 offset:12288\n\t"
-          "ds_read_b128 %12, %19\n\t"
-          "ds_read_b128 %13, %19 offset:4096\n\t"
-          "ds_read_b128 %14, %19 offset:8192\n\t"
-          "ds_read_b128 %15, %19 offset:12288\n\t"
+          "ds_write_b128 %24, %25\n\t"
+          "ds_write_b128 %24, %26 offset:1024\n\t"
+          "ds_write_b128 %24, %27 offset:2048\n\t"
+          "ds_write_b128 %24, %28 offset:3072\n\t"
+          "ds_read_b128 %16, %29\n\t"
+          "ds_read_b128 %17, %30\n\t"
+          "ds_read_b128 %18, %31\n\t"
+          "ds_read_b128 %19, %32\n\t"
+          "ds_read_b128 %0, %20\n\t"
+          "ds_read_b128 %1, %20 offset:4096\n\t"
+          "ds_read_b128 %2, %20 offset:8192\n\t"
+          "ds_read_b128 %3, %20 offset:12288\n\t"
+          "ds_read_b128 %4, %21\n\t"
+          "ds_read_b128 %5, %21 offset:4096\n\t"
+          "ds_read_b128 %6, %21 offset:8192\n\t"
+          "ds_read_b128 %7, %21 offset:12288\n\t"
+          "ds_read_b128 %8, %22\n\t"
+          "ds_read_b128 %9, %22 offset:4096\n\t"
+          "ds_read_b128 %10, %22 offset:8192\n\t"
+          "ds_read_b128 %11, %22 offset:12288\n\t"
+          "ds_read_b128 %12, %23\n\t"
+          "ds_read_b128 %13, %23 offset:4096\n\t"
+          "ds_read_b128 %14, %23 offset:8192\n\t"
+          "ds_read_b128 %15, %23 offset:12288\n\t"
           "s_waitcnt lgkmcnt(0)"
           : "=&v"(a[0][0]), "=&v"(a[1][0]), "=&v"(a[2][0]), "=&v"(a[3][0]),
             "=&v"(a[0][1]), "=&v"(a[1][1]), "=&v"(a[2][1]), "=&v"(a[3][1]),
             "=&v"(a[0][2]), "=&v"(a[1][2]), "=&v"(a[2][2]), "=&v"(a[3][2]),
-            "=&v"(a[0][3]), "=&v"(a[1][3]), "=&v"(a[2][3]), "=&v"(a[3][3])
-          : "v"(fa[0] + sa), "v"(fa[1] + sa), "v"(fa[2] + sa), "v"(fa[3] + sa));
+            "=&v"(a[0][3]), "=&v"(a[1][3]), "=&v"(a[2][3]), "=&v"(a[3][3]),
+            "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3])
+          : "v"(fa[0] + sa), "v"(fa[1] + sa), "v"(fa[2] + sa), "v"(fa[3] + sa), "v"(ewr),
+            "v"(ec[0]), "v"(ec[1]), "v"(ec[2]), "v"(ec[3]), "v"(erd[0]), "v"(erd[1]), "v"(erd[2]),
+            "v"(erd[3]));
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int m = 0; m < 4; ++m)
           acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, a[m][s]), __builtin_bit_cast(bf16x8, ec[s]), acc[m], 0, 0,
+              __builtin_bit_cast(bf16x8, a[m][s]), __builtin_bit_cast(bf16x8, bf[s]), acc[m], 0, 0,
               0);
     } else {
       // consume E(ks) here too, so that on both paths its registers are known
@@ -274,19 +317,33 @@ __global__ __launch_bounds__(kTsThreads, 2) void ts_gemm_kernel(TsGemmParams p) 
     }
   };
 
+  // The prologue issues W(0), E(0), W(1), E(1), W(2) in that order, with the
+  // parents' tokens read first: the step's vmcnt(12) relies on it, and a
+  // prologue reordered by the compiler (E after every W, behind a wait for
+  // the token loads) makes it add waits of its own inside the loop that
+  // drain the W look-ahead.
+  asm volatile("" ::"v"(eoff[0]), "v"(eoff[1]), "v"(eoff[2]), "v"(eoff[3]));
   u32x4 e0[4], e1[4], e2[4];
   load_w(0);
+  asm volatile("" ::: "memory");
   load_e(e0, 0);
+  asm volatile("" ::: "memory");
   load_w(1);
+  asm volatile("" ::: "memory");
   load_e(e1, 1);
+  asm volatile("" ::: "memory");
   load_w(2);
-  for (int ks = 0; ks < nks; ks += 3) {
+  // whole rotations in the loop, the one or two remaining steps after it (an
+  // exit between the steps of a rotation also makes the compiler add waits
+  // that drain the look-ahead)
+  int ks = 0;
+  for (; ks + 3 <= nks; ks += 3) {
     step(ks, e0, e2);
-    if (ks + 1 >= nks) break;
     step(ks + 1, e1, e0);
-    if (ks + 2 >= nks) break;
     step(ks + 2, e2, e1);
   }
+  if (ks < nks) step(ks, e0, e2);
+  if (ks + 1 < nks) step(ks + 1, e1, e0);
   // drain the look-ahead loads (they target LDS this workgroup owns)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (!active) return;
@@ -303,27 +360,39 @@ __global__ __launch_bounds__(kTsThreads, 2) void ts_gemm_kernel(TsGemmParams p) 
   // and the logit is added after the mask (-inf plus a finite logit) so that
   // every load is used and all 64 issue unconditionally, back to back
   const uint16_t* lrow = p.bb + ((int64_t)req * p.D + p.d) * V;
-  // one vocabulary tile's 16 logits per batch of loads, the next batch in
-  // flight while the current one is used
-  uint16_t lb[2][16];
-  auto load_l = [&](uint16_t (&dst)[16], int t) {
+  // all 64 logits in flight at once: each group of four consecutive rows
+  // (r % 4) is one 8-byte load when the tile lies inside the vocabulary and
+  // V is a multiple of 4 (so the row starts 8-byte aligned), else one load
+  // per row
+  uint32_t lq[16][2];
+  if (vt0 + kTsBV <= V && (V & 3) == 0) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t v = vt0 + 32 * t + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-      dst[r] = lrow[v < V ? v : V - 1];
+    for (int g = 0; g < 16; ++g) {
+      const int64_t v = vt0 + 32 * (g >> 2) + 8 * (g & 3) + 4 * (l >> 5);
+      const uint2 q = *reinterpret_cast<const uint2*>(lrow + v);
+      lq[g][0] = q.x;
+      lq[g][1] = q.y;
     }
-  };
+  } else {
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      const int64_t v = vt0 + 32 * (g >> 2) + 8 * (g & 3) + 4 * (l >> 5);
+      uint32_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = lrow[v + e < V ? v + e : V - 1];
+      lq[g][0] = h[0] | (h[1] << 16);
+      lq[g][1] = h[2] | (h[3] << 16);
+    }
+  }
   float z[64];
   float mx = -INFINITY;
-  load_l(lb[0], 0);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    if (t + 1 < 4) load_l(lb[(t + 1) & 1], t + 1);
-    asm volatile("" ::: "memory");  // the next batch issued before this one is used
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t v = vt0 + 32 * t + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-      const float lv = __uint_as_float((uint32_t)lb[t & 1][r] << 16);
+      const uint32_t pr = lq[4 * t + (r >> 2)][(r >> 1) & 1];
+      const float lv = __uint_as_float((r & 1) ? (pr & 0xFFFF0000u) : (pr << 16));
       z[16 * t + r] = (v < V ? acc[t][r] : -INFINITY) + lv;
       mx = fmaxf(mx, z[16 * t + r]);
     }
