@@ -21,11 +21,18 @@ def _dev_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
 
 
-def _run_gpu(bb, W, E, anc, k, F, N):
-    out = pkg.treespark_expand(_dev_bf16(bb), _dev_bf16(W), _dev_bf16(E),
-                               torch.from_numpy(anc.astype(np.int32)).cuda(), k=k, F=F, N=N)
+def _run_gpu(bb, W, E, anc, k, F, N, repeats=0):
+    """One expansion; with repeats, that many more calls on the same device
+    inputs and output buffers, each compared bit for bit with the first."""
+    args = (_dev_bf16(bb), _dev_bf16(W), _dev_bf16(E), torch.from_numpy(anc.astype(np.int32)).cuda())
+    out = pkg.treespark_expand(*args, k=k, F=F, N=N)
+    first = {key: v.clone() for key, v in out.items()}
+    for i in range(repeats):
+        pkg.treespark_expand(*args, k=k, F=F, N=N, out=out)
+        for key in first:
+            assert torch.equal(first[key], out[key]), f"repeat {i}: {key} differs"
     torch.cuda.synchronize()
-    return {key: v.cpu().numpy() for key, v in out.items()}
+    return {key: v.cpu().numpy() for key, v in first.items()}
 
 
 def _classify(o, g, diags, rows, label, bb, W, E, anc, k, F, N, W64=None):
@@ -71,10 +78,11 @@ def test_treespark_small(seed, batch, D, V, H, k, F, N, ws):
 
 def test_treespark_readme_shape_sampled():
     """The README's shape: 32 requests, 7 depths, V = 151936, H = 2560, k = 4,
-    F = 4, N = 32; the oracle checks eight requests of the full launch."""
+    F = 4, N = 32; the oracle checks eight requests of the full launch, and
+    20 more launches on the same inputs must repeat it bit for bit."""
     c = gen.TREESPARK
     bb, W, E, anc = gen.treespark_inputs(0)
-    g = _run_gpu(bb, W, E, anc, c["k"], c["F"], c["N"])
+    g = _run_gpu(bb, W, E, anc, c["k"], c["F"], c["N"], repeats=20)
     rows = list(range(0, 32, 4))
     diags = []
     W64 = T.bf16_to_f64(W)
