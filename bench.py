@@ -511,6 +511,56 @@ def read_probe_bench(args) -> int:
     return 0
 
 
+def ts_load_probe_bench(args) -> int:
+    """TreeSpark's head-evaluation loads alone (ddtree_ts_load_probe) at the
+    README shape (V = 151936, H = 2560, 128 parents): W alone and W with the
+    parents' embedding rows in each load pattern, for 128 distinct parent
+    tokens and for 8 (each repeated 16 times). Launches interleaved by round."""
+    import numpy as np
+    import torch
+
+    import draft_tree_construction_depth_amd as pkg
+    from draft_tree_construction_depth_amd import gen
+
+    c = gen.TREESPARK
+    V, H = c["V"], c["H"]
+    dev = torch.device("cuda:0")
+    W = torch.zeros((V, H), dtype=torch.bfloat16, device=dev)
+    E = torch.zeros((V, H), dtype=torch.bfloat16, device=dev)
+    toks = {128: [(i * 1187 + 13) % V for i in range(128)],
+            8: [((i % 8) * 1187 + 13) % V for i in range(128)]}
+    toks = {n: torch.tensor(t, dtype=torch.int32, device=dev) for n, t in toks.items()}
+    names = {0: "W alone (nt)", 1: "W (nt) + rows in MFMA layout", 2: "W (nt) + rows as lines",
+             3: "W (sc1 nt) + rows as lines", 4: "W alone (sc1 nt)",
+             5: "W (nt) + half the rows as lines"}
+    cases = [(v, 128) for v in range(6)] + [(1, 8), (2, 8), (3, 8)]
+    sink = torch.empty(256, dtype=torch.int32, device=dev)
+    for v, n in cases:
+        pkg.ddtree_ts_load_probe(W, E, toks[n], v, sink)
+    torch.cuda.synchronize()
+    rounds = max(args.steps // 10, 5)
+    times = {cs: [] for cs in cases}
+    for _ in range(rounds):
+        for cs in cases:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(5):
+                pkg.ddtree_ts_load_probe(W, E, toks[cs[1]], cs[0], sink)
+            b.record()
+            torch.cuda.synchronize()
+            times[cs].append(a.elapsed_time(b) / 5 * 1e3)
+    wbytes = V * H * 2
+    res = []
+    for (v, n), t in times.items():
+        us = float(np.median(t))
+        res.append({"variant": v, "loads": names[v], "distinct_parent_rows": n,
+                    "median_launch_us": round(us, 1), "w_gbps": round(wbytes / us / 1e3, 1)})
+    print(json.dumps({"probe": "TreeSpark head-evaluation loads (ddtree_ts_load_probe)",
+                      "V": V, "H": H, "parents": 128, "launches_per_case": 5 * rounds,
+                      "cases": res}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -531,6 +581,8 @@ def main() -> int:
     ap.add_argument("--workload", choices=("c3", "c2", "c5"), default="c3",
                     help="c3: batch 64, B 128 (default, the headline); c2: batch 1, B 64 latency "
                          "of build + mask + accept; c5: batch 256, B 256 (own JSON lines)")
+    ap.add_argument("--ts-load-probe", action="store_true",
+                    help="TreeSpark's head-evaluation loads alone, by load pattern and W policy")
     ap.add_argument("--read-probe", action="store_true",
                     help="only time the read probe over the batch-64 buffers (own JSON line)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -574,6 +626,8 @@ def main() -> int:
         return latency_bench(args)
     if args.read_probe:
         return read_probe_bench(args)
+    if args.ts_load_probe:
+        return ts_load_probe_bench(args)
     cfg = 5 if args.workload == "c5" else 3
 
     c = gen.CONFIGS[cfg]

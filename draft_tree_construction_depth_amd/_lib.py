@@ -58,6 +58,8 @@ def lib() -> C.CDLL:
         L.ddtree_compact_kv.argtypes = [p, p, i64, i64, i32, i64, i32, p, p, p, i32, p, p]
         L.ddtree_read_probe.restype = C.c_int
         L.ddtree_read_probe.argtypes = [p, i64, i64, p, p]
+        L.ddtree_ts_load_probe.restype = C.c_int
+        L.ddtree_ts_load_probe.argtypes = [p, p, p, i64, i32, i32, p, p]
         L.ddtree_row_topk.restype = C.c_int
         L.ddtree_row_topk.argtypes = [p, C.c_int, i64, i64, i32, p, p, p, p, sz, p]
         L.treespark_workspace_size.restype = sz
@@ -309,6 +311,23 @@ def ddtree_read_probe(src: torch.Tensor, rows: int, row_bytes: int,
         sink = torch.empty((rows, 4), dtype=torch.int32, device=src.device)
     _check("ddtree_read_probe", lib().ddtree_read_probe(_ptr(src), rows, row_bytes, _ptr(sink),
                                                         _stream(src.device)))
+    return sink
+
+
+def ddtree_ts_load_probe(W: torch.Tensor, E: torch.Tensor, ptok: torch.Tensor, variant: int,
+                         sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Measurement probe: one TreeSpark head evaluation's loads (W [V, H] and
+    the 128 parents' rows ptok of E [V, H], bf16) with nothing computed;
+    variant 0-4 as in the header. Returns the sink [256] (int32)."""
+    _arg(W, "W", _BF16)
+    V, H = W.shape
+    _arg(E, "E", _BF16, (V, H))
+    _arg(ptok, "ptok", _I32, (128,))
+    if sink is None:
+        sink = torch.empty(256, dtype=torch.int32, device=W.device)
+    _check("ddtree_ts_load_probe", lib().ddtree_ts_load_probe(_ptr(W), _ptr(E), _ptr(ptok), V, H,
+                                                              variant, _ptr(sink),
+                                                              _stream(W.device)))
     return sink
 
 

@@ -616,6 +616,31 @@ int ddtree_read_probe(const void* src, int64_t rows, int64_t row_bytes, uint32_t
   return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
 }
 
+int ddtree_ts_load_probe(const void* W, const void* E, const int32_t* ptok, int64_t V, int32_t H,
+                         int32_t variant, uint32_t* sink, hipStream_t stream) {
+  if (!W || !E || !ptok || !sink || V <= 0 || H <= 0 || H % ddt::kTsKT != 0) return DDT_EINVAL;
+  if ((uintptr_t)W % 16 != 0 || (uintptr_t)E % 16 != 0) return DDT_EINVAL;
+  if (variant < 0 || variant > 5) return DDT_EINVAL;
+  if (V * H * 2 >= (int64_t)1 << 32 || V > 0x7FFFFFFFLL) return DDT_ENOTSUP;
+  ddt::TsProbeParams tp;
+  tp.W = (const uint16_t*)W;
+  tp.E = (const uint16_t*)E;
+  tp.ptok = ptok;
+  tp.V = V;
+  tp.H = H;
+  tp.sink = sink;
+  const dim3 grid((unsigned)((V + ddt::kTsBV - 1) / ddt::kTsBV)), block(ddt::kTsThreads);
+  switch (variant) {
+    case 0: hipLaunchKernelGGL((ddt::ts_load_probe_kernel<0, 2>), grid, block, 0, stream, tp); break;
+    case 1: hipLaunchKernelGGL((ddt::ts_load_probe_kernel<1, 2>), grid, block, 0, stream, tp); break;
+    case 2: hipLaunchKernelGGL((ddt::ts_load_probe_kernel<2, 2>), grid, block, 0, stream, tp); break;
+    case 3: hipLaunchKernelGGL((ddt::ts_load_probe_kernel<2, 0x12>), grid, block, 0, stream, tp); break;
+    case 4: hipLaunchKernelGGL((ddt::ts_load_probe_kernel<0, 0x12>), grid, block, 0, stream, tp); break;
+    default: hipLaunchKernelGGL((ddt::ts_load_probe_kernel<3, 2>), grid, block, 0, stream, tp); break;
+  }
+  return hipGetLastError() == hipSuccess ? DDT_OK : DDT_EHIP;
+}
+
 int ddtree_compact_kv(void* k_cache, void* v_cache, int64_t layers, int64_t batch,
                       int32_t heads, int64_t cap, int32_t row_bytes, const int32_t* past_len,
                       const int32_t* accepted_nodes, const int32_t* accept_len, int32_t L,

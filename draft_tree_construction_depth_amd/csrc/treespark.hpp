@@ -134,13 +134,10 @@ __device__ __forceinline__ void ts_merge_sorted(float (&av)[KK], int (&ai)[KK], 
 // against all 128 vocabulary rows of the tile, so each parent's partial
 // record comes out of one wave, with no cross-wave combine.
 constexpr int kTsStages = 4;  // W ring depth (16 KiB per stage)
-// W is read once per launch: its loads carry the nontemporal hint at system
-// scope (sc1 nt), so that they do not push the parents' embedding rows and
-// the partial records (read by the merge next) out of the L2. With nt alone
-// the embedding rows, re-read by every workgroup, kept missing: a load-only
-// copy of this schedule streamed 128 parents' rows at 154 us per launch
-// with nt and 134 us with sc1 nt (8 distinct rows: 125 and 116 us).
-constexpr int kTsLoadNT = 0x12;
+// W is read once per launch: its loads carry the nontemporal hint, so that
+// they do not push the parents' embedding rows and the partial records (read
+// by the merge next) out of the caches
+constexpr int kTsLoadNT = 2;
 
 // LDS row r, 16-byte chunk c holds W chunk c ^ (r & 7) of that row's step
 // segment, so that a fragment read of 32 consecutive rows spreads over all

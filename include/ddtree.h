@@ -372,6 +372,25 @@ int dspark_budget(const float* conf, int64_t batch, int32_t P, const float* cost
 int ddtree_read_probe(const void* src, int64_t rows, int64_t row_bytes, uint32_t* sink,
                       hipStream_t stream);
 
+/*
+ * ddtree_ts_load_probe -- measurement probe: the loads of one TreeSpark head
+ * evaluation (TreeSpark README, item 1: z_d(u) = l_d + W . e(t_u) streams the
+ * head weight W once per depth while every vocabulary tile re-reads its
+ * parents' embedding rows) with nothing computed. W and E: device bf16
+ * [V][H], 16-byte aligned, H a multiple of 64; ptok: device int32 [128]
+ * parent tokens (each < V; a token past the table reads zeros); sink:
+ * device uint32 [256], written only on an impossible XOR value (the loads
+ * stay live). Launch geometry, LDS ring, wait and barrier per step are
+ * ts_gemm_kernel's. variant: 0 W alone (nontemporal), 1 W + the parents'
+ * rows 16 bytes of 32 rows per instruction (the MFMA B layout), 2 W + the
+ * rows as whole 128-byte lines, 3 as 2 with W at system-scope nontemporal,
+ * 4 W alone at system-scope nontemporal, 5 as 2 for only the first 16
+ * parents of each 32 (half the rows' traffic). DDT_EINVAL for null or misaligned
+ * pointers, bad sizes or variants; DDT_ENOTSUP for V x H x 2 >= 4 GiB.
+ */
+int ddtree_ts_load_probe(const void* W, const void* E, const int32_t* ptok, int64_t V, int32_t H,
+                         int32_t variant, uint32_t* sink, hipStream_t stream);
+
 int sparkling_beam(const void* logits, int dtype, const uint16_t* W1, const uint16_t* W2t,
                    int64_t batch, int32_t L, int64_t V, int32_t C, int32_t R,
                    const int32_t* widths, int32_t budget, int32_t* tree_tokens,

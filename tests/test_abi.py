@@ -131,6 +131,19 @@ def test_mask_accept_topk_validation(L):
     assert L.ddtree_row_topk(FAKE, 0, 0, 1000, 64, FAKE, FAKE, FAKE, FAKE, 0, None) == 0
 
 
+def test_probe_validation(L):
+    assert L.ddtree_read_probe(None, 4, 64, FAKE, None) == -1
+    assert L.ddtree_read_probe(FAKE, 4, 60, FAKE, None) == -1
+    assert L.ddtree_read_probe(FAKE, 0, 64, FAKE, None) == 0
+    # W, E, ptok, V, H, variant, sink
+    assert L.ddtree_ts_load_probe(None, FAKE, FAKE, 1000, 128, 0, FAKE, None) == -1
+    assert L.ddtree_ts_load_probe(FAKE, FAKE, FAKE, 1000, 100, 0, FAKE, None) == -1
+    assert L.ddtree_ts_load_probe(FAKE, FAKE, FAKE, 1000, 128, 6, FAKE, None) == -1
+    assert L.ddtree_ts_load_probe(FAKE, FAKE, FAKE, 0, 128, 0, FAKE, None) == -1
+    assert L.ddtree_ts_load_probe(MISALIGNED, FAKE, FAKE, 1000, 128, 0, FAKE, None) == -1
+    assert L.ddtree_ts_load_probe(FAKE, FAKE, FAKE, 1 << 20, 4096, 0, FAKE, None) == -2
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
