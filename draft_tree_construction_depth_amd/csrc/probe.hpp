@@ -151,4 +151,82 @@ __global__ __launch_bounds__(kTsThreads, 2) void ts_load_probe_kernel(TsProbePar
   if (acc == 0x9E3779B9u) p.sink[tid] = acc;
 }
 
+// The same loads for a 256-row vocabulary tile: eight waves (one workgroup
+// per CU, a 4-stage 32 KB W ring), waves w and w + 4 sharing parents
+// 32 (w % 4) .. + 31, each loading half of their whole-line chunks, so the
+// embedding traffic per W byte is half the 128-row tile's.
+template <int WPOL>
+__global__ __launch_bounds__(2 * kTsThreads, 1) void ts_load_probe256_kernel(TsProbeParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t w256[kTsStages][2 * kTsBV][kTsKT];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int ws = __builtin_amdgcn_readfirstlane(w);
+  const int64_t V = p.V;
+  const int H = p.H, nks = H / kTsKT;
+  const int64_t vt0 = (int64_t)blockIdx.x * 2 * kTsBV;
+  const int64_t wbytes = (V - vt0) * H * 2;
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.W + vt0 * H), (short)0, (int)(wbytes < 0x7FFFFFFF ? wbytes : 0x7FFFFFFF), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.E, (short)0, (int)(uint32_t)(V * H * 2), 0x00020000);
+  uint32_t woff[4], eoff[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t v = vt0 + 8 * (8 * i + w) + (l >> 3);
+    woff[i] = (uint32_t)(((v < V ? v : V - 1) - vt0) * H * 2 + (((l & 7) ^ (l >> 3)) << 4));
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    eoff[i] = (uint32_t)p.ptok[32 * (w & 3) + 16 * (w >> 2) + 8 * i + (l >> 3)] * (uint32_t)H * 2u +
+              (uint32_t)(((l & 7) ^ (l >> 3)) << 4);
+  auto load_w = [&](int ks) {
+    const int kc = ks < nks ? ks : nks - 1;
+    const int st = ks % kTsStages;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (ts_lds_ptr)&w256[st][8 * (8 * i + ws)][0], 16,
+                                               woff[i], kc * kTsKT * 2, 0, WPOL);
+  };
+  auto load_e = [&](u32x4 (&d)[2], int ks) {
+    const int kc = ks < nks ? ks : nks - 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      d[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ers, (int)eoff[i], kc * kTsKT * 2, 0));
+  };
+  uint32_t acc = 0;
+  auto step = [&](int ks, u32x4 (&ec)[2], u32x4 (&en)[2]) {
+    __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10): W(ks) and E(ks) arrived
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    load_e(en, ks + 2);
+    load_w(ks + 3);
+    const uint32_t a = (uint32_t)(uintptr_t)(ts_lds_ptr)&w256[ks % kTsStages][l & 31][0] +
+                       16u * (uint32_t)(l >> 5);
+    u32x4 x;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(x) : "v"(a));
+    acc ^= x[0] ^ x[3] ^ ec[0][0] ^ ec[1][1];
+  };
+  asm volatile("" ::"v"(eoff[0]), "v"(eoff[1]));
+  u32x4 e0[2] = {}, e1[2] = {}, e2[2] = {};
+  load_w(0);
+  asm volatile("" ::: "memory");
+  load_e(e0, 0);
+  asm volatile("" ::: "memory");
+  load_w(1);
+  asm volatile("" ::: "memory");
+  load_e(e1, 1);
+  asm volatile("" ::: "memory");
+  load_w(2);
+  int ks = 0;
+  for (; ks + 3 <= nks; ks += 3) {
+    step(ks, e0, e2);
+    step(ks + 1, e1, e0);
+    step(ks + 2, e2, e1);
+  }
+  if (ks < nks) step(ks, e0, e2);
+  if (ks + 1 < nks) step(ks + 1, e1, e0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (acc == 0x9E3779B9u) p.sink[tid & 255] = acc;
+}
+
 }  // namespace ddt
