@@ -196,12 +196,11 @@ __global__ __launch_bounds__(kTsThreads, 2) void ts_gemm_kernel(TsGemmParams p) 
     eoff[i] = (uint32_t)p.ptok[pcol] * (uint32_t)H * 2u + (uint32_t)(((l & 7) ^ (l >> 3)) << 4);
   }
 
-  // always issue (clamped past the last step): the wait counts stay static
-  // (past the last step the four loads still issue, so that the wait counts
-  // stay static, but read the last embedding chunk, which the L2 holds,
-  // instead of W lines from HBM again)
-  // (one code path for both, selected by value: a branch here makes the
-  // compiler add waits of its own in every step)
+  // W loads always issue, so that the wait counts stay static; past the last
+  // step they read the last embedding chunk, which the L2 holds, instead of
+  // W lines from HBM again. One code path for both, the source selected by
+  // value: a branch here makes the compiler add waits of its own in every
+  // step. E past the last step re-reads the last chunk.
   auto load_w = [&](int ks) {
     const int st = ks % kTsStages;
     const bool past = ks >= nks;
