@@ -533,8 +533,9 @@ def ts_load_probe_bench(args) -> int:
     names = {0: "W alone (nt)", 1: "W (nt) + rows in MFMA layout", 2: "W (nt) + rows as lines",
              3: "W (sc1 nt) + rows as lines", 4: "W alone (sc1 nt)",
              5: "W (nt) + half the rows as lines",
-             6: "W (nt) + rows as lines, 256-row tiles of eight waves"}
-    cases = [(v, 128) for v in range(7)] + [(1, 8), (2, 8), (3, 8), (6, 8)]
+             6: "W (nt) + rows as lines, 256-row tiles of eight waves",
+             7: "W (nt) + rows as lines, 256-row tiles, one persistent workgroup per CU"}
+    cases = [(v, 128) for v in range(8)] + [(1, 8), (2, 8), (3, 8), (6, 8), (7, 8)]
     sink = torch.empty(256, dtype=torch.int32, device=dev)
     for v, n in cases:
         pkg.ddtree_ts_load_probe(W, E, toks[n], v, sink)

@@ -620,7 +620,7 @@ int ddtree_ts_load_probe(const void* W, const void* E, const int32_t* ptok, int6
                          int32_t variant, uint32_t* sink, hipStream_t stream) {
   if (!W || !E || !ptok || !sink || V <= 0 || H <= 0 || H % ddt::kTsKT != 0) return DDT_EINVAL;
   if ((uintptr_t)W % 16 != 0 || (uintptr_t)E % 16 != 0) return DDT_EINVAL;
-  if (variant < 0 || variant > 6) return DDT_EINVAL;
+  if (variant < 0 || variant > 7) return DDT_EINVAL;
   if (V * H * 2 >= (int64_t)1 << 32 || V > 0x7FFFFFFFLL) return DDT_ENOTSUP;
   ddt::TsProbeParams tp;
   tp.W = (const uint16_t*)W;
@@ -637,6 +637,16 @@ int ddtree_ts_load_probe(const void* W, const void* E, const int32_t* ptok, int6
     case 3: hipLaunchKernelGGL((ddt::ts_load_probe_kernel<2, 0x12>), grid, block, 0, stream, tp); break;
     case 4: hipLaunchKernelGGL((ddt::ts_load_probe_kernel<0, 0x12>), grid, block, 0, stream, tp); break;
     case 5: hipLaunchKernelGGL((ddt::ts_load_probe_kernel<3, 2>), grid, block, 0, stream, tp); break;
+    case 7: {
+      int dev = 0, cus = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+          cus <= 0)
+        return DDT_EHIP;
+      hipLaunchKernelGGL((ddt::ts_load_probe256p_kernel<2>), dim3((unsigned)cus),
+                         dim3(2 * ddt::kTsThreads), 0, stream, tp);
+      break;
+    }
     default:
       hipLaunchKernelGGL((ddt::ts_load_probe256_kernel<2>),
                          dim3((unsigned)((V + 2 * ddt::kTsBV - 1) / (2 * ddt::kTsBV))),

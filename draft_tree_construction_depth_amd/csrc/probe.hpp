@@ -229,4 +229,89 @@ __global__ __launch_bounds__(2 * kTsThreads, 1) void ts_load_probe256_kernel(TsP
   if (acc == 0x9E3779B9u) p.sink[tid & 255] = acc;
 }
 
+// The 256-row loads again with persistent workgroups: G workgroups (one per
+// CU), workgroup x streams tiles x, x + G, ... as one continuous step
+// sequence (no workgroup start between its tiles; the embedding chunk of
+// step g is chunk g mod H / 64 of every tile).
+template <int WPOL>
+__global__ __launch_bounds__(2 * kTsThreads, 1) void ts_load_probe256p_kernel(TsProbeParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t w256[kTsStages][2 * kTsBV][kTsKT];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int ws = __builtin_amdgcn_readfirstlane(w);
+  const int64_t V = p.V;
+  const int H = p.H, nks = H / kTsKT;
+  const int G = gridDim.x;
+  const int ntile = (int)((V + 2 * kTsBV - 1) / (2 * kTsBV));
+  const int mytiles = ntile > (int)blockIdx.x ? (ntile - 1 - (int)blockIdx.x) / G + 1 : 0;
+  const int nsteps = mytiles * nks;
+  // one resource over all of W (byte offsets below 2^31); rows past V read zeros
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.W, (short)0, (int)(V * H * 2 < 0x7FFFFFFF ? V * H * 2 : 0x7FFFFFFF), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.E, (short)0, (int)(uint32_t)(V * H * 2), 0x00020000);
+  uint32_t woff[4], eoff[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    woff[i] = (uint32_t)((8 * (8 * i + w) + (l >> 3)) * H * 2 + (((l & 7) ^ (l >> 3)) << 4));
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    eoff[i] = (uint32_t)p.ptok[32 * (w & 3) + 16 * (w >> 2) + 8 * i + (l >> 3)] * (uint32_t)H * 2u +
+              (uint32_t)(((l & 7) ^ (l >> 3)) << 4);
+  // step g of this workgroup: tile blockIdx.x + (g / nks) G, chunk g % nks
+  auto load_w = [&](int g) {
+    const int gc = g < nsteps ? g : nsteps - 1;
+    const int t = gc / nks, kc = gc - t * nks;
+    const int64_t row0 = (int64_t)((int)blockIdx.x + t * G) * 2 * kTsBV;
+    const int so = (int)(row0 * H * 2) + kc * kTsKT * 2;
+    const int st = g % kTsStages;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (ts_lds_ptr)&w256[st][8 * (8 * i + ws)][0], 16,
+                                               woff[i], so, 0, WPOL);
+  };
+  auto load_e = [&](u32x4 (&d)[2], int g) {
+    const int gc = g < nsteps ? g : nsteps - 1;
+    const int kc = gc % nks;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      d[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ers, (int)eoff[i], kc * kTsKT * 2, 0));
+  };
+  uint32_t acc = 0;
+  auto step = [&](int g, u32x4 (&ec)[2], u32x4 (&en)[2]) {
+    __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    load_e(en, g + 2);
+    load_w(g + 3);
+    const uint32_t a = (uint32_t)(uintptr_t)(ts_lds_ptr)&w256[g % kTsStages][l & 31][0] +
+                       16u * (uint32_t)(l >> 5);
+    u32x4 x;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(x) : "v"(a));
+    acc ^= x[0] ^ x[3] ^ ec[0][0] ^ ec[1][1];
+  };
+  if (nsteps == 0) return;
+  asm volatile("" ::"v"(eoff[0]), "v"(eoff[1]));
+  u32x4 e0[2] = {}, e1[2] = {}, e2[2] = {};
+  load_w(0);
+  asm volatile("" ::: "memory");
+  load_e(e0, 0);
+  asm volatile("" ::: "memory");
+  load_w(1);
+  asm volatile("" ::: "memory");
+  load_e(e1, 1);
+  asm volatile("" ::: "memory");
+  load_w(2);
+  int g = 0;
+  for (; g + 3 <= nsteps; g += 3) {
+    step(g, e0, e2);
+    step(g + 1, e1, e0);
+    step(g + 2, e2, e1);
+  }
+  if (g < nsteps) step(g, e0, e2);
+  if (g + 1 < nsteps) step(g + 1, e1, e0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (acc == 0x9E3779B9u) p.sink[tid & 255] = acc;
+}
+
 }  // namespace ddt

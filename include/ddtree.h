@@ -387,7 +387,9 @@ int ddtree_read_probe(const void* src, int64_t rows, int64_t row_bytes, uint32_t
  * 4 W alone at system-scope nontemporal, 5 as 2 for only the first 16
  * parents of each 32 (half the rows' traffic), 6 as 2 with 256-row tiles
  * (eight waves, one workgroup per CU, each pair of waves sharing its 32
- * parents' lines: half the rows' traffic per W byte). DDT_EINVAL for null or misaligned
+ * parents' lines: half the rows' traffic per W byte), 7 as 6 with one
+ * persistent workgroup per CU streaming its tiles as one step sequence.
+ * DDT_EINVAL for null or misaligned
  * pointers, bad sizes or variants; DDT_ENOTSUP for V x H x 2 >= 4 GiB.
  */
 int ddtree_ts_load_probe(const void* W, const void* E, const int32_t* ptok, int64_t V, int32_t H,

@@ -138,7 +138,7 @@ def test_probe_validation(L):
     # W, E, ptok, V, H, variant, sink
     assert L.ddtree_ts_load_probe(None, FAKE, FAKE, 1000, 128, 0, FAKE, None) == -1
     assert L.ddtree_ts_load_probe(FAKE, FAKE, FAKE, 1000, 100, 0, FAKE, None) == -1
-    assert L.ddtree_ts_load_probe(FAKE, FAKE, FAKE, 1000, 128, 7, FAKE, None) == -1
+    assert L.ddtree_ts_load_probe(FAKE, FAKE, FAKE, 1000, 128, 8, FAKE, None) == -1
     assert L.ddtree_ts_load_probe(FAKE, FAKE, FAKE, 0, 128, 0, FAKE, None) == -1
     assert L.ddtree_ts_load_probe(MISALIGNED, FAKE, FAKE, 1000, 128, 0, FAKE, None) == -1
     assert L.ddtree_ts_load_probe(FAKE, FAKE, FAKE, 1 << 20, 4096, 0, FAKE, None) == -2
