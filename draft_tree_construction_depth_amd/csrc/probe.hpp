@@ -5,7 +5,7 @@
 // every drafter row once. Its speed of light on this chip is not the HBM
 // data-sheet peak but what a kernel that only streams those rows reaches: one
 // 256-thread workgroup per row, chunks of 256 threads x NV x 16 bytes loaded
-// through per-slab buffer resources with the nontemporal hint, double
+// through one buffer resource per chunk with the nontemporal hint, double
 // buffered in registers. The loaded words are XOR-folded and one word per
 // wave is written, so the loads cannot be dropped; the written bytes (16 per
 // row) are negligible. The measured rate is the practical ceiling the stage-1

@@ -619,9 +619,9 @@ __global__ __launch_bounds__(kWave* kMergeWaves) void stage1_merge_kernel(Stage1
 // raising the offset rescales the float64 sum exactly (ldexp). Each chunk
 // takes a max pass (vector maxima, which also feed the claims and the keep
 // test) and an exponent pass.
-// Loads. Every 16-byte load is a buffer load whose resource covers one 4 KiB
-// slab of the row (its bytes left, clamped): vectors past the row's end read
-// as zero without touching memory and are then set to -inf.
+// Loads. Every 16-byte load is a buffer load whose resource covers the
+// chunk's bytes inside the row (clamped): vectors past the row's end read as
+// zero without touching memory and are then set to -inf.
 
 constexpr int kVecCap = 448;          // kept vectors per wave
 constexpr int kKeyCap = 2 * kVecCap;  // candidate keys per wave (in the wave's vector region)
@@ -674,24 +674,29 @@ __device__ __forceinline__ float vec_max(const float (&x)[DT == 0 ? 8 : 4]) {
   }
 }
 
-// Chunk loads: slab j of the chunk (256 threads x 16 B) through its own
-// buffer resource; the thread's offset is the same for every slab. The
-// logits are read once, so the loads carry the nontemporal hint.
+// Chunk loads: slab j of the chunk (256 threads x 16 B) at vector offset
+// 16 t + 4096 j through one buffer resource over the chunk's bytes inside the
+// row, so vectors past the row's end read as zero without touching memory.
+// (One resource per slab cost about 17 scalar instructions per load; one per
+// chunk, 2.8 us less per batch-64 launch.) The logits are read once, so the
+// loads carry the nontemporal hint.
 constexpr int kLoadNT = 2;  // cache-policy bit "nt" of buffer loads
 template <int NV>
 __device__ __forceinline__ void load_chunk_buf(v4u32 (&buf)[NV], const char* rowp,
                                                int64_t cbyte, int64_t rowbytes) {
-  const int voff = (int)threadIdx.x * 16;
+  // one resource over the chunk's bytes that lie inside the row; slab j at
+  // vector offset j x 4 KiB (the bounds check covers the vector offset)
+  const int64_t left = rowbytes - cbyte;
+  constexpr int kCB = NV * kS1Threads * 16;
+  const int nrec = left <= 0 ? 0 : (left >= kCB ? kCB : (int)left);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(rowp + (left > 0 ? cbyte : 0)), (short)0, nrec, 0x00020000);
+  // (the slab offsets are formed at each load, not held in registers)
+  int voff = (int)threadIdx.x * 16;
+  asm volatile("" : "+v"(voff));
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int64_t off = cbyte + (int64_t)j * kS1Threads * 16;
-    const int64_t left = rowbytes - off;
-    const int nrec = left <= 0 ? 0 : (left >= kS1Threads * 16 ? kS1Threads * 16 : (int)left);
-    __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(rowp + (left > 0 ? off : 0)), (short)0, nrec,
-                                          0x00020000);
-    buf[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, kLoadNT);
-  }
+  for (int j = 0; j < NV; ++j)
+    buf[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + j * kS1Threads * 16, 0, kLoadNT);
 }
 
 // Vector maxima of a register-resident chunk.
