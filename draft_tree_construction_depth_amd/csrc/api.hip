@@ -728,9 +728,9 @@ int treespark_expand(const void* backbone, const void* W, const void* E, const i
   float* pval = (float*)(ws + lay.pval);
   int32_t* pid = (int32_t*)(ws + lay.pid);
 
-  hipLaunchKernelGGL(ddt::ts_init_kernel, dim3((unsigned)((batch + 255) / 256)), dim3(256), 0,
-                     stream, st, anchor, batch);
-  if (hipGetLastError() != hipSuccess) return DDT_EHIP;
+  // depth 0's parents are the anchors themselves (the merge at depth 0 takes
+  // one parent, candidate -1, and no candidates before it), so no state is
+  // initialised on the device
   for (int d = 0; d < D; ++d) {
     const int Fd = sh.Fd[d];
     const int64_t M = batch * Fd;
@@ -738,7 +738,7 @@ int treespark_expand(const void* backbone, const void* W, const void* E, const i
     gp.W = (const uint16_t*)W;
     gp.E = (const uint16_t*)E;
     gp.bb = (const uint16_t*)backbone;
-    gp.ptok = st.ptok[d & 1];
+    gp.ptok = d == 0 ? anchor : st.ptok[d & 1];
     gp.V = V;
     gp.H = H;
     gp.D = D;

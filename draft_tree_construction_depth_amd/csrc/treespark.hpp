@@ -440,21 +440,12 @@ struct TsState {
   uint64_t* ckey;   // [batch][cmax] rank-tuple keys
   int32_t* cpar;    // [batch][cmax] parent candidate (-1: the anchor)
   int32_t* cdep;    // [batch][cmax] depth (1-based)
-  int32_t* ccount;  // [batch]
-  int32_t* fcount;  // [batch] parents of the current depth
-  int32_t* ptok[2];   // [batch * F] parent tokens, by depth parity
+  int32_t* ccount;  // [batch] (written from depth 0 on; depth 0 reads none)
+  int32_t* fcount;  // [batch] parents of the current depth (likewise)
+  int32_t* ptok[2];   // [batch * F] parent tokens, by depth parity (depth 0: the anchors)
   int32_t* pcand[2];  // [batch * F] parent candidate index (-1: anchor)
   int32_t cmax;
 };
-
-__global__ void ts_init_kernel(TsState st, const int32_t* anchor, int64_t batch) {
-  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= batch) return;
-  st.ccount[b] = 0;
-  st.fcount[b] = 1;
-  st.ptok[0][b] = anchor[b];
-  st.pcand[0][b] = -1;
-}
 
 struct TsMergeParams {
   TsState st;
@@ -497,9 +488,10 @@ __global__ __launch_bounds__(kTsMergeThreads) void ts_merge_kernel(TsMergeParams
   const int64_t b = blockIdx.x;
   TsState& st = p.st;
   const int par = p.d & 1;
-  const int nf = st.fcount[b];
+  // depth 0: one parent (the anchor, candidate -1), no candidates yet
+  const int nf = p.d == 0 ? 1 : st.fcount[b];
   const int K = p.k;
-  const int base = st.ccount[b];
+  const int base = p.d == 0 ? 0 : st.ccount[b];
   const int shift = 4 * (kTsDMax - 1 - p.d);  // this depth's digit
   const int rounds = (nf + kTsMergeGroups - 1) / kTsMergeGroups;
   for (int rd = 0; rd < rounds; ++rd) {  // uniform trip count: every group reaches each barrier
@@ -629,7 +621,7 @@ __global__ __launch_bounds__(kTsMergeThreads) void ts_merge_kernel(TsMergeParams
       for (int q = 0; q < kTsGroupWaves; ++q) tot += red_d[g][q];
       const double lse = (double)M + log(tot);
       if (lane < K) {
-        const int pc = st.pcand[par][m];
+        const int pc = p.d == 0 ? -1 : st.pcand[par][m];
         const double pscore = pc < 0 ? 0.0 : st.cscore[b * st.cmax + pc];
         const uint64_t pkey = pc < 0 ? 0ull : st.ckey[b * st.cmax + pc];
         const int c = i * K + lane;
