@@ -731,6 +731,7 @@ int treespark_expand(const void* backbone, const void* W, const void* E, const i
   // depth 0's parents are the anchors themselves (the merge at depth 0 takes
   // one parent, candidate -1, and no candidates before it), so no state is
   // initialised on the device
+  int base = 0;  // candidates per request before depth d
   for (int d = 0; d < D; ++d) {
     const int Fd = sh.Fd[d];
     const int64_t M = batch * Fd;
@@ -772,6 +773,7 @@ int treespark_expand(const void* backbone, const void* W, const void* E, const i
     mp.Fn = d + 1 < D ? sh.Fd[d + 1] : 1;
     mp.k = sh.kk;
     mp.F = F;
+    mp.base = base;
     if (sh.kk <= 4)
       hipLaunchKernelGGL(ddt::ts_merge_kernel<4>, dim3((unsigned)batch),
                          dim3(ddt::kTsMergeThreads), 0, stream, mp);
@@ -779,6 +781,7 @@ int treespark_expand(const void* backbone, const void* W, const void* E, const i
       hipLaunchKernelGGL(ddt::ts_merge_kernel<8>, dim3((unsigned)batch),
                          dim3(ddt::kTsMergeThreads), 0, stream, mp);
     if (hipGetLastError() != hipSuccess) return DDT_EHIP;
+    base += Fd * sh.kk;
   }
   ddt::TsPackParams pp;
   pp.st = st;

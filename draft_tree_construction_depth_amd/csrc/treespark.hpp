@@ -457,6 +457,7 @@ struct TsMergeParams {
   int32_t d, D;       // 0-based depth, depths
   int32_t Fd, Fn;     // parents per request at this depth / the next
   int32_t k, F;
+  int32_t base;       // candidates per request before this depth
 };
 
 __device__ __forceinline__ uint64_t ts_zkey(float x, int id) {
@@ -488,16 +489,21 @@ __global__ __launch_bounds__(kTsMergeThreads) void ts_merge_kernel(TsMergeParams
   const int64_t b = blockIdx.x;
   TsState& st = p.st;
   const int par = p.d & 1;
-  // depth 0: one parent (the anchor, candidate -1), no candidates yet
-  const int nf = p.d == 0 ? 1 : st.fcount[b];
+  // parents and earlier candidates per request are the same for every
+  // request (each parent has exactly k children): taken from the host, so
+  // that the record loads need not wait for a load of them
+  const int nf = p.Fd;
   const int K = p.k;
-  const int base = p.d == 0 ? 0 : st.ccount[b];
+  const int base = p.base;
   const int shift = 4 * (kTsDMax - 1 - p.d);  // this depth's digit
   const int rounds = (nf + kTsMergeGroups - 1) / kTsMergeGroups;
   for (int rd = 0; rd < rounds; ++rd) {  // uniform trip count: every group reaches each barrier
     const int i = rd * kTsMergeGroups + g;
     const bool act = i < nf;
     const int m = (int)b * p.Fd + (act ? i : 0);
+    // the parent's candidate index (-1: the anchor), read now so that its
+    // score and key can be read while the tiles' records are reduced
+    const int pc = (p.d == 0 || !act) ? -1 : st.pcand[par][m];
     // One pass over the parent's tiles: each thread loads, for a batch of its
     // tiles at once (consecutive in memory for consecutive threads), the
     // tile's maximum, exp sum and best entry, and keeps its own maximum, its
@@ -547,6 +553,8 @@ __global__ __launch_bounds__(kTsMergeThreads) void ts_merge_kernel(TsMergeParams
         }
       }
     }
+    const double pscore = pc < 0 ? 0.0 : st.cscore[b * st.cmax + pc];
+    const uint64_t pkey = pc < 0 ? 0ull : st.ckey[b * st.cmax + pc];
     // the group's maximum, then every thread's sum rescaled to it
     const float wm = wave_max(mx);
     if (lane == 0) red_m[g][gw] = wm;
@@ -621,9 +629,6 @@ __global__ __launch_bounds__(kTsMergeThreads) void ts_merge_kernel(TsMergeParams
       for (int q = 0; q < kTsGroupWaves; ++q) tot += red_d[g][q];
       const double lse = (double)M + log(tot);
       if (lane < K) {
-        const int pc = p.d == 0 ? -1 : st.pcand[par][m];
-        const double pscore = pc < 0 ? 0.0 : st.cscore[b * st.cmax + pc];
-        const uint64_t pkey = pc < 0 ? 0ull : st.ckey[b * st.cmax + pc];
         const int c = i * K + lane;
         ch_tok[c] = (int32_t)(0xFFFFFFFFu - (uint32_t)pick);
         ch_score[c] = pscore + ((double)key_value((uint32_t)(pick >> 32)) - lse);
