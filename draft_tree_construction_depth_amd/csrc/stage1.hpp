@@ -1020,15 +1020,26 @@ __global__ __launch_bounds__(kS1Threads, 4) void stage1_row_kernel(Stage1Params 
   v4u32 A[NV], Bf[NV];
   load_chunk_buf<NV>(A, rowp, 0, rowbytes);
   load_chunk_buf<NV>(Bf, rowp, CB, rowbytes);
-  if (PRIO) progress_priority(0, S);
+  // the priority changes only at the first chunk of each quarter of the row:
+  // pnext is the next such chunk (one compare per chunk instead of the
+  // division and the level switch)
+  int pnext = 0;
+  auto prio = [&](int c) {
+    if (PRIO && c >= pnext) {
+      progress_priority(c, S);
+      const int q = (4 * c) / S;
+      pnext = ((q + 1) * S + 3) / 4;
+    }
+  };
+  prio(0);
   row_chunk<DT, NV, GS, true>(A, sm, 0, nvec_of(0), need, lregs, st, true);
   load_chunk_buf<NV>(A, rowp, 2 * CB, rowbytes);
   for (int c = 1; c < S; c += 2) {
-    if (PRIO) progress_priority(c, S);
+    prio(c);
     row_chunk<DT, NV, GS, false>(Bf, sm, (int64_t)c * CH, nvec_of(c), need, lregs, st,
                                  claim_due(c));
     load_chunk_buf<NV>(Bf, rowp, (int64_t)(c + 2) * CB, rowbytes);
-    if (PRIO) progress_priority(c + 1, S);
+    prio(c + 1);
     if (c + 1 < S)
       row_chunk<DT, NV, GS, false>(A, sm, (int64_t)(c + 1) * CH, nvec_of(c + 1), need, lregs, st,
                                    claim_due(c + 1));
