@@ -632,7 +632,7 @@ constexpr int kListRegs = 2;          // list of 64 * kListRegs group maxima per
 // is still one element, so the certificate stays valid, only looser). The
 // looser threshold keeps more vectors; a wave whose region would overflow
 // first compacts it against its current threshold (compact_kept).
-constexpr int kClaimDense = 4;
+constexpr int kClaimDense = 5;
 constexpr int kClaimEvery = 3;
 
 // 37.1 KiB: four workgroups fit in one CU's 160 KiB.
