@@ -119,6 +119,9 @@ __global__ __launch_bounds__(kBmThreads) void beam_kernel(BeamParams bp) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t b = blockIdx.x;
   const int L = p.L, C = p.K, B = p.B, LC = L * C, bpd = p.bpd;
+  // m / C by a multiply with the host's ceil(2^32 / C) (exact for m C < 2^32)
+  const uint64_t cmag = p.kmag;
+  auto divC = [&](int m) { return (int)(((uint64_t)(uint32_t)m * cmag) >> 32); };
   const float* lpb = p.sp_lp + (size_t)b * (L - 1) * C * C;
   for (int i = tid; i < LC; i += kBmThreads) sm.tok[i] = p.ids[(size_t)b * LC + i];
   if (wv == 0) {
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(kBmThreads) void beam_kernel(BeamParams bp) {
     // ---- candidate scores, their range --------------------------------------
     double mn = INFINITY, mxs = -INFINITY;
     for (int m = tid; m < M; m += kBmThreads) {
-      const int u = m / C, j = m - u * C;
+      const int u = divC(m), j = m - u * C;
       const float v = row(u)[j];
       const double s = sm.bS[u] + (double)v;
       sm.cs[m] = s;
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(kBmThreads) void beam_kernel(BeamParams bp) {
     int nsel = 0;  // candidates taken before the cut bin's
     if (w >= M) {
       for (int m = tid; m < M; m += kBmThreads) {
-        const int u = m / C;
+        const int u = divC(m);
         sm.sel[m] = m;
         sm.sS[m] = sm.cs[m];
         sm.sH[m] = sm.bh[u];
@@ -188,12 +191,8 @@ __global__ __launch_bounds__(kBmThreads) void beam_kernel(BeamParams bp) {
       nsel = M;
       lds_barrier();
     } else {
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const double a = __shfl_xor(mn, o), c = __shfl_xor(mxs, o);
-        mn = a < mn ? a : mn;
-        mxs = c > mxs ? c : mxs;
-      }
+      mn = wave_min(mn);
+      mxs = wave_max(mxs);
       if (lane == 0) {
         sm.rmin[wv] = mn;
         sm.rmax[wv] = mxs;
@@ -237,7 +236,7 @@ __global__ __launch_bounds__(kBmThreads) void beam_kernel(BeamParams bp) {
       for (int m = tid; m < M; m += kBmThreads) {
         const double sc = sm.cs[m];
         const int bn = bin_of(sc);
-        const int u = m / C;
+        const int u = divC(m);
         if (bn < kc) {
           const int k = atomicAdd(&sm.nsel, 1);
           sm.sel[k] = m;
@@ -259,7 +258,7 @@ __global__ __launch_bounds__(kBmThreads) void beam_kernel(BeamParams bp) {
       if (nc <= kBmCut) {
         // members' child ranks, then their order by full key
         for (int k = wv; k < nc; k += kBmWaves) {
-          const int m = sm.cut[k], u = m / C;
+          const int m = sm.cut[k], u = divC(m);
           const int r = bm_rank_wave(sm.clp + u * C, tk, C, m - u * C);
           if (lane == 0) sm.crank[k] = r;
         }
@@ -292,7 +291,7 @@ __global__ __launch_bounds__(kBmThreads) void beam_kernel(BeamParams bp) {
           int br = 0x7FFFFFFF, bm = -1;
           for (int m = tid; m < M; m += kBmThreads) {
             if (bin_of(sm.cs[m]) != kc || ((sm.taken[m >> 6] >> (m & 63)) & 1)) continue;
-            const int u = m / C;
+            const int u = divC(m);
             const int r = bm_rank(sm.clp + u * C, tk, C, m - u * C);
             if (bm < 0 || bm_before(sm.cs[m], sm.bh[u], sm.bl[u], r, bs, bh, bl, br)) {
               bs = sm.cs[m];
@@ -329,12 +328,12 @@ __global__ __launch_bounds__(kBmThreads) void beam_kernel(BeamParams bp) {
                 best = q;
                 continue;
               }
-              const int mb = sm.cut[best], ub = mb / C, uq = mq / C;
+              const int mb = sm.cut[best], ub = divC(mb), uq = divC(mq);
               if (bm_before(sm.cs[mq], sm.bh[uq], sm.bl[uq], sm.crank[q], sm.cs[mb], sm.bh[ub],
                             sm.bl[ub], sm.crank[best]))
                 best = q;
             }
-            const int mb = sm.cut[best], ub = mb / C;
+            const int mb = sm.cut[best], ub = divC(mb);
             sm.sel[nsel + t] = mb;
             sm.srank[nsel + t] = sm.crank[best];
             sm.sS[nsel + t] = sm.cs[mb];
@@ -350,7 +349,7 @@ __global__ __launch_bounds__(kBmThreads) void beam_kernel(BeamParams bp) {
     // ---- the new beam: child ranks of the whole-bin entries, keys, order ----
     const int cutfrom = w >= M ? M : sm.kexc;  // entries before it need their rank
     for (int k = wv; k < cutfrom; k += kBmWaves) {
-      const int m = sm.sel[k], u = m / C;
+      const int m = sm.sel[k], u = divC(m);
       const int r = bm_rank_wave(sm.clp + u * C, tk, C, m - u * C);
       if (lane == 0) sm.srank[k] = r;
     }
@@ -361,7 +360,7 @@ __global__ __launch_bounds__(kBmThreads) void beam_kernel(BeamParams bp) {
     double nb_S = 0.0;
     uint64_t nb_h = 0, nb_l = 0;
     if (tid < nsel) {
-      const int m = sm.sel[tid], u = m / C, j = m - u * C;
+      const int m = sm.sel[tid], u = divC(m), j = m - u * C;
       const double s = sm.sS[tid];
       uint64_t h = sm.sH[tid], l = sm.sL[tid];
       const int r = sm.srank[tid];
